@@ -1,0 +1,298 @@
+"""CPU oracle of the QuantSparse attention hot path.  TEST INFRASTRUCTURE ONLY.
+
+Plain, slow, obviously correct NumPy code (fp64 unless a step's definition
+fixes fp32).  It defines what the HIP path must compute.  Only the tests, the
+smoke check in ``__graft_entry__`` and the benchmark's CPU-baseline leg may
+import it; the product path never does.  It shares no code with the HIP path
+(only the seeded input generator ``qsa_gen`` serves both).
+
+Sources (gist.science summaries of arXiv 2509.23681, "QuantSparse:
+Comprehensively Compressing Video Diffusion Transformer with Model
+Quantization and Attention Sparsification"):
+
+* [QS-es] gist.science/es/paper/2509.23681, "Resumen técnico";
+* [QS-ko] gist.science/ko/paper/2509.23681, "기술 요약".
+
+The pages describe the method, not its operational detail.  Where they are
+silent the readings below are taken (each is also listed with its reason in
+the design notes of this repository):
+
+R1  8-bit activations ([QS-es] §1 and §4, W4A8): symmetric int8 codes for Q
+    and K with one fp32 scale per (batch, head, token block) over all D.
+R2  scale = fl32(amax / 127); code = clamp(rint(fl32(x / scale)), -127, 127)
+    with IEEE fp32 division and round-half-to-even; an all-zero block has
+    scale 0 and codes 0.
+R3  tail blocks (seq_len not a multiple of the block) are shorter blocks:
+    statistics over valid tokens only; no padding enters any softmax.
+R4  block saliency for the inference mask: the dot product of the
+    mean-pooled dequantised Q and K blocks, the pooling idea of MSAD's global
+    guidance and the top-k idea of its local guidance ([QS-es] §2A,
+    [QS-ko] §2.1) -- score_ij = fl64(fl64(S_ij * (sq_i * sk_j)) / (n_i * n_j))
+    with S_ij the exact integer dot of the pooled code sums.
+R5  kept(i) = band(i) union top-k(i); the top-k ranks all key blocks by score
+    descending, ties to the lowest block index; lists ascending.
+R6  attention is non-causal; logits are sm_scale * sq_i * sk_j * (int dot).
+R7  SSAR ([QS-es] §2B, [QS-ko] §2.2): the first-order residual is the
+    difference of the attention OUTPUTS of full and sparse attention at a
+    refresh step; the second-order residual is the change of that residual
+    between consecutive refresh steps (0 at the first refresh); sparse steps
+    output sparse + r + dr.  Both residuals are stored in bf16.
+R8  the SVD projection of the second-order residual ([QS-es] §2B) is not
+    part of this path.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_to_f64",
+    "f64_to_bf16",
+    "default_sm_scale",
+    "block_bounds",
+    "quantize",
+    "block_scores",
+    "select_blocks",
+    "attention",
+    "attention_block_probs",
+    "full_kept_lists",
+    "ResidualState",
+    "refresh_step",
+    "sparse_step",
+]
+
+
+# ---------------------------------------------------------------------------
+# number formats
+# ---------------------------------------------------------------------------
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to float64; exact."""
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32).astype(np.float64)
+
+
+def _bf16_to_f32(bits) -> np.ndarray:
+    u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u.view(np.float32)
+
+
+def f64_to_bf16(x) -> np.ndarray:
+    """Round float64 to the nearest bf16 (ties to even); returns uint16 bits.
+
+    bf16 keeps 8 significant bits; below 2**-126 the spacing is fixed at
+    2**-133 (subnormals).  Values beyond the largest finite bf16 after
+    rounding become +-inf.
+    """
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros(x.shape, dtype=np.uint16)
+    fin = np.isfinite(x) & (x != 0)
+    m, e = np.frexp(np.where(fin, x, 1.0))  # x = m * 2**e, 0.5 <= |m| < 1
+    quantum = np.ldexp(1.0, np.maximum(e, -125) - 8)
+    y = np.where(fin, np.rint(x / quantum) * quantum, x)  # exact scaling by 2**k
+    with np.errstate(over="ignore"):
+        y32 = y.astype(np.float32)  # exact: y has <= 8 significant bits
+    bits = (y32.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    out[...] = bits
+    return out
+
+
+def default_sm_scale(head_dim: int) -> np.float32:
+    """Softmax scale 1/sqrt(D) as the fp32 value handed to the kernels."""
+    return np.float32(1.0 / np.sqrt(head_dim))
+
+
+def block_bounds(seq_len: int, block: int):
+    """[(start, end)] token ranges of the blocks; the last may be short (R3)."""
+    nb = -(-seq_len // block)
+    return [(i * block, min((i + 1) * block, seq_len)) for i in range(nb)]
+
+
+# ---------------------------------------------------------------------------
+# step 1: per-block symmetric int8 quantisation and pooled code sums
+# ---------------------------------------------------------------------------
+
+def quantize(x_bits, block: int):
+    """Quantise one of Q/K, bf16 bits [B, H, L, D] (R1, R2, R3).
+
+    Returns codes int8 [B, H, L, D], scales float32 [B, H, nb] and the pooled
+    code sums int64 [B, H, nb, D] (sum of a block's codes per channel).
+    """
+    x = _bf16_to_f32(x_bits)
+    B, H, L, D = x.shape
+    bounds = block_bounds(L, block)
+    codes = np.zeros((B, H, L, D), dtype=np.int8)
+    scales = np.zeros((B, H, len(bounds)), dtype=np.float32)
+    pooled = np.zeros((B, H, len(bounds), D), dtype=np.int64)
+    f127 = np.float32(127.0)
+    for b in range(B):
+        for h in range(H):
+            for i, (t0, t1) in enumerate(bounds):
+                xs = x[b, h, t0:t1]                      # float32 [n_i, D]
+                amax = np.max(np.abs(xs))                # exact
+                if amax == 0:
+                    continue                             # scale 0, codes 0
+                s = np.float32(amax / f127)              # IEEE fp32 division
+                q = np.rint(xs / s)                      # fp32 division, half-even
+                c = np.clip(q, -127, 127).astype(np.int8)
+                scales[b, h, i] = s
+                codes[b, h, t0:t1] = c
+                pooled[b, h, i] = c.astype(np.int64).sum(axis=0)
+    return codes, scales, pooled
+
+
+# ---------------------------------------------------------------------------
+# step 2: block saliency and top-k + band selection
+# ---------------------------------------------------------------------------
+
+def block_scores(pooled_q, scale_q, pooled_k, scale_k, seq_len: int, block: int):
+    """score[b, h, i, j] in float64 (R4).
+
+    S_ij is the exact integer dot product of pooled code sums (an fp64
+    matrix product of integer-valued arrays is exact here: every partial sum
+    is an integer below 2**53).  a_ij = sq_i * sk_j is exact in fp64.
+    """
+    n = np.array([t1 - t0 for t0, t1 in block_bounds(seq_len, block)], dtype=np.float64)
+    pq = np.asarray(pooled_q, dtype=np.float64)
+    pk = np.asarray(pooled_k, dtype=np.float64)
+    S = np.einsum("bhid,bhjd->bhij", pq, pk, optimize=True)
+    assert np.all(np.abs(S) < 2.0 ** 53)
+    a = (np.asarray(scale_q, np.float64)[..., :, None]
+         * np.asarray(scale_k, np.float64)[..., None, :])
+    b = S * a
+    c = n[:, None] * n[None, :]
+    return b / c
+
+
+def select_blocks(scores, topk: int, band, kmax: int):
+    """kept_idx int32 [B, H, nb, kmax] (ascending, padded with -1), kept_cnt (R5).
+
+    top-k orders all key blocks by score descending (IEEE comparison, so
+    -0 equals +0) and then by block index ascending, and keeps the first
+    min(topk, nb); band(i) = {i + o : 0 <= i + o < nb}.
+    """
+    B, H, nb, _ = scores.shape
+    k = min(int(topk), nb)
+    kept_idx = np.full((B, H, nb, kmax), -1, dtype=np.int32)
+    kept_cnt = np.zeros((B, H, nb), dtype=np.int32)
+    j = np.arange(nb)
+    for b in range(B):
+        for h in range(H):
+            # lexsort: last key is primary -> score descending, then j ascending
+            order = np.lexsort((np.broadcast_to(j, (nb, nb)), -scores[b, h]), axis=-1)
+            for i in range(nb):
+                chosen = set(order[i, :k].tolist())
+                chosen.update(i + o for o in band if 0 <= i + o < nb)
+                lst = sorted(chosen)
+                if len(lst) > kmax:
+                    raise ValueError("kmax too small for top-k plus band")
+                kept_idx[b, h, i, : len(lst)] = lst
+                kept_cnt[b, h, i] = len(lst)
+    return kept_idx, kept_cnt
+
+
+def full_kept_lists(B: int, H: int, nb: int):
+    """Kept lists that keep every block (dense attention)."""
+    idx = np.broadcast_to(np.arange(nb, dtype=np.int32), (B, H, nb, nb)).copy()
+    return idx, np.full((B, H, nb), nb, dtype=np.int32)
+
+
+# ---------------------------------------------------------------------------
+# step 3: block-sparse attention on the int8 codes
+# ---------------------------------------------------------------------------
+
+def _block_logits(q_codes, q_scales, k_codes, k_scales, b, h, i, blocks, block, seq_len,
+                  sm_scale):
+    t0, t1 = i * block, min((i + 1) * block, seq_len)
+    keys, sk = [], []
+    for j in blocks:
+        u0, u1 = j * block, min((j + 1) * block, seq_len)
+        keys.append(np.arange(u0, u1))
+        sk.append(np.full(u1 - u0, k_scales[b, h, j], dtype=np.float64))
+    keys = np.concatenate(keys)
+    sk = np.concatenate(sk)
+    dots = q_codes[b, h, t0:t1].astype(np.float64) @ k_codes[b, h, keys].astype(np.float64).T
+    z = (np.float64(sm_scale) * np.float64(q_scales[b, h, i])) * sk[None, :] * dots
+    return z, keys
+
+
+def attention_block_probs(q_codes, q_scales, k_codes, k_scales, b, h, i, blocks, block,
+                          seq_len, sm_scale):
+    """Softmax probabilities [n_i, n_keys] of query block i over ``blocks``."""
+    z, keys = _block_logits(q_codes, q_scales, k_codes, k_scales, b, h, i, blocks, block,
+                            seq_len, sm_scale)
+    z = z - z.max(axis=1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=1, keepdims=True), keys
+
+
+def attention(q_codes, q_scales, k_codes, k_scales, v_bits, kept_idx, kept_cnt, block: int,
+              sm_scale, which=None):
+    """Block-sparse attention output in float64 (R3, R6).
+
+    For each query block i the keys are the valid tokens of the blocks in
+    kept(i); logits z = sm_scale * sq_i * sk_j * (q_codes . k_codes); softmax
+    in fp64 (max-subtracted); O = P V with V the bf16 values widened to fp64.
+    A query block with an empty kept list outputs zeros.
+
+    ``which``: optional iterable of (b, h, i); then only those query blocks
+    are computed and a dict {(b, h, i): O_block} is returned.
+    """
+    B, H, L, D = q_codes.shape
+    nb = -(-L // block)
+    sel = which if which is not None else [(b, h, i) for b in range(B) for h in range(H)
+                                           for i in range(nb)]
+    res = {}
+    for (b, h, i) in sel:
+        t0, t1 = i * block, min((i + 1) * block, L)
+        blocks = [int(j) for j in kept_idx[b, h, i, : kept_cnt[b, h, i]]]
+        if not blocks:
+            res[(b, h, i)] = np.zeros((t1 - t0, D))
+            continue
+        p, keys = attention_block_probs(q_codes, q_scales, k_codes, k_scales, b, h, i,
+                                        blocks, block, L, sm_scale)
+        res[(b, h, i)] = p @ bf16_to_f64(v_bits[b, h, keys])
+    if which is not None:
+        return res
+    out = np.zeros((B, H, L, D), dtype=np.float64)
+    for (b, h, i), o in res.items():
+        out[b, h, i * block: i * block + o.shape[0]] = o
+    return out
+
+
+# ---------------------------------------------------------------------------
+# step 4: second-order sparse attention reparameterisation (SSAR)
+# ---------------------------------------------------------------------------
+
+class ResidualState:
+    """Per-layer residual cache ([QS-es] §2B): r and dr in bf16, has_prev."""
+
+    def __init__(self, shape):
+        self.r = np.zeros(shape, dtype=np.uint16)
+        self.dr = np.zeros(shape, dtype=np.uint16)
+        self.has_prev = False
+
+
+def refresh_step(state: ResidualState, o_full, o_sparse):
+    """Full-attention refresh step (R7).
+
+    rho = O_full - O_sparse (fp64); dr = bf16(rho - r_prev) if a previous
+    refresh exists, else 0; r = bf16(rho).  Returns O_full.
+    """
+    rho = np.asarray(o_full, np.float64) - np.asarray(o_sparse, np.float64)
+    if state.has_prev:
+        state.dr = f64_to_bf16(rho - bf16_to_f64(state.r))
+    else:
+        state.dr = np.zeros(rho.shape, dtype=np.uint16)
+    state.r = f64_to_bf16(rho)
+    state.has_prev = True
+    return np.asarray(o_full, np.float64)
+
+
+def sparse_step(state: ResidualState, o_sparse, order: int = 2):
+    """Sparse step output (R7): sparse + r + dr (order 2) or sparse + r (order 1)."""
+    if not state.has_prev:
+        raise RuntimeError("sparse step before any full-attention refresh")
+    out = np.asarray(o_sparse, np.float64) + bf16_to_f64(state.r)
+    if order == 2:
+        out = out + bf16_to_f64(state.dr)
+    return out

@@ -1,0 +1,89 @@
+"""Plant plausible mistakes in the oracle (on the CPU) and check a pin catches each.
+
+Each case swaps one oracle step for a subtly wrong variant (a dropped term, a
+wrong rounding, a flipped sign, a transposed operand, the wrong tie order)
+and runs the pin that should notice it; the pin must fail.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from oracle import qsa_oracle as Q
+from tests import test_oracle_attention as TA
+from tests import test_oracle_quantize as TQ
+from tests import test_oracle_residual as TR
+from tests import test_oracle_select as TS
+
+
+def _floor_quantize(x_bits, block):
+    codes, scales, pooled = ORIG_QUANTIZE(x_bits, block)
+    x = Q._bf16_to_f32(x_bits)
+    for i in range(scales.shape[-1]):
+        s = scales[0, 0, i]
+        if s > 0:
+            sl = slice(i * block, (i + 1) * block)
+            codes[0, 0, sl] = np.clip(np.floor(x[0, 0, sl] / s + np.float32(0.5)), -127, 127)
+    return codes, scales, pooled
+
+
+def _scores_no_count(pq, sq, pk, sk, L, block):
+    return ORIG_SCORES(pq, sq, pk, sk, L, block) * (block * block) / (block * block) * \
+        _counts(L, block)
+
+
+def _counts(L, block):
+    n = np.array([t1 - t0 for t0, t1 in Q.block_bounds(L, block)], np.float64)
+    return n[:, None] * n[None, :]
+
+
+def _select_high_ties(scores, topk, band, kmax):
+    nb = scores.shape[-1]
+    flipped = scores[..., ::-1]
+    idx, cnt = ORIG_SELECT(flipped, topk, [-o for o in band], kmax)
+    out = np.full_like(idx, -1)
+    for b in range(idx.shape[0]):
+        for h in range(idx.shape[1]):
+            for i in range(nb):
+                lst = sorted(nb - 1 - j for j in idx[b, h, nb - 1 - i, : cnt[b, h, nb - 1 - i]])
+                out[b, h, i, : len(lst)] = lst
+    return out, cnt[..., ::-1].copy()
+
+
+def _attention_no_kscale(qc, sq, kc, sk, v, idx, cnt, block, sm, which=None):
+    return ORIG_ATTN(qc, sq, kc, np.ones_like(sk) * sk.mean(), v, idx, cnt, block, sm, which)
+
+
+def _attention_transposed_v(qc, sq, kc, sk, v, idx, cnt, block, sm, which=None):
+    vt = v.copy()
+    vt[..., :, :] = v[..., ::-1, :]
+    return ORIG_ATTN(qc, sq, kc, sk, vt, idx, cnt, block, sm, which)
+
+
+def _refresh_flipped(state, o_full, o_sparse):
+    return ORIG_REFRESH(state, o_sparse, o_full)
+
+
+ORIG_QUANTIZE = Q.quantize
+ORIG_SCORES = Q.block_scores
+ORIG_SELECT = Q.select_blocks
+ORIG_ATTN = Q.attention
+ORIG_REFRESH = Q.refresh_step
+
+CASES = [
+    ("quantize", _floor_quantize, lambda: TQ.test_half_integer_ties_round_to_even()),
+    ("block_scores", _scores_no_count, lambda: TS.test_scores_against_exact_rationals()),
+    ("select_blocks", _select_high_ties,
+     lambda: TS.test_selection_against_brute_force_sort(12, 1, ())),
+    ("attention", _attention_no_kscale,
+     lambda: TA.test_sparse_attention_equals_masked_sdpa((1, 10, 30), 64, 64, 2, (0,))),
+    ("attention", _attention_transposed_v, lambda: TA.test_hand_examples_outputs("H2_band0")),
+    ("refresh_step", _refresh_flipped, lambda: TR.test_refresh_and_sparse_step_hand_values()),
+]
+
+
+@pytest.mark.parametrize("name,bad,pin", CASES, ids=[f"{c[0]}-{c[1].__name__}" for c in CASES])
+def test_planted_mistake_is_caught(monkeypatch, name, bad, pin):
+    monkeypatch.setattr(Q, name, bad)
+    monkeypatch.setattr(oracle, name, bad)
+    with pytest.raises(AssertionError):
+        pin()
