@@ -1,0 +1,194 @@
+/*
+ * qsa.h -- C ABI of the QuantSparse attention hot path on MI355X (gfx950).
+ *
+ * The method: video diffusion transformers run with 8-bit activations and
+ * attention sparsified down to ~15 % density, with the information lost by
+ * sparsification recovered by a cache of first- and second-order residuals
+ * ("QuantSparse: Comprehensively Compressing Video Diffusion Transformer with
+ * Model Quantization and Attention Sparsification", gist.science summaries
+ * es/paper/2509.23681 and ko/paper/2509.23681, technical summary §1, §2A, §2B,
+ * §4).  One attention layer step is:
+ *
+ *   sparse step : qsa_quantize(Q), qsa_quantize(K), qsa_select_blocks,
+ *                 qsa_sparse_attn (with the cached r, dr added in its epilogue)
+ *   refresh step: qsa_quantize(Q), qsa_quantize(K), qsa_select_blocks,
+ *                 qsa_full_attn_residual (updates r and dr, outputs full attention)
+ *
+ * Conventions for every entry point
+ *   - Tensors are DEVICE pointers, row-major and contiguous.  [B,H,L,D] means
+ *     batch, head, token, channel.  bf16 data are passed as uint16_t bit
+ *     patterns.  nb = ceil(seq_len / block) token blocks per (batch, head);
+ *     the last block is shorter when block does not divide seq_len.
+ *   - Every tensor pointer must be 16-byte aligned (QSA_ERR_ALIGN).
+ *   - The caller owns all memory.  The library allocates nothing, keeps no
+ *     state between calls and needs no workspace; calls are re-entrant.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
+ *     and runs asynchronously.  Argument errors are detected on the host
+ *     before anything is enqueued; device faults surface at the caller's next
+ *     synchronisation.
+ *   - Return value: QSA_OK (0) or a negative QSA_ERR_* code; the text of the
+ *     last error on the calling thread is available from qsa_last_error_detail.
+ *   - There is no fallback path: on a device other than gfx950 every compute
+ *     entry point returns QSA_ERR_DEVICE.
+ *   - NaN or Inf inputs give undefined (but memory-safe) results.
+ */
+#ifndef QSA_H_
+#define QSA_H_
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QSA_VERSION 10000 /* 1.0.0 */
+
+enum qsa_status {
+  QSA_OK = 0,
+  QSA_ERR_NULL = -1,   /* a required pointer is NULL */
+  QSA_ERR_SHAPE = -2,  /* head_dim or block not in {64,128}, a size < 1, or too large */
+  QSA_ERR_PARAM = -3,  /* a scalar argument is out of range */
+  QSA_ERR_ALIGN = -4,  /* a tensor pointer is not 16-byte aligned */
+  QSA_ERR_DEVICE = -5, /* no usable gfx950 device is current */
+  QSA_ERR_LAUNCH = -6  /* the HIP runtime reported an error when enqueuing */
+};
+
+/* Problem shape shared by all calls. */
+typedef struct qsa_dims {
+  int32_t batch;    /* B >= 1 */
+  int32_t heads;    /* H >= 1 */
+  int32_t seq_len;  /* L >= 1 */
+  int32_t head_dim; /* D: 64 or 128 */
+  int32_t block;    /* token block used for quantisation and sparsity: 64 or 128 */
+} qsa_dims;
+
+/* Largest number of key blocks qsa_select_blocks supports (nb). */
+#define QSA_MAX_BLOCKS 16384
+/* Largest number of band offsets. */
+#define QSA_MAX_BAND 8
+
+/*
+ * qsa_quantize -- per-block symmetric int8 quantisation of Q or K with pooled
+ * code sums (8-bit activations, technical summary §1 and §4; the pooled sums
+ * feed the block saliency of qsa_select_blocks, after the average-pooling
+ * idea of §2A).
+ *
+ * For every (b, h, block i) with tokens T_i (n_i valid tokens):
+ *   amax      = max |x| over T_i x D (exact, in fp32)
+ *   scale[i]  = amax / 127 in IEEE fp32 (round to nearest even); 0 if amax = 0
+ *   code[t,d] = clamp(rint(x[t,d] / scale[i]), -127, 127), the quotient an
+ *               IEEE fp32 division, rint rounding half to even; 0 if scale is 0
+ *   pooled[i,d] = sum over t in T_i of code[t,d]  (|pooled| <= 127 * block)
+ *
+ *   x      in : bf16 [B,H,L,D]
+ *   codes  out: int8 [B,H,L,D]
+ *   scales out: fp32 [B,H,nb]
+ *   pooled out: int32 [B,H,nb,D]
+ */
+int qsa_quantize(const qsa_dims* dims, const uint16_t* x, int8_t* codes, float* scales,
+                 int32_t* pooled, void* stream);
+
+/*
+ * qsa_select_blocks -- block-sparse attention mask: for every query block i
+ * keep its top-k key blocks by pooled saliency plus a fixed band of block
+ * offsets (attention sparsification to ~15 % density, technical summary §1
+ * and §4; saliency from average-pooled blocks and top-k salient keys after
+ * §2A's global and local guidance).
+ *
+ * For every (b, h, i) and every key block j:
+ *   S_ij     = sum_d pooled_q[i,d] * pooled_k[j,d]            (exact integer)
+ *   score_ij = fl64( fl64(S_ij * (double)scale_q[i] * (double)scale_k[j])
+ *                    / (n_i * n_j) )
+ *   top-k(i) = the first min(topk, nb) key blocks ordered by score descending
+ *              (IEEE comparison: -0 equals +0), ties to the lower index j
+ *   kept(i)  = top-k(i) union { i + o : o in band_offsets, 0 <= i + o < nb }
+ *
+ *   pooled_q, pooled_k in: int32 [B,H,nb,D]  (from qsa_quantize)
+ *   scale_q, scale_k   in: fp32 [B,H,nb]
+ *   topk               in: >= 0
+ *   band_offsets       in: HOST array of n_band block offsets (may be NULL
+ *                          when n_band = 0); 0 <= n_band <= QSA_MAX_BAND
+ *   kmax               in: row stride of kept_idx; must be >= min(nb, topk + n_band)
+ *   kept_idx          out: int32 [B,H,nb,kmax], ascending, unused slots = -1
+ *   kept_cnt          out: int32 [B,H,nb], number of kept blocks of each row
+ * QSA_ERR_PARAM if topk < 0, n_band outside [0, QSA_MAX_BAND], kmax too small,
+ * or a row could keep nothing (topk = 0 and no band offset 0).
+ * QSA_ERR_SHAPE if nb > QSA_MAX_BLOCKS.
+ */
+int qsa_select_blocks(const qsa_dims* dims, const int32_t* pooled_q, const float* scale_q,
+                      const int32_t* pooled_k, const float* scale_k, int32_t topk,
+                      const int32_t* band_offsets, int32_t n_band, int32_t kmax,
+                      int32_t* kept_idx, int32_t* kept_cnt, void* stream);
+
+/*
+ * qsa_sparse_attn -- block-sparse attention on int8 Q/K codes, with the
+ * second-order residual correction of sparse steps fused in its epilogue
+ * (sparse attention, technical summary §1; residual cache of §2B).
+ *
+ * For every query token t of block i, over the valid key tokens u of the
+ * blocks in kept(i) (the first kept_cnt entries of the row; entries outside
+ * [0, nb) are skipped):
+ *   z_tu = sm_scale * scale_q[i] * scale_k[j(u)] * (q_codes[t] . k_codes[u])
+ *   p    = softmax_u(z)   (fp32, online, max-subtracted)
+ *   o_t  = sum_u p_tu * v[u]   (P rounded to bf16, fp32 accumulation)
+ *   out_t = bf16(o_t + r_t + dr_t)   (r, dr each added only when non-NULL)
+ * A row with kept_cnt = 0 has o_t = 0.
+ *
+ *   q_codes, k_codes in: int8 [B,H,L,D];  q_scales, k_scales in: fp32 [B,H,nb]
+ *   v                in: bf16 [B,H,L,D]
+ *   kept_idx, kept_cnt in: as written by qsa_select_blocks with row stride kmax
+ *   sm_scale         in: finite, > 0 (usually 1/sqrt(D))
+ *   r, dr            in: bf16 [B,H,L,D] or NULL
+ *   out             out: bf16 [B,H,L,D]; must not alias any input
+ */
+int qsa_sparse_attn(const qsa_dims* dims, const int8_t* q_codes, const float* q_scales,
+                    const int8_t* k_codes, const float* k_scales, const uint16_t* v,
+                    const int32_t* kept_idx, const int32_t* kept_cnt, int32_t kmax,
+                    float sm_scale, const uint16_t* r, const uint16_t* dr, uint16_t* out,
+                    void* stream);
+
+/*
+ * qsa_full_attn_residual -- refresh step of the second-order sparse attention
+ * reparameterisation (technical summary §2B): full attention over ALL key
+ * blocks and sparse attention over kept(i), with the numerics of
+ * qsa_sparse_attn, computed in one pass over the key blocks; then
+ *   rho    = o_full - o_sparse                     (fp32)
+ *   dr     = has_prev ? bf16(rho - r_prev) : 0     (second-order residual)
+ *   r      = bf16(rho)                             (first-order residual)
+ *   out_full = bf16(o_full)
+ *
+ *   inputs as qsa_sparse_attn;  has_prev in: 0 or 1
+ *   r     in/out: bf16 [B,H,L,D]; read (r_prev) only when has_prev = 1
+ *   dr       out: bf16 [B,H,L,D]
+ *   out_full out: bf16 [B,H,L,D]
+ * r, dr and out_full must not alias each other or any input.
+ */
+int qsa_full_attn_residual(const qsa_dims* dims, const int8_t* q_codes, const float* q_scales,
+                           const int8_t* k_codes, const float* k_scales, const uint16_t* v,
+                           const int32_t* kept_idx, const int32_t* kept_cnt, int32_t kmax,
+                           float sm_scale, int32_t has_prev, uint16_t* r, uint16_t* dr,
+                           uint16_t* out_full, void* stream);
+
+/*
+ * qsa_apply_residual -- standalone sparse-step correction (technical summary
+ * §2B: cached residuals correct the sparse output at small cost):
+ *   out = bf16(sparse_out + r + dr)   elementwise in fp32; dr may be NULL
+ *
+ *   sparse_out, r, dr in: bf16 [B,H,L,D];  out: bf16 [B,H,L,D]
+ * out may alias sparse_out (in place); it must not alias r or dr.
+ */
+int qsa_apply_residual(const qsa_dims* dims, const uint16_t* sparse_out, const uint16_t* r,
+                       const uint16_t* dr, uint16_t* out, void* stream);
+
+/* Static text of a status code. */
+const char* qsa_status_string(int status);
+/* Text naming the cause of the last error on the calling thread ("" if none). */
+const char* qsa_last_error_detail(void);
+/* QSA_VERSION of the built library. */
+int qsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H_ */

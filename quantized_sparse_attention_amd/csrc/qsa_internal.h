@@ -1,0 +1,84 @@
+// Internal declarations shared by the C-ABI layer and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qsa.h"
+
+namespace qsa {
+
+// ---------------------------------------------------------------------------
+// vector types of the gfx950 MFMA builtins
+// ---------------------------------------------------------------------------
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+
+// bf16 bit pattern -> fp32 (exact)
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// two fp32 -> packed bf16 pair (round to nearest even; v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  v2f t = {a, b};
+  v2bf r = __builtin_convertvector(t, v2bf);
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Map a linear workgroup id onto a logical work index so that each of the 8
+// XCDs (which receive workgroups round-robin) walks one contiguous range of
+// logical indices.  A bijection on [0, n).
+__device__ __forceinline__ uint32_t xcd_contiguous(uint32_t p, uint32_t n) {
+  const uint32_t q = n >> 3, rem = n & 7u;
+  const uint32_t x = p & 7u, k = p >> 3;
+  return x * q + (x < rem ? x : rem) + k;
+}
+
+struct Band {
+  int32_t off[QSA_MAX_BAND];
+  int32_t n;
+};
+
+// ---------------------------------------------------------------------------
+// kernel launchers (one per entry point); arguments already validated
+// ---------------------------------------------------------------------------
+hipError_t launch_quantize(const qsa_dims& d, const uint16_t* x, int8_t* codes, float* scales,
+                           int32_t* pooled, hipStream_t s);
+
+hipError_t launch_select(const qsa_dims& d, const int32_t* pooled_q, const float* scale_q,
+                         const int32_t* pooled_k, const float* scale_k, int32_t topk,
+                         const Band& band, int32_t kmax, int32_t* kept_idx, int32_t* kept_cnt,
+                         hipStream_t s);
+
+struct AttnArgs {
+  const int8_t* q_codes;
+  const float* q_scales;
+  const int8_t* k_codes;
+  const float* k_scales;
+  const uint16_t* v;
+  const int32_t* kept_idx;
+  const int32_t* kept_cnt;
+  int32_t kmax;
+  float sm_scale;
+  // sparse step: optional residual inputs; refresh step: r in/out, dr out
+  const uint16_t* r_in;
+  const uint16_t* dr_in;
+  uint16_t* r_out;
+  uint16_t* dr_out;
+  int32_t has_prev;
+  uint16_t* out;
+};
+
+hipError_t launch_sparse_attn(const qsa_dims& d, const AttnArgs& a, hipStream_t s);
+hipError_t launch_full_attn_residual(const qsa_dims& d, const AttnArgs& a, hipStream_t s);
+
+hipError_t launch_apply_residual(const qsa_dims& d, const uint16_t* sparse_out,
+                                 const uint16_t* r, const uint16_t* dr, uint16_t* out,
+                                 hipStream_t s);
+
+}  // namespace qsa

@@ -1,0 +1,150 @@
+// Per-block symmetric int8 quantisation of Q or K plus pooled code sums.
+//
+// QuantSparse (gist.science/es/paper/2509.23681), technical summary §1 and §4:
+// activations are quantised to 8 bits; the pooled sums feed the block
+// saliency (average pooling of §2A's global guidance).
+//
+// One workgroup (4 waves) per (batch, head, token block).  HBM-bound: each
+// bf16 element is read once and each code written once, with 16-byte
+// coalesced loads (8 bf16 per lane) and 8-byte stores.
+//
+// Bit-exactness: the scale is an IEEE fp32 division amax / 127 and each code
+// the round-half-even of an IEEE fp32 division x / scale.  The library is
+// compiled with correctly rounded fp32 division, no fast-math and no FP
+// contraction in this file, and fp32 denormals preserved.
+#include "qsa_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace qsa {
+namespace {
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ int code_of(float x, float s) {
+  // s > 0; |x| <= amax so |x / s| <= 127 * (1 + 2^-23): the clamp only
+  // guards the contract.
+  float q = __builtin_rintf(x / s);
+  q = fminf(fmaxf(q, -127.0f), 127.0f);
+  return (int)q;
+}
+
+template <int BS, int D>
+__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x,
+                                                       int8_t* __restrict__ codes,
+                                                       float* __restrict__ scales,
+                                                       int32_t* __restrict__ pooled, int L,
+                                                       int nb) {
+  constexpr int CPR = D / 8;        // 16-byte chunks per token row
+  constexpr int RPP = 256 / CPR;    // rows covered per pass
+  constexpr int PASSES = BS / RPP;  // passes over the block
+  static_assert(BS % RPP == 0, "block must be a multiple of rows per pass");
+
+  __shared__ float s_amax[4];
+  __shared__ int32_t s_pool[4][D];
+
+  const uint32_t wg = blockIdx.x;
+  const uint32_t i = wg % (uint32_t)nb;
+  const uint64_t bh = wg / (uint32_t)nb;
+  const int t0 = (int)i * BS;
+  const int n = min(BS, L - t0);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int cc = tid % CPR;
+  const int r0 = tid / CPR;
+
+  const uint16_t* xb = x + (bh * (uint64_t)L + (uint64_t)t0) * D + cc * 8;
+  int8_t* cb = codes + (bh * (uint64_t)L + (uint64_t)t0) * D + cc * 8;
+
+  uint4 raw[PASSES];
+  float amax = 0.0f;
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = r0 + p * RPP;
+    if (row < n) {
+      raw[p] = *reinterpret_cast<const uint4*>(xb + (size_t)row * D);
+    } else {
+      raw[p] = make_uint4(0, 0, 0, 0);
+    }
+    const uint32_t w[4] = {raw[p].x, raw[p].y, raw[p].z, raw[p].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      amax = fmaxf(amax, fabsf(bf16_lo(w[e])));
+      amax = fmaxf(amax, fabsf(bf16_hi(w[e])));
+    }
+  }
+  amax = wave_max(amax);
+  if (lane == 0) s_amax[wave] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(s_amax[0], s_amax[1]), fmaxf(s_amax[2], s_amax[3]));
+  const float s = amax / 127.0f;  // IEEE division; 0 for an all-zero block
+
+  int psum[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) psum[e] = 0;
+
+#pragma unroll
+  for (int p = 0; p < PASSES; ++p) {
+    const int row = r0 + p * RPP;
+    if (row < n) {
+      const uint32_t w[4] = {raw[p].x, raw[p].y, raw[p].z, raw[p].w};
+      int c[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        c[2 * e] = s > 0.0f ? code_of(bf16_lo(w[e]), s) : 0;
+        c[2 * e + 1] = s > 0.0f ? code_of(bf16_hi(w[e]), s) : 0;
+      }
+      uint32_t lo = 0, hi = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        lo |= (uint32_t)(c[e] & 0xff) << (8 * e);
+        hi |= (uint32_t)(c[4 + e] & 0xff) << (8 * e);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) psum[e] += c[e];
+      *reinterpret_cast<uint2*>(cb + (size_t)row * D) = make_uint2(lo, hi);
+    }
+  }
+
+  // reduce the per-lane channel sums over lanes holding the same channels
+#pragma unroll
+  for (int o = CPR; o < 64; o <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) psum[e] += __shfl_xor(psum[e], o, 64);
+  }
+  if (lane < CPR) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) s_pool[wave][lane * 8 + e] = psum[e];
+  }
+  __syncthreads();
+  const uint64_t blk = bh * (uint64_t)nb + i;
+  if (tid < D) {
+    pooled[blk * D + tid] = s_pool[0][tid] + s_pool[1][tid] + s_pool[2][tid] + s_pool[3][tid];
+  }
+  if (tid == 0) scales[blk] = s;
+}
+
+template <int BS, int D>
+hipError_t launch_t(const qsa_dims& d, const uint16_t* x, int8_t* codes, float* scales,
+                    int32_t* pooled, hipStream_t s) {
+  const int nb = (d.seq_len + BS - 1) / BS;
+  const uint64_t n_wg = (uint64_t)d.batch * d.heads * nb;
+  hipLaunchKernelGGL((quantize_kernel<BS, D>), dim3((uint32_t)n_wg), dim3(256), 0, s, x, codes,
+                     scales, pooled, d.seq_len, nb);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const qsa_dims& d, const uint16_t* x, int8_t* codes, float* scales,
+                           int32_t* pooled, hipStream_t s) {
+  if (d.block == 64 && d.head_dim == 128) return launch_t<64, 128>(d, x, codes, scales, pooled, s);
+  if (d.block == 64 && d.head_dim == 64) return launch_t<64, 64>(d, x, codes, scales, pooled, s);
+  if (d.block == 128 && d.head_dim == 128) return launch_t<128, 128>(d, x, codes, scales, pooled, s);
+  return launch_t<128, 64>(d, x, codes, scales, pooled, s);
+}
+
+}  // namespace qsa

@@ -1,0 +1,254 @@
+// Block saliency and top-k + band selection of the block-sparse mask.
+//
+// QuantSparse (gist.science/es/paper/2509.23681), technical summary §1 and §4
+// (attention kept at ~15 % density) and §2A (average-pooled global guidance,
+// top-k salient local guidance): every query block keeps the key blocks whose
+// mean-pooled dequantised codes score highest, plus a fixed band of offsets.
+//
+// One workgroup (4 waves) per (batch*head, tile of TR query blocks).
+//  1. Exact integer scores S_ij = sum_d Pq[i,d] Pk[j,d] on the int8 MFMA:
+//     each pooled sum P (|P| <= 127*128) is split into int8 digits
+//     P = 128*hi + lo with lo in [0,127], hi in [-127,127], and
+//       S = 16384*sum(hi*hi') + 128*(sum(hi*lo') + sum(lo*hi')) + sum(lo*lo')
+//     where every partial sum fits int32 and the recombination is exact in
+//     fp64 (all values are integers below 2^53).
+//  2. score = fl64(fl64(S * sq*sk) / (n_i*n_j)) in IEEE fp64, mapped to an
+//     order-preserving uint64 key (-0 canonicalised to +0), kept in LDS.
+//  3. Per row (one wave), an 8-pass radix select over the keys finds the
+//     k-th largest key T and how many keys equal to T are taken.
+//  4. Ascending compaction with wave ballots: j is kept if key > T, or
+//     key == T and fewer than `take` lower-indexed ties precede it, or
+//     j - i is a band offset.
+#include "qsa_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace qsa {
+namespace {
+
+constexpr int kSelThreads = 256;
+constexpr int kHist = 256;
+
+__device__ __forceinline__ uint64_t order_key(double score) {
+  uint64_t b = (uint64_t)__double_as_longlong(score);
+  if (score == 0.0) b = 0;  // -0 and +0 are equal scores
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+// Digits of 16 consecutive pooled sums, packed 4 per 32-bit word.
+__device__ __forceinline__ void split16(const int32_t* __restrict__ p, bool valid, v4i& hi,
+                                        v4i& lo) {
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t h = 0, l = 0;
+    if (valid) {
+      const int4 v = *reinterpret_cast<const int4*>(p + 4 * w);
+      const int vv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int hv = vv[e] >> 7;   // floor division by 128
+        const int lv = vv[e] & 127;  // remainder in [0, 127]
+        h |= (uint32_t)(hv & 0xff) << (8 * e);
+        l |= (uint32_t)lv << (8 * e);
+      }
+    }
+    hi[w] = (int)h;
+    lo[w] = (int)l;
+  }
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) {
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+template <int D>
+__global__ __launch_bounds__(kSelThreads) void select_kernel(
+    const int32_t* __restrict__ pq, const float* __restrict__ sq, const int32_t* __restrict__ pk,
+    const float* __restrict__ sk, int L, int bs, int nb, int TR, int topk, Band band, int kmax,
+    int32_t* __restrict__ kept_idx, int32_t* __restrict__ kept_cnt) {
+  extern __shared__ uint64_t s_keys[];  // [TR][nb]
+  __shared__ uint32_t s_hist[4][kHist];
+
+  constexpr int KSTEPS = D / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t bh = blockIdx.y;
+  const int r0 = blockIdx.x * TR;
+  const int32_t* pqh = pq + bh * (uint64_t)nb * D;
+  const int32_t* pkh = pk + bh * (uint64_t)nb * D;
+  const float* sqh = sq + bh * (uint64_t)nb;
+  const float* skh = sk + bh * (uint64_t)nb;
+
+  // ---- 1+2: scores of TR query blocks against every key block -------------
+  const int g = lane >> 4;  // k-group of the 16x16x64 MFMA operands
+  const int arow = lane & 15;
+  v4i a_hi[KSTEPS], a_lo[KSTEPS];
+  {
+    const int i = r0 + arow;
+    const bool ok = arow < TR && i < nb;
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks)
+      split16(pqh + (uint64_t)(ok ? i : 0) * D + ks * 64 + g * 16, ok, a_hi[ks], a_lo[ks]);
+  }
+  const int n_ctiles = (nb + 15) / 16;
+  for (int ct = wave; ct < n_ctiles; ct += 4) {
+    const int j = ct * 16 + (lane & 15);
+    const bool okj = j < nb;
+    v4i hh = {0, 0, 0, 0}, mid = {0, 0, 0, 0}, ll = {0, 0, 0, 0};
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      v4i b_hi, b_lo;
+      split16(pkh + (uint64_t)(okj ? j : 0) * D + ks * 64 + g * 16, okj, b_hi, b_lo);
+      hh = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_hi[ks], b_hi, hh, 0, 0, 0);
+      mid = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_hi[ks], b_lo, mid, 0, 0, 0);
+      mid = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_lo[ks], b_hi, mid, 0, 0, 0);
+      ll = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_lo[ks], b_lo, ll, 0, 0, 0);
+    }
+    if (okj) {
+      const double skj = (double)skh[j];
+      const int nj = min(bs, L - j * bs);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = 4 * g + r;  // accumulator row of this lane
+        const int i = r0 + row;
+        if (row < TR && i < nb) {
+          const double S = (double)hh[r] * 16384.0 + (double)mid[r] * 128.0 + (double)ll[r];
+          const double a = (double)sqh[i] * skj;
+          const double b = S * a;
+          const double c = (double)min(bs, L - i * bs) * (double)nj;
+          s_keys[(uint64_t)row * nb + j] = order_key(b / c);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // ---- 3+4: per-row radix select and ascending compaction -----------------
+  const int k_eff = min(topk, nb);
+  const int rows_per_wave = (TR + 3) / 4;
+  for (int it = 0; it < rows_per_wave; ++it) {
+    const int row = it * 4 + wave;
+    const int i = r0 + row;
+    const bool active = row < TR && i < nb;
+    const uint64_t* keys = s_keys + (uint64_t)(active ? row : 0) * nb;
+
+    uint64_t prefix = 0, pmask = 0;
+    int need = k_eff;  // how many still to take among keys matching prefix
+    const bool do_select = active && k_eff > 0 && k_eff < nb;
+    for (int pass = 0; pass < 8; ++pass) {
+      const int shift = 56 - 8 * pass;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) s_hist[wave][lane * 4 + e] = 0;
+      __syncthreads();
+      if (do_select) {
+        for (int j = lane; j < nb; j += 64) {
+          const uint64_t key = keys[j];
+          if ((key & pmask) == prefix) atomicAdd(&s_hist[wave][(key >> shift) & 0xff], 1u);
+        }
+      }
+      __syncthreads();
+      if (do_select) {
+        uint32_t c[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) c[e] = s_hist[wave][lane * 4 + e];
+        const uint32_t mine = c[0] + c[1] + c[2] + c[3];
+        // inclusive suffix sum over lanes (lanes >= this one)
+        uint32_t suf = mine;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t v = __shfl_down(suf, o, 64);
+          if (lane + o < 64) suf += v;
+        }
+        const uint32_t above = suf - mine;  // keys in higher digit bins
+        const bool here = above < (uint32_t)need && (uint32_t)need <= suf;
+        int digit = 0;
+        uint32_t cnt_above = above;
+        if (here) {
+          for (int e = 3; e >= 0; --e) {
+            if (cnt_above + c[e] >= (uint32_t)need) {
+              digit = lane * 4 + e;
+              break;
+            }
+            cnt_above += c[e];
+          }
+        }
+        const uint64_t who = __ballot(here);
+        const int src = __ffsll((unsigned long long)who) - 1;
+        digit = __shfl(digit, src, 64);
+        cnt_above = __shfl(cnt_above, src, 64);
+        need -= (int)cnt_above;
+        prefix |= (uint64_t)digit << shift;
+        pmask |= 0xffull << shift;
+      }
+    }
+
+    if (active) {
+      int32_t* out = kept_idx + ((bh * (uint64_t)nb) + i) * (uint64_t)kmax;
+      int pos = 0, ties_seen = 0;
+      for (int base = 0; base < nb; base += 64) {
+        const int j = base + lane;
+        const bool valid = j < nb;
+        const uint64_t key = valid ? keys[j] : 0;
+        bool in_band = false;
+        for (int b = 0; b < band.n; ++b) in_band |= (j - i) == band.off[b];
+        bool sel;
+        if (k_eff == 0) {
+          sel = false;
+        } else if (k_eff == nb) {
+          sel = true;
+        } else {
+          const bool eq = key == prefix;
+          const uint64_t eqb = __ballot(valid && eq);
+          const int rank = ties_seen + __popcll(eqb & lanemask_lt(lane));
+          sel = key > prefix || (eq && rank < need);
+          ties_seen += __popcll(eqb);
+        }
+        sel = valid && (sel || in_band);
+        const uint64_t selb = __ballot(sel);
+        const int p = pos + __popcll(selb & lanemask_lt(lane));
+        if (sel && p < kmax) out[p] = j;
+        pos += __popcll(selb);
+      }
+      for (int p = pos + lane; p < kmax; p += 64) out[p] = -1;
+      if (lane == 0) kept_cnt[bh * (uint64_t)nb + i] = min(pos, kmax);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_select(const qsa_dims& d, const int32_t* pooled_q, const float* scale_q,
+                         const int32_t* pooled_k, const float* scale_k, int32_t topk,
+                         const Band& band, int32_t kmax, int32_t* kept_idx, int32_t* kept_cnt,
+                         hipStream_t s) {
+  const int nb = (d.seq_len + d.block - 1) / d.block;
+  const size_t lds_cap = 160 * 1024 - sizeof(uint32_t) * 4 * kHist - 256;
+  int TR = 16;
+  while (TR > 1 && (size_t)TR * nb * sizeof(uint64_t) > lds_cap) TR >>= 1;
+  const size_t lds = (size_t)TR * nb * sizeof(uint64_t);
+  if (lds > lds_cap) return hipErrorInvalidValue;
+  const dim3 grid((nb + TR - 1) / TR, (uint32_t)(d.batch * d.heads));
+  if (d.head_dim == 128) {
+    static bool attr = false;
+    if (!attr) {
+      (void)hipFuncSetAttribute((const void*)select_kernel<128>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_cap);
+      attr = true;
+    }
+    hipLaunchKernelGGL(select_kernel<128>, grid, dim3(kSelThreads), lds, s, pooled_q, scale_q,
+                       pooled_k, scale_k, d.seq_len, d.block, nb, TR, topk, band, kmax,
+                       kept_idx, kept_cnt);
+  } else {
+    static bool attr = false;
+    if (!attr) {
+      (void)hipFuncSetAttribute((const void*)select_kernel<64>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_cap);
+      attr = true;
+    }
+    hipLaunchKernelGGL(select_kernel<64>, grid, dim3(kSelThreads), lds, s, pooled_q, scale_q,
+                       pooled_k, scale_k, d.seq_len, d.block, nb, TR, topk, band, kmax,
+                       kept_idx, kept_cnt);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qsa

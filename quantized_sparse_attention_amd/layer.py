@@ -1,0 +1,83 @@
+"""Per-layer step driver of the QuantSparse attention hot path.
+
+Holds one layer's residual cache across denoising steps (QuantSparse,
+gist.science/es/paper/2509.23681, technical summary §2B: first- and
+second-order residuals cached and reused on sparse steps) and issues the
+C-ABI calls of one step on the current torch stream.  All arithmetic runs in
+libqsa.so.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+from . import binding as B
+
+
+@dataclass
+class QSAConfig:
+    block: int = 64
+    topk: int = 1
+    band: tuple = (0,)
+    sm_scale: float | None = None
+    order: int = 2  # 2: sparse + r + dr; 1: sparse + r (first-order reuse)
+
+
+@dataclass
+class StepBuffers:
+    """Outputs of one step, kept for inspection (codes, scales, masks)."""
+    q_codes: torch.Tensor = None
+    q_scales: torch.Tensor = None
+    q_pooled: torch.Tensor = None
+    k_codes: torch.Tensor = None
+    k_scales: torch.Tensor = None
+    k_pooled: torch.Tensor = None
+    kept_idx: torch.Tensor = None
+    kept_cnt: torch.Tensor = None
+
+
+class QuantSparseAttention:
+    """One attention layer: refresh steps update the residual cache, sparse
+    steps add it to the block-sparse output."""
+
+    def __init__(self, cfg: QSAConfig):
+        self.cfg = cfg
+        self.r = None
+        self.dr = None
+        self.has_prev = False
+        self.last = StepBuffers()
+
+    def reset(self):
+        self.r = self.dr = None
+        self.has_prev = False
+
+    def state_dict(self):
+        return {"r": self.r, "dr": self.dr, "has_prev": self.has_prev}
+
+    def load_state_dict(self, sd):
+        self.r, self.dr, self.has_prev = sd["r"], sd["dr"], bool(sd["has_prev"])
+
+    def _front(self, q, k):
+        c = self.cfg
+        qc, qs, qp = B.qsa_quantize(q, c.block)
+        kc, ks, kp = B.qsa_quantize(k, c.block)
+        idx, cnt = B.qsa_select_blocks(qp, qs, kp, ks, q.shape[2], c.block, c.topk, c.band)
+        self.last = StepBuffers(qc, qs, qp, kc, ks, kp, idx, cnt)
+        return qc, qs, kc, ks, idx, cnt
+
+    def step(self, q, k, v, refresh: bool) -> torch.Tensor:
+        c = self.cfg
+        qc, qs, kc, ks, idx, cnt = self._front(q, k)
+        if refresh:
+            if self.r is None:
+                self.r = torch.zeros_like(v)
+                self.dr = torch.zeros_like(v)
+            out = B.qsa_full_attn_residual(qc, qs, kc, ks, v, idx, cnt, c.block, self.r, self.dr,
+                                           self.has_prev, c.sm_scale)
+            self.has_prev = True
+            return out
+        if self.r is None:
+            raise RuntimeError("sparse step before any full-attention refresh step")
+        return B.qsa_sparse_attn(qc, qs, kc, ks, v, idx, cnt, c.block, c.sm_scale, r=self.r,
+                                 dr=self.dr if c.order == 2 else None)

@@ -1,0 +1,157 @@
+"""The C ABI library loads, exports every declared symbol, and validates its
+arguments on the host (exact status codes, nothing launched).  Runs without a
+GPU: fake device pointers are only ever passed where validation must reject
+them first, and the checks that rely on "no device present" skip on a GPU machine.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from quantized_sparse_attention_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+
+def _gpu_present() -> bool:
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+NO_GPU = not _gpu_present()
+needs_no_gpu = pytest.mark.skipif(not NO_GPU, reason="uses fake device pointers")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.skip("libqsa.so not built")
+    return B.load_library()
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_[a-z_]+)\s*\(", txt)))
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ("qsa_quantize", "qsa_select_blocks", "qsa_sparse_attn", "qsa_full_attn_residual",
+              "qsa_apply_residual", "qsa_status_string", "qsa_last_error_detail", "qsa_version"):
+        assert n in names
+    assert set(names) == set(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (qsa_\w+)", out))
+    for n in _declared():
+        assert n in exported, n
+        assert hasattr(lib, n)
+
+
+def test_version_and_status_strings(lib):
+    assert lib.qsa_version() == 10000
+    for st in (0, -1, -2, -3, -4, -5, -6):
+        assert lib.qsa_status_string(st)
+    assert b"unknown" in lib.qsa_status_string(-99)
+
+
+def _d(B_=1, H=2, L=128, D=64, bs=64):
+    return ctypes.byref(B.qsa_dims(B_, H, L, D, bs))
+
+
+P = [ctypes.c_void_p(0x1000 * (i + 1)) for i in range(12)]  # aligned, never dereferenced
+
+
+def _q(lib, dims, ptrs=None):
+    p = ptrs or P[:4]
+    return lib.qsa_quantize(dims, *p, None)
+
+
+def test_quantize_validation(lib):
+    assert lib.qsa_quantize(None, *P[:4], None) == B.QSA_ERR_NULL
+    assert _q(lib, _d(D=96)) == B.QSA_ERR_SHAPE
+    assert _q(lib, _d(bs=32)) == B.QSA_ERR_SHAPE
+    assert _q(lib, _d(B_=0)) == B.QSA_ERR_SHAPE
+    assert _q(lib, _d(L=0)) == B.QSA_ERR_SHAPE
+    assert _q(lib, _d(H=-1)) == B.QSA_ERR_SHAPE
+    assert _q(lib, _d(), [None] + P[1:4]) == B.QSA_ERR_NULL
+    assert b"x is NULL" in lib.qsa_last_error_detail()
+    assert _q(lib, _d(), P[:3] + [None]) == B.QSA_ERR_NULL
+    assert _q(lib, _d(), [ctypes.c_void_p(0x1008)] + P[1:4]) == B.QSA_ERR_ALIGN
+    assert _q(lib, _d(B_=1 << 20, H=1 << 10, L=1 << 12, bs=64)) == B.QSA_ERR_SHAPE
+
+
+@needs_no_gpu
+def test_valid_arguments_reach_the_device_check(lib):
+    assert _q(lib, _d()) == B.QSA_ERR_DEVICE
+    band = (ctypes.c_int32 * 1)(0)
+    assert lib.qsa_select_blocks(_d(), *P[:4], 1, band, 1, 2, P[4], P[5], None) == B.QSA_ERR_DEVICE
+    assert lib.qsa_sparse_attn(_d(), *P[:7], 2, ctypes.c_float(0.125), None, None, P[7],
+                               None) == B.QSA_ERR_DEVICE
+    assert lib.qsa_full_attn_residual(_d(), *P[:7], 2, ctypes.c_float(0.125), 1, P[7], P[8], P[9],
+                                      None) == B.QSA_ERR_DEVICE
+    assert lib.qsa_apply_residual(_d(), P[0], P[1], None, P[0], None) == B.QSA_ERR_DEVICE
+
+
+def _sel(lib, topk=1, band=(0,), n_band=None, kmax=2, dims=None, ptrs=None):
+    arr = (ctypes.c_int32 * max(1, len(band)))(*band) if band is not None else None
+    nb_ = len(band) if n_band is None and band is not None else (n_band or 0)
+    p = ptrs or P[:6]
+    return lib.qsa_select_blocks(dims or _d(), p[0], p[1], p[2], p[3], topk, arr, nb_, kmax, p[4],
+                                 p[5], None)
+
+
+def test_select_validation(lib):
+    assert _sel(lib, topk=-1) == B.QSA_ERR_PARAM
+    assert _sel(lib, band=tuple(range(9))) == B.QSA_ERR_PARAM
+    assert _sel(lib, band=None, n_band=2) == B.QSA_ERR_NULL
+    assert _sel(lib, topk=0, band=(1,)) == B.QSA_ERR_PARAM           # a row could keep nothing
+    assert _sel(lib, topk=2, band=(0,), kmax=1) == B.QSA_ERR_PARAM    # kmax < min(nb, k+band)
+    assert _sel(lib, topk=1, kmax=0) == B.QSA_ERR_PARAM
+    assert _sel(lib, ptrs=[P[0], None] + P[2:6]) == B.QSA_ERR_NULL
+    assert _sel(lib, ptrs=P[:5] + [ctypes.c_void_p(0x2004)]) == B.QSA_ERR_ALIGN
+    big = _d(L=64 * (B.QSA_MAX_BLOCKS + 1))
+    assert _sel(lib, dims=big, kmax=2) == B.QSA_ERR_SHAPE
+
+
+def test_attention_validation(lib):
+    f = ctypes.c_float
+
+    def sp(sm=0.125, kmax=2, ptrs=None, out=P[7]):
+        p = ptrs or P[:7]
+        return lib.qsa_sparse_attn(_d(), *p, kmax, f(sm), None, None, out, None)
+
+    assert sp(sm=0.0) == B.QSA_ERR_PARAM
+    assert sp(sm=-1.0) == B.QSA_ERR_PARAM
+    assert sp(sm=float("nan")) == B.QSA_ERR_PARAM
+    assert sp(sm=float("inf")) == B.QSA_ERR_PARAM
+    assert sp(kmax=0) == B.QSA_ERR_PARAM
+    assert sp(out=None) == B.QSA_ERR_NULL
+    assert sp(ptrs=P[:6] + [None]) == B.QSA_ERR_NULL
+    assert lib.qsa_sparse_attn(_d(), *P[:7], 2, f(0.1), ctypes.c_void_p(0x3002), None, P[7],
+                               None) == B.QSA_ERR_ALIGN
+    assert lib.qsa_full_attn_residual(_d(), *P[:7], 2, f(0.1), 2, P[7], P[8], P[9],
+                                      None) == B.QSA_ERR_PARAM
+    assert lib.qsa_full_attn_residual(_d(), *P[:7], 2, f(0.1), 0, None, P[8], P[9],
+                                      None) == B.QSA_ERR_NULL
+    assert lib.qsa_apply_residual(_d(), P[0], None, None, P[0], None) == B.QSA_ERR_NULL
+    assert lib.qsa_apply_residual(_d(D=80), P[0], P[1], None, P[0], None) == B.QSA_ERR_SHAPE
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros((1, 1, 64, 64), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        B.qsa_quantize(x, 64)
+    with pytest.raises(TypeError):
+        B.qsa_quantize(x.float(), 64)

@@ -1,0 +1,299 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Bit-exact: int8 codes, fp32 scales, pooled sums and kept block lists.
+Within tolerance (rel-L2 <= 5e-3 and max-abs <= 2e-2 against fp64): every
+bf16 attention output, and the residuals relative to the full output.
+Shapes span several tiles and a ragged tail at sizes the oracle finishes in
+seconds.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import qsa_gen
+from quantized_sparse_attention_amd import binding as B
+from tests.gpu_util import (assert_close, dev_bf16, host_bits, host_f64, oracle_front, rel_l2)
+
+pytestmark = pytest.mark.gpu
+
+TINY = qsa_gen.get_workload("tiny")
+CFGS = {
+    "tiny": (TINY, {}),
+    "tail64_d128": (TINY.with_(grid=(1, 10, 30), block=64, head_dim=128, outlier_channels=3,
+                               outlier_gain=10.0), dict(topk=2, band=(0,))),
+    "tail128_d128": (TINY.with_(grid=(1, 1, 333), block=128, head_dim=128),
+                     dict(topk=1, band=(-1, 0))),
+    "d64_b128": (TINY.with_(grid=(3, 7, 11), block=128, head_dim=64), dict(topk=1, band=())),
+    "batch2_h3": (TINY.with_(batch=2, heads=3, grid=(2, 12, 40), block=64, head_dim=128,
+                             noise_std=0.3, outlier_channels=3, outlier_gain=10.0),
+                  dict(topk=3, band=(0,))),
+    "wide_band": (TINY.with_(grid=(1, 20, 64), block=64, head_dim=128),
+                  dict(topk=4, band=(-3, -1, 0, 1, 3))),
+}
+
+
+def _gpu_front(x, w, topk, band, kmax):
+    q, k = dev_bf16(x["q"]), dev_bf16(x["k"])
+    qc, qs, qp = B.qsa_quantize(q, w.block)
+    kc, ks, kp = B.qsa_quantize(k, w.block)
+    idx, cnt = B.qsa_select_blocks(qp, qs, kp, ks, w.seq_len, w.block, topk, band, kmax)
+    torch.cuda.synchronize()
+    return dict(qc=qc, qs=qs, qp=qp, kc=kc, ks=ks, kp=kp, idx=idx, cnt=cnt)
+
+
+def _setup(name, step=0):
+    w, kw = CFGS[name]
+    x = qsa_gen.make_qkv(w, step)
+    o = oracle_front(x, w, **kw)
+    g = _gpu_front(x, w, o["topk"], o["band"], o["kmax"])
+    return w, x, o, g
+
+
+@pytest.mark.parametrize("name", list(CFGS))
+def test_quantize_bit_exact(name):
+    w, x, o, g = _setup(name)
+    assert np.array_equal(g["qc"].cpu().numpy(), o["qc"])
+    assert np.array_equal(g["kc"].cpu().numpy(), o["kc"])
+    assert np.array_equal(g["qs"].cpu().numpy().view(np.uint32), o["sq"].view(np.uint32))
+    assert np.array_equal(g["ks"].cpu().numpy().view(np.uint32), o["sk"].view(np.uint32))
+    assert np.array_equal(g["qp"].cpu().numpy(), o["pq"])
+    assert np.array_equal(g["kp"].cpu().numpy(), o["pk"])
+
+
+@pytest.mark.parametrize("name", list(CFGS))
+def test_select_bit_exact(name):
+    w, x, o, g = _setup(name)
+    assert np.array_equal(g["cnt"].cpu().numpy(), o["cnt"])
+    assert np.array_equal(g["idx"].cpu().numpy(), o["idx"])
+
+
+def _oracle_attn(o, x, w, kept=None):
+    idx, cnt = (o["idx"], o["cnt"]) if kept is None else kept
+    return oracle.attention(o["qc"], o["sq"], o["kc"], o["sk"], x["v"], idx, cnt, w.block,
+                            oracle.default_sm_scale(w.head_dim))
+
+
+@pytest.mark.parametrize("name", list(CFGS))
+def test_sparse_attn_parity(name):
+    w, x, o, g = _setup(name)
+    v = dev_bf16(x["v"])
+    out = B.qsa_sparse_attn(g["qc"], g["qs"], g["kc"], g["ks"], v, g["idx"], g["cnt"], w.block)
+    want = _oracle_attn(o, x, w)
+    assert_close(host_f64(out), want, what=f"{name} sparse")
+    # residual inputs fused in the epilogue
+    rng = np.random.default_rng(1)
+    r = qsa_gen.f32_to_bf16_bits(rng.standard_normal(x["v"].shape).astype(np.float32) * 0.05)
+    dr = qsa_gen.f32_to_bf16_bits(rng.standard_normal(x["v"].shape).astype(np.float32) * 0.01)
+    out2 = B.qsa_sparse_attn(g["qc"], g["qs"], g["kc"], g["ks"], v, g["idx"], g["cnt"], w.block,
+                             r=dev_bf16(r), dr=dev_bf16(dr))
+    want2 = want + oracle.bf16_to_f64(r) + oracle.bf16_to_f64(dr)
+    assert_close(host_f64(out2), want2, what=f"{name} sparse+r+dr")
+    out1 = B.qsa_sparse_attn(g["qc"], g["qs"], g["kc"], g["ks"], v, g["idx"], g["cnt"], w.block,
+                             r=dev_bf16(r))
+    assert_close(host_f64(out1), want + oracle.bf16_to_f64(r), what=f"{name} sparse+r")
+
+
+@pytest.mark.parametrize("name", list(CFGS))
+@pytest.mark.parametrize("has_prev", [0, 1])
+def test_refresh_parity(name, has_prev):
+    w, x, o, g = _setup(name)
+    v = dev_bf16(x["v"])
+    shape = x["v"].shape
+    rng = np.random.default_rng(2)
+    r_prev = qsa_gen.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32) * 0.02)
+    r = dev_bf16(r_prev)
+    dr = torch.zeros_like(v)
+    out = B.qsa_full_attn_residual(g["qc"], g["qs"], g["kc"], g["ks"], v, g["idx"], g["cnt"],
+                                   w.block, r, dr, has_prev)
+    o_sp = _oracle_attn(o, x, w)
+    o_full = _oracle_attn(o, x, w, oracle.full_kept_lists(w.batch, w.heads, w.n_blocks))
+    st = oracle.ResidualState(shape)
+    if has_prev:
+        st.r, st.has_prev = r_prev.copy(), True
+    oracle.refresh_step(st, o_full, o_sp)
+    assert_close(host_f64(out), o_full, what=f"{name} full")
+    # r and dr are stored in bf16 by both sides; compare each against its
+    # unrounded fp64 value (a bf16 rounding flip is not an error of the path).
+    # They are cancellations, so the relative measure uses the full output.
+    rho = o_full - o_sp
+    dr_ref = rho - oracle.bf16_to_f64(r_prev) if has_prev else np.zeros_like(rho)
+    scale = np.linalg.norm(o_full)
+    for got, ref, nm in ((host_f64(r), rho, "r"), (host_f64(dr), dr_ref, "dr")):
+        err = got - ref
+        assert np.linalg.norm(err) / scale <= 5e-3, (nm, np.linalg.norm(err) / scale)
+        assert np.max(np.abs(err)) <= 2e-2, (nm, np.max(np.abs(err)))
+    if not has_prev:
+        assert np.all(host_bits(dr) == 0)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tail64_d128", "tail128_d128"])
+def test_refresh_sparse_part_matches_sparse_kernel(name):
+    # The refresh kernel's sparse partition uses the sparse kernel's numerics:
+    # r + (sparse output) reproduces the full output up to bf16 rounding.
+    w, x, o, g = _setup(name)
+    v = dev_bf16(x["v"])
+    sp = B.qsa_sparse_attn(g["qc"], g["qs"], g["kc"], g["ks"], v, g["idx"], g["cnt"], w.block)
+    r = torch.zeros_like(v)
+    dr = torch.zeros_like(v)
+    full = B.qsa_full_attn_residual(g["qc"], g["qs"], g["kc"], g["ks"], v, g["idx"], g["cnt"],
+                                    w.block, r, dr, 0)
+    recon = host_f64(sp) + host_f64(r)
+    assert rel_l2(recon, host_f64(full)) < 4e-3
+
+
+@pytest.mark.parametrize("schedule", ["FSS", "FSFS", "FSSFSS"])
+@pytest.mark.parametrize("order", [2, 1])
+def test_schedule_against_oracle_state_machine(schedule, order):
+    from quantized_sparse_attention_amd import QSAConfig, QuantSparseAttention
+    w = TINY.with_(grid=(2, 8, 24), head_dim=64)  # 384 tokens, 6 blocks
+    topk, band = 2, (0,)
+    steps = qsa_gen.make_qkv_steps(w, len(schedule))
+    layer = QuantSparseAttention(QSAConfig(block=w.block, topk=topk, band=band, order=order))
+    st = oracle.ResidualState(steps[0]["v"].shape)
+    sm = oracle.default_sm_scale(w.head_dim)
+    for s, kind in enumerate(schedule):
+        x = steps[s]
+        out = layer.step(dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"]), kind == "F")
+        o = oracle_front(x, w, topk=topk, band=band)
+        o_sp = oracle.attention(o["qc"], o["sq"], o["kc"], o["sk"], x["v"], o["idx"], o["cnt"],
+                                w.block, sm)
+        if kind == "F":
+            fi, fc = oracle.full_kept_lists(w.batch, w.heads, w.n_blocks)
+            o_full = oracle.attention(o["qc"], o["sq"], o["kc"], o["sk"], x["v"], fi, fc,
+                                      w.block, sm)
+            want = oracle.refresh_step(st, o_full, o_sp)
+            assert_close(host_f64(out), want, what=f"step {s} {kind}")
+        else:
+            want = oracle.sparse_step(st, o_sp, order=order)
+            # end to end against the oracle's own state machine
+            r_ = rel_l2(host_f64(out), want)
+            assert r_ <= 5e-3, (s, kind, r_)
+            # the epilogue adds exactly the cached residuals to the sparse output
+            # (the caches may sit one bf16 rounding away from the oracle's)
+            cached = host_f64(layer.r) + (host_f64(layer.dr) if order == 2 else 0.0)
+            assert_close(host_f64(out), o_sp + cached, what=f"step {s} {kind}")
+            # and the caches track the oracle's to within one bf16 ulp
+            for got, ref in ((layer.r, st.r), (layer.dr, st.dr)):
+                g, rf = host_f64(got), oracle.bf16_to_f64(ref)
+                ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(rf), 2.0 ** -126))) - 7)
+                assert np.all(np.abs(g - rf) <= ulp * 1.0001 + 2e-2)
+        assert np.array_equal(layer.last.kept_idx.cpu().numpy(), o["idx"])
+
+
+def test_apply_residual():
+    rng = np.random.default_rng(4)
+    shape = (1, 3, 200, 128)
+    a, r, dr = (qsa_gen.f32_to_bf16_bits(rng.standard_normal(shape).astype(np.float32) * s)
+                for s in (1.0, 0.1, 0.01))
+    want = oracle.bf16_to_f64(a) + oracle.bf16_to_f64(r) + oracle.bf16_to_f64(dr)
+    got = B.qsa_apply_residual(dev_bf16(a), dev_bf16(r), dev_bf16(dr))
+    assert_close(host_f64(got), want, what="apply")
+    # bf16 rounding of an fp32 sum: within half a bf16 ulp of the fp64 sum (plus fp32 rounding)
+    assert np.all(np.abs(host_f64(got) - want) <= np.abs(want) * (2.0 ** -8 + 2.0 ** -22) + 1e-30)
+    # in place, and without dr
+    ta = dev_bf16(a)
+    B.qsa_apply_residual(ta, dev_bf16(r), None, out=ta)
+    assert_close(host_f64(ta), oracle.bf16_to_f64(a) + oracle.bf16_to_f64(r), what="apply r only")
+
+
+def test_quantize_map_sweep():
+    # Every finite bf16 x against a ladder of bf16 amax values across the whole
+    # exponent range (subnormal scales included): codes and scales bit-exact.
+    allx = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    xf = qsa_gen.bf16_bits_to_f32(allx)
+    xf = xf[np.isfinite(xf)]
+    mags = np.unique(np.abs(xf))
+    amaxes = [m for m in mags[1:] if True][::97] + [mags[-1]]
+    rows = []
+    for am in amaxes:
+        xs = xf[np.abs(xf) <= am]
+        blk = np.concatenate([[am], xs]).astype(np.float32)
+        pad = (-len(blk)) % (64 * 128)
+        blk = np.concatenate([blk, np.full(pad, am, np.float32)])  # fill with amax itself
+        rows.append(blk.reshape(-1, 64, 128))
+    data = np.concatenate(rows).reshape(1, 1, -1, 128)
+    bits = qsa_gen.f32_to_bf16_bits(data)
+    c_o, s_o, p_o = oracle.quantize(bits, 64)
+    c_g, s_g, p_g = B.qsa_quantize(dev_bf16(bits), 64)
+    assert np.array_equal(s_g.cpu().numpy().view(np.uint32), s_o.view(np.uint32))
+    assert np.array_equal(c_g.cpu().numpy(), c_o)
+    assert np.array_equal(p_g.cpu().numpy(), p_o)
+
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
+
+
+@pytest.mark.parametrize("name", ["H1", "H2_noband", "H2_band0"])
+def test_hand_examples_on_gpu(name):
+    with open(GOLDEN) as f:
+        gd = json.load(f)[name]
+    blk, D = gd["block"], gd["head_dim"]
+    nb = len(gd["q_blocks"])
+
+    def const(vals):
+        xx = np.concatenate([np.full((blk, D), v, np.float32) for v in vals])
+        return qsa_gen.f32_to_bf16_bits(xx)[None, None]
+
+    L = nb * blk
+    t = np.arange(L)[:, None]
+    d = np.arange(D)[None, :]
+    vf = ((((7 * t + 3 * d) % 17) - 8) / 8.0).astype(np.float32)
+    q, k, v = const(gd["q_blocks"]), const(gd["k_blocks"]), qsa_gen.f32_to_bf16_bits(vf)[None, None]
+    qc, qs, qp = B.qsa_quantize(dev_bf16(q), blk)
+    kc, ks, kp = B.qsa_quantize(dev_bf16(k), blk)
+    idx, cnt = B.qsa_select_blocks(qp, qs, kp, ks, L, blk, gd["topk"], gd["band"], nb)
+    got = [idx[0, 0, i, : cnt[0, 0, i]].tolist() for i in range(nb)]
+    assert got == gd["kept"]
+    out = host_f64(B.qsa_sparse_attn(qc, qs, kc, ks, dev_bf16(v), idx, cnt, blk))[0, 0]
+    means = [vf[j * blk:(j + 1) * blk].astype(np.float64).mean(axis=0) for j in range(nb)]
+    for i, kept in enumerate(gd["kept"]):
+        if len(kept) == 1:
+            want = np.broadcast_to(means[kept[0]], (blk, D))
+            assert np.max(np.abs(out[i * blk:(i + 1) * blk] - want)) <= 2e-2
+
+
+def test_select_edges():
+    w = TINY.with_(grid=(1, 9, 64), head_dim=128)  # 576 tokens, 9 blocks
+    x = qsa_gen.make_qkv(w)
+    # an all-zero key block gives +-0 scores that tie
+    x["k"][0, 0, 128:192] = 0
+    for topk, band in [(0, (0,)), (9, (0,)), (20, (0,)), (3, (-8, 0, 8)), (1, (0, 2, -2, 5))]:
+        o = oracle_front(x, w, topk=topk, band=band, kmax=9)
+        g = _gpu_front(x, w, topk, band, 9)
+        assert np.array_equal(g["idx"].cpu().numpy(), o["idx"]), (topk, band)
+        assert np.array_equal(g["cnt"].cpu().numpy(), o["cnt"]), (topk, band)
+    assert np.all(g["ks"].cpu().numpy()[0, 0, 2] == 0)
+
+
+def test_attention_edges():
+    w, x, o, g = _setup("tail64_d128")
+    v = dev_bf16(x["v"])
+    idx, cnt = g["idx"].clone(), g["cnt"].clone()
+    cnt[0, 0, 1] = 0            # an empty row outputs zeros
+    idx[0, 1, 2, 0] = -1        # entries outside [0, nb) are skipped
+    idx[0, 1, 3, 0] = 10 ** 6
+    out = host_f64(B.qsa_sparse_attn(g["qc"], g["qs"], g["kc"], g["ks"], v, idx, cnt, w.block))
+    assert np.all(out[0, 0, 64:128] == 0)
+    oi, oc = o["idx"].copy(), o["cnt"].copy()
+    oc[0, 0, 1] = 0
+    for (h, i) in [(1, 2), (1, 3)]:
+        lst = [j for j in oi[0, h, i, 1:oc[0, h, i]]]
+        oi[0, h, i] = -1
+        oi[0, h, i, :len(lst)] = lst
+        oc[0, h, i] = len(lst)
+    want = _oracle_attn(o, x, w, (oi, oc))
+    assert_close(out, want, what="edges")
+
+
+def test_deterministic():
+    w, x, o, g = _setup("batch2_h3")
+    v = dev_bf16(x["v"])
+    a = host_bits(B.qsa_sparse_attn(g["qc"], g["qs"], g["kc"], g["ks"], v, g["idx"], g["cnt"],
+                                    w.block))
+    b = host_bits(B.qsa_sparse_attn(g["qc"], g["qs"], g["kc"], g["ks"], v, g["idx"], g["cnt"],
+                                    w.block))
+    assert np.array_equal(a, b)
