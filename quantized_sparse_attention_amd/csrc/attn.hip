@@ -9,18 +9,27 @@
 //
 // Layout of the work (gfx950, wave64):
 //  * one workgroup per (batch*head, query block i) with BS/32 waves; wave w
-//    owns query rows 32w..32w+31 of the block;
-//  * per kept key block j: K codes [BS x D] int8 and V [BS x D] bf16 are read
-//    from HBM/L2 with 16-byte loads into registers one tile ahead, then stored
-//    to LDS (V transposed to [D x BS] so that P.V operands are contiguous);
+//    owns query rows 32w..32w+31 of the block; its Q codes stay in registers;
+//  * key blocks are walked as 64-key tiles (a 128-token block is two tiles).
+//    Per tile the K codes [64 x D] int8 and V [64 x D] bf16 go HBM/L2 -> LDS
+//    with 16-byte direct-to-LDS loads (no register staging), rows
+//    XOR-swizzled at 16-byte granularity so the operand reads are free of
+//    bank conflicts.  Each wave copies its MFMA operands of the tile into
+//    registers right away, so the single LDS tile is refilled with the next
+//    tile while this one is computed;
 //  * S^T = K_j . Q^T on v_mfma_i32_32x32x32_i8 (exact int32 dots);
-//  * logits z = (sm_scale * sq_i * sk_j * log2 e) * S, online softmax in fp32
-//    with exp2; the running max is only moved when a tile's max exceeds it
-//    by more than TAU (so P <= 2^TAU, exact in fp32 and bf16 ranges);
-//  * P is rounded to bf16 straight from the S^T accumulator registers (its
-//    layout is the B operand of the next MFMA, no LDS round trip) and
-//    O^T += V^T . P^T on v_mfma_f32_32x32x16_bf16 with fp32 accumulation;
-//    the softmax denominator sums the same bf16-rounded P (v_dot2_f32_bf16);
+//  * logits z = (sm_scale * sq_i * sk_j * log2 e) * S and softmax in fp32
+//    with exp2.  The running max is computed on the first tile only; later
+//    tiles exponentiate against it directly and the per-lane sum of the tile
+//    (which bounds every P) tells whether the max must move (sum > 2^64):
+//    only then is the tile max taken and the state rescaled.  Online
+//    softmax is exact in real arithmetic for any max used, so this only
+//    removes per-element max work;
+//  * P is rounded to bf16 straight from the S^T accumulator registers (their
+//    layout is the B operand of the next MFMA, no LDS round trip); the
+//    denominator sums the same bf16-rounded P (v_dot2_f32_bf16), and
+//    O^T += V^T . P^T on v_mfma_f32_32x32x16_bf16 with fp32 accumulation,
+//    the V^T operand read from the row-major V tile with ds_read_b64_tr_b16;
 //  * the epilogue normalises, adds the cached residuals (sparse step) or
 //    forms the residuals (refresh step), and stores bf16.
 // The refresh step keeps two online-softmax states, one over the kept blocks
@@ -32,93 +41,92 @@ namespace qsa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kTau = 8.0f;
+constexpr float kRsLimit = 18446744073709551616.0f;  // 2^64: bound on any P of a tile
 constexpr v2bf kOnes = {(__bf16)1.0f, (__bf16)1.0f};
+constexpr int KT = 64;  // keys per tile
 
 template <int BS, int D>
 struct Cfg {
   static constexpr int WAVES = BS / 32;
   static constexpr int THREADS = WAVES * 64;
-  static constexpr int KP = D + 16;  // K tile row pitch in bytes
-  static constexpr int VP = BS + 8;  // V^T tile row pitch in bf16 elements
-  static constexpr int NT = BS / 32;  // 32-key accumulator tiles per key block
-  static constexpr int DT = D / 32;   // 32-channel output tiles
-  static constexpr int KS = D / 32;   // 32-channel steps of the QK^T MFMA
-  static constexpr int PS = BS / 16;  // 16-key steps of the PV MFMA
-  static constexpr int K_CHUNKS = BS * D / 16 / THREADS;
-  static constexpr int V_TASKS = (BS / 4) * (D / 8) / THREADS;
-  static constexpr int LDS_K = BS * KP;
-  static constexpr int LDS_V = D * VP * 2;
+  static constexpr int SUB = BS / KT;  // tiles per key block
+  static constexpr int NT = KT / 32;   // 32-key accumulator tiles per tile
+  static constexpr int DT = D / 32;    // 32-channel output tiles
+  static constexpr int KS = D / 32;    // 32-channel steps of the QK^T MFMA
+  static constexpr int PS = KT / 16;   // 16-key steps of the PV MFMA
+  static constexpr int K_BYTES = KT * D;
+  static constexpr int V_BYTES = KT * D * 2;
+  static constexpr int K_CPR = D / 16;  // 16-byte chunks per K row
+  static constexpr int V_CPR = D / 8;   // 16-byte chunks per V row
+  static constexpr int K_ROWS_PER_KB = 1024 / D;
+  static constexpr int V_ROWS_PER_KB = 512 / D;
+  static constexpr int K_DMA = K_BYTES / 1024 / WAVES;  // 1 KB loads per wave
+  static constexpr int V_DMA = V_BYTES / 1024 / WAVES;
+  static_assert(K_DMA >= 1 && V_DMA >= 1, "tile loads must cover every wave");
 };
 
+// Chunk swizzles: 16-byte chunk p of tile row r holds logical chunk p ^ swz(r).
+// K rows are D bytes (256/D rows share one 256-byte bank line); V rows 2D bytes.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+  return (r / (256 / D)) & (D / 16 - 1);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+  return ((r / (128 / D)) & (D / 16 - 1)) << 1;
+}
+
+// Enqueue the direct-to-LDS loads of one tile (rows past the sequence end
+// re-read the last valid row: finite values that the softmax masks).
 template <int BS, int D>
-struct Stage {
-  uint4 k[Cfg<BS, D>::K_CHUNKS];
-  uint4 v[Cfg<BS, D>::V_TASKS][4];
+__device__ __forceinline__ void dma_tile(const int8_t* __restrict__ kt,
+                                         const uint16_t* __restrict__ vt, int8_t* lk,
+                                         uint16_t* lv, int wave, int lane, int nvalid) {
+  using C = Cfg<BS, D>;
+#pragma unroll
+  for (int n = 0; n < C::K_DMA; ++n) {
+    const int kb = wave * C::K_DMA + n;
+    const int row = kb * C::K_ROWS_PER_KB + lane / C::K_CPR;
+    const int p = lane % C::K_CPR;
+    const int src = min(row, nvalid - 1);
+    const int8_t* g = kt + (size_t)src * D + ((p ^ kswz<D>(row)) << 4);
+    __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(lk + kb * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int n = 0; n < C::V_DMA; ++n) {
+    const int kb = wave * C::V_DMA + n;
+    const int row = kb * C::V_ROWS_PER_KB + lane / C::V_CPR;
+    const int p = lane % C::V_CPR;
+    const int src = min(row, nvalid - 1);
+    const uint16_t* g = vt + (size_t)src * D + ((p ^ vswz<D>(row)) << 3);
+    __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(lv + kb * 512), 16, 0, 0);
+  }
+}
+
+// Per-lane LDS byte offsets of the MFMA operands (the swizzle of a lane's rows
+// does not depend on the tile, so these are computed once).
+template <int BS, int D>
+struct LaneOffs {
+  int k[Cfg<BS, D>::KS];  // K operand of K-step c, key rows 0..31
+  int v[Cfg<BS, D>::DT];  // V^T operand of channel tile dt, key step 0, half 0
+  __device__ __forceinline__ void init(int lane) {
+    using C = Cfg<BS, D>;
+    const int g = lane >> 5, r = lane & 31;
+#pragma unroll
+    for (int c = 0; c < C::KS; ++c) k[c] = r * D + (((g * C::KS + c) ^ kswz<D>(r)) << 4);
+    // ds_read_b64_tr_b16 in 16-lane groups: out lane i element e comes from
+    // source lane (i>>2) + 4e, element i&3.  Source lane 16G+j points at
+    // V[key 4(G>>1) + (j>>2)][d 32dt + 16(G&1) + 4(j&3)], so out lane l holds
+    // V[keys 4g + 0..3][d = 32dt + l%32]: the A operand of the PV MFMA.
+    const int G = lane >> 4, j = lane & 15;
+    const int r0 = 4 * (G >> 1) + (j >> 2);
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      const int chunk = 4 * dt + 2 * (G & 1) + ((j & 3) >> 1);
+      v[dt] = r0 * (2 * D) + ((chunk ^ vswz<D>(r0)) << 4) + 8 * (j & 1);
+    }
+  }
 };
-
-// Global -> registers for key block j (rows beyond the sequence read as 0).
-template <int BS, int D>
-__device__ __forceinline__ void load_stage(Stage<BS, D>& st, const int8_t* __restrict__ kc,
-                                           const uint16_t* __restrict__ v, int tid, int nvalid) {
-  using C = Cfg<BS, D>;
-#pragma unroll
-  for (int c = 0; c < C::K_CHUNKS; ++c) {
-    const int chunk = tid + c * C::THREADS;
-    const int row = chunk / (D / 16), col = chunk % (D / 16);
-    st.k[c] = row < nvalid ? *reinterpret_cast<const uint4*>(kc + (size_t)row * D + col * 16)
-                           : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int t = 0; t < C::V_TASKS; ++t) {
-    const int task = tid + t * C::THREADS;
-    const int dg = task % (D / 8), kg = task / (D / 8);
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int key = 4 * kg + kk;
-      st.v[t][kk] = key < nvalid
-                        ? *reinterpret_cast<const uint4*>(v + (size_t)key * D + dg * 8)
-                        : make_uint4(0, 0, 0, 0);
-    }
-  }
-}
-
-__device__ __forceinline__ uint32_t word_of(const uint4& u, int w) {
-  return w == 0 ? u.x : w == 1 ? u.y : w == 2 ? u.z : u.w;
-}
-
-// Registers -> LDS: K as [BS][KP] bytes, V transposed as [D][VP] bf16.
-template <int BS, int D>
-__device__ __forceinline__ void store_stage(const Stage<BS, D>& st, int8_t* lk, uint16_t* lv,
-                                            int tid) {
-  using C = Cfg<BS, D>;
-#pragma unroll
-  for (int c = 0; c < C::K_CHUNKS; ++c) {
-    const int chunk = tid + c * C::THREADS;
-    const int row = chunk / (D / 16), col = chunk % (D / 16);
-    *reinterpret_cast<uint4*>(lk + row * C::KP + col * 16) = st.k[c];
-  }
-#pragma unroll
-  for (int t = 0; t < C::V_TASKS; ++t) {
-    const int task = tid + t * C::THREADS;
-    const int dg = task % (D / 8), kg = task / (D / 8);
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const int w = dd >> 1;
-      uint32_t a0 = word_of(st.v[t][0], w), a1 = word_of(st.v[t][1], w);
-      uint32_t a2 = word_of(st.v[t][2], w), a3 = word_of(st.v[t][3], w);
-      uint32_t lo, hi;
-      if (dd & 1) {
-        lo = (a0 >> 16) | (a1 & 0xffff0000u);
-        hi = (a2 >> 16) | (a3 & 0xffff0000u);
-      } else {
-        lo = (a0 & 0xffffu) | (a1 << 16);
-        hi = (a2 & 0xffffu) | (a3 << 16);
-      }
-      *reinterpret_cast<uint2*>(lv + (dg * 8 + dd) * C::VP + 4 * kg) = make_uint2(lo, hi);
-    }
-  }
-}
 
 // Online-softmax state of one query row (held by lanes l and l^32).
 template <int BS, int D>
@@ -126,6 +134,7 @@ struct Acc {
   v16f o[Cfg<BS, D>::DT];
   float m;
   float l;
+  bool started;
   __device__ __forceinline__ void init() {
 #pragma unroll
     for (int t = 0; t < Cfg<BS, D>::DT; ++t)
@@ -133,58 +142,21 @@ struct Acc {
       for (int r = 0; r < 16; ++r) o[t][r] = 0.0f;
     m = -__builtin_inff();
     l = 0.0f;
+    started = false;
   }
 };
 
-// One key block against this wave's 32 query rows: QK^T, softmax update, PV.
-template <int BS, int D>
-__device__ __forceinline__ void process_tile(Acc<BS, D>& acc, const v4i (&qb)[Cfg<BS, D>::KS],
-                                             const int8_t* lk, const uint16_t* lv, int lane,
-                                             float cs, int nvalid) {
-  using C = Cfg<BS, D>;
-  const int g = lane >> 5, ql = lane & 31;
+__device__ __forceinline__ bool key_valid(int t, int r, int g, int nvalid) {
+  return 32 * t + 8 * (r >> 2) + 4 * g + (r & 3) < nvalid;
+}
 
-  v16i s[C::NT];
-#pragma unroll
-  for (int t = 0; t < C::NT; ++t) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) s[t][r] = 0;
-#pragma unroll
-    for (int c = 0; c < C::KS; ++c) {
-      const v4i a = *reinterpret_cast<const v4i*>(lk + (32 * t + ql) * C::KP + 32 * c + 16 * g);
-      s[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(a, qb[c], s[t], 0, 0, 0);
-    }
-  }
-  // s[t][r] = S[query ql][key 32t + 8(r/4) + 4g + r%4]
-  const bool tail = nvalid < BS;
-  if (tail) {
-#pragma unroll
-    for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = 32 * t + 8 * (r >> 2) + 4 * g + (r & 3);
-        if (key >= nvalid) s[t][r] = INT32_MIN;
-      }
-  }
-  int imax = INT32_MIN;
-#pragma unroll
-  for (int t = 0; t < C::NT; ++t)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) imax = max(imax, s[t][r]);
-  imax = max(imax, __shfl_xor(imax, 32, 64));
-  const float mt = cs * (float)imax;
-  if (__ballot(mt > acc.m + kTau)) {
-    const float mn = fmaxf(acc.m, mt);
-    const float alpha = __builtin_amdgcn_exp2f(acc.m - mn);
-#pragma unroll
-    for (int t = 0; t < C::DT; ++t)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc.o[t][r] *= alpha;
-    acc.l *= alpha;
-    acc.m = mn;
-  }
-  const float negm = -acc.m;
-  uint32_t pk[C::NT][8];
+// P = exp2(S * cs - m) as packed bf16 pairs; returns the lane's sum of the
+// rounded P.
+template <int BS, int D, bool TAIL>
+__device__ __forceinline__ float exp_pack(const v16i (&s)[Cfg<BS, D>::NT],
+                                          uint32_t (&pk)[Cfg<BS, D>::NT][8], float cs,
+                                          float negm, int g, int nvalid) {
+  using C = Cfg<BS, D>;
   float rs = 0.0f;
 #pragma unroll
   for (int t = 0; t < C::NT; ++t)
@@ -192,31 +164,134 @@ __device__ __forceinline__ void process_tile(Acc<BS, D>& acc, const v4i (&qb)[Cf
     for (int r = 0; r < 16; r += 2) {
       float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[t][r], cs, negm));
       float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf((float)s[t][r + 1], cs, negm));
-      if (tail) {
-        if (s[t][r] == INT32_MIN) p0 = 0.0f;
-        if (s[t][r + 1] == INT32_MIN) p1 = 0.0f;
+      if (TAIL) {
+        if (!key_valid(t, r, g, nvalid)) p0 = 0.0f;
+        if (!key_valid(t, r + 1, g, nvalid)) p1 = 0.0f;
       }
       pk[t][r >> 1] = pack_bf16x2(p0, p1);
-      // the row sum adds the bf16-rounded P that the PV MFMA consumes, so the
-      // normalisation matches the numerator exactly (one v_dot2 per pair)
       rs = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(v2bf, pk[t][r >> 1]), kOnes, rs,
                                            false);
     }
-  acc.l += rs;
+  return rs;
+}
 
+template <int BS, int D, bool TAIL>
+__device__ __forceinline__ float tile_max(const v16i (&s)[Cfg<BS, D>::NT], float cs, int g,
+                                          int nvalid) {
+  using C = Cfg<BS, D>;
+  int imax = INT32_MIN;
+#pragma unroll
+  for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (!TAIL || key_valid(t, r, g, nvalid)) imax = max(imax, s[t][r]);
+  imax = max(imax, __shfl_xor(imax, 32, 64));
+  return cs * (float)imax;
+}
+
+// MFMA operands of one tile held in registers, so the LDS tile can be
+// refilled with the next tile while this one is computed.
+template <int BS, int D>
+struct Ops {
+  v4i k[Cfg<BS, D>::NT][Cfg<BS, D>::KS];   // A operands of S^T = K Q^T
+  v8bf v[Cfg<BS, D>::PS][Cfg<BS, D>::DT];  // A operands of O^T += V^T P^T
+};
+
+template <int BS, int D>
+__device__ __forceinline__ void load_ops(Ops<BS, D>& op, const LaneOffs<BS, D>& lo,
+                                         const int8_t* lk, const uint16_t* lv) {
+  using C = Cfg<BS, D>;
+#pragma unroll
+  for (int t = 0; t < C::NT; ++t)
+#pragma unroll
+    for (int c = 0; c < C::KS; ++c)
+      op.k[t][c] = *reinterpret_cast<const v4i*>(lk + 32 * t * D + lo.k[c]);
+  const char* lvb = reinterpret_cast<const char*>(lv);
+#pragma unroll
+  for (int st = 0; st < C::PS; ++st)
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+      const char* base = lvb + 16 * st * (2 * D) + lo.v[dt];
+      const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(base));
+      const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(base + 8 * (2 * D)));
+      const uint2 ul = __builtin_bit_cast(uint2, lo4), uh = __builtin_bit_cast(uint2, hi4);
+      op.v[st][dt] = __builtin_bit_cast(v8bf, make_uint4(ul.x, ul.y, uh.x, uh.y));
+    }
+}
+
+// S^T = K . Q^T for this wave's 32 query rows: s[t][r] holds
+// S[query lane%32][key 32t + 8(r/4) + 4g + r%4] (exact int32).
+template <int BS, int D>
+__device__ __forceinline__ void qk(const v4i (&kop)[Cfg<BS, D>::NT][Cfg<BS, D>::KS],
+                                   const v4i (&qb)[Cfg<BS, D>::KS], v16i (&s)[Cfg<BS, D>::NT]) {
+  using C = Cfg<BS, D>;
+#pragma unroll
+  for (int t = 0; t < C::NT; ++t) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[t][r] = 0;
+#pragma unroll
+    for (int c = 0; c < C::KS; ++c)
+      s[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kop[t][c], qb[c], s[t], 0, 0, 0);
+  }
+}
+
+// Softmax update and O^T += V^T P^T for one tile whose scores s are in
+// registers.  TAIL: the tile is the short last one of the sequence (keys >=
+// nvalid are masked); every other tile runs without masking work.
+// kglob: the tile's K codes in global memory, used only to recompute the
+// scores when the running max has to move up (rare).
+template <int BS, int D, bool TAIL>
+__device__ __forceinline__ void softmax_pv(Acc<BS, D>& acc, const v16i (&s)[Cfg<BS, D>::NT],
+                                           const v8bf (&vop)[Cfg<BS, D>::PS][Cfg<BS, D>::DT],
+                                           const v4i (&qb)[Cfg<BS, D>::KS],
+                                           const int8_t* __restrict__ kglob, int lane, float cs,
+                                           int nvalid) {
+  using C = Cfg<BS, D>;
+  const int g = lane >> 5;
+  uint32_t pk[C::NT][8];
+  if (!acc.started) {
+    acc.m = tile_max<BS, D, TAIL>(s, cs, g, nvalid);
+    acc.started = true;
+  }
+  float rs = exp_pack<BS, D, TAIL>(s, pk, cs, -acc.m, g, nvalid);
+  if (__ballot(!(rs <= kRsLimit))) {
+    // The running max moved up by a lot: rescale the state to the new max and
+    // redo the tile, with the K operand reloaded from global memory (this
+    // lane's rows of K in the channel order of qb; rows past the end clamp).
+    v16i s2[C::NT];
+#pragma unroll
+    for (int t = 0; t < C::NT; ++t) {
+      const int row = min(32 * t + (lane & 31), nvalid - 1);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s2[t][r] = 0;
+#pragma unroll
+      for (int c = 0; c < C::KS; ++c) {
+        // one operand at a time: this path must not raise register pressure
+        const v4i ka =
+            *reinterpret_cast<const v4i*>(kglob + (size_t)row * D + g * (D / 2) + 16 * c);
+        s2[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(ka, qb[c], s2[t], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    const float mn = fmaxf(acc.m, tile_max<BS, D, TAIL>(s2, cs, g, nvalid));
+    const float alpha = __builtin_amdgcn_exp2f(acc.m - mn);
+#pragma unroll
+    for (int t = 0; t < C::DT; ++t)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc.o[t][r] *= alpha;
+    acc.l *= alpha;
+    acc.m = mn;
+    rs = exp_pack<BS, D, TAIL>(s2, pk, cs, -acc.m, g, nvalid);
+  }
+  acc.l += rs;
 #pragma unroll
   for (int st = 0; st < C::PS; ++st) {
     const int t = st >> 1, h = st & 1;
     const uint4 bu = make_uint4(pk[t][4 * h], pk[t][4 * h + 1], pk[t][4 * h + 2], pk[t][4 * h + 3]);
     const v8bf b = __builtin_bit_cast(v8bf, bu);
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-      const uint16_t* base = lv + (32 * dt + ql) * C::VP + 16 * st + 4 * g;
-      const uint2 lo = *reinterpret_cast<const uint2*>(base);
-      const uint2 hi = *reinterpret_cast<const uint2*>(base + 8);
-      const v8bf a = __builtin_bit_cast(v8bf, make_uint4(lo.x, lo.y, hi.x, hi.y));
-      acc.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc.o[dt], 0, 0, 0);
-    }
+    for (int dt = 0; dt < C::DT; ++dt)
+      acc.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[st][dt], b, acc.o[dt], 0, 0, 0);
   }
 }
 
@@ -229,23 +304,121 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* p, float a, float b, floa
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
 }
 
+// A kept list read through a 64-entry register window: lane l holds entry
+// base + l, so sequential reads cost one coalesced load per 64 entries and a
+// v_readlane each (no memory round trip per key tile).
+struct ListWin {
+  const int32_t* kl;
+  int n;
+  int base;
+  int win;
+  int lane;
+  __device__ __forceinline__ void init(const int32_t* k, int cnt, int ln) {
+    kl = k;
+    n = cnt;
+    lane = ln;
+    base = -64;
+    win = 0;
+  }
+  // entry p (wave-uniform, 0 <= p < n)
+  __device__ __forceinline__ int get(int p) {
+    const int b = p & ~63;
+    if (b != base) {
+      base = b;
+      win = b + lane < n ? kl[b + lane] : 0;
+    }
+    return __builtin_amdgcn_readlane(win, p - b);
+  }
+};
+
 // Next usable position of a kept list at or after `pos` (entries outside
-// [0, nb) are skipped); returns kc when none is left.
-__device__ __forceinline__ int next_kept(const int32_t* kl, int pos, int kc, int nb) {
-  while (pos < kc) {
-    const int j = kl[pos];
+// [0, nb) are skipped); returns the list length when none is left.
+__device__ __forceinline__ int next_kept(ListWin& w, int pos, int nb) {
+  while (pos < w.n) {
+    const int j = w.get(pos);
     if (j >= 0 && j < nb) break;
     ++pos;
   }
   return pos;
 }
 
-template <int BS, int D, bool REFRESH>
-__global__ __launch_bounds__((Cfg<BS, D>::THREADS)) void attn_kernel(AttnArgs a, int L, int nb,
-                                                                  uint32_t n_work) {
+// Shared per-workgroup context of the tile loop.
+template <int BS, int D>
+struct Ctx {
+  const int8_t* kc_h;
+  const uint16_t* v_h;
+  const float* sk_h;
+  int8_t* s_k;
+  uint16_t* s_v;
+  int L;
+  int wave, lane;
+  float c0;
+};
+
+// Run the online softmax of `acc` over the tiles produced by next() (64-key
+// tile indices, -1 at the end), with the next tile's loads in flight while
+// the current one is computed.  next() never returns the short last tile.
+template <int BS, int D, typename Next>
+__device__ __forceinline__ void walk(const Ctx<BS, D>& x, const v4i (&qb)[Cfg<BS, D>::KS],
+                                     const LaneOffs<BS, D>& lo, Acc<BS, D>& acc, Next&& next) {
   using C = Cfg<BS, D>;
-  __shared__ __attribute__((aligned(16))) int8_t s_k[C::LDS_K];
-  __shared__ __attribute__((aligned(16))) uint16_t s_v[C::LDS_V / 2];
+  auto dma = [&](int t) {
+    dma_tile<BS, D>(x.kc_h + (size_t)t * KT * D, x.v_h + (size_t)t * KT * D, x.s_k, x.s_v,
+                    x.wave, x.lane, KT);
+  };
+  int cur = next();
+  if (cur < 0) return;
+  __syncthreads();  // the LDS tile is free
+  dma(cur);
+  __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's loads landed in LDS
+  __syncthreads();                     // and every other wave's
+  while (cur >= 0) {
+    cur = __builtin_amdgcn_readfirstlane(cur);  // wave-uniform: scalar loads
+    const float cs = x.c0 * x.sk_h[cur / C::SUB];
+    Ops<BS, D> op;
+    load_ops<BS, D>(op, lo, x.s_k, x.s_v);
+    v16i s[C::NT];
+    qk<BS, D>(op.k, qb, s);
+    __syncthreads();  // every wave holds its operands: the LDS tile is free
+    const int nxt = next();
+    if (nxt >= 0) dma(nxt);  // lands while this tile is computed
+    softmax_pv<BS, D, false>(acc, s, op.v, qb, x.kc_h + (size_t)cur * KT * D, x.lane, cs, KT);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // the next tile landed in LDS
+    __syncthreads();
+    cur = nxt;
+  }
+}
+
+// The short last tile of the sequence (keys >= nvalid masked).
+template <int BS, int D>
+__device__ __forceinline__ void tail_tile(const Ctx<BS, D>& x, const v4i (&qb)[Cfg<BS, D>::KS],
+                                          const LaneOffs<BS, D>& lo, Acc<BS, D>& acc, int t) {
+  using C = Cfg<BS, D>;
+  const int nvalid = x.L - t * KT;
+  __syncthreads();
+  dma_tile<BS, D>(x.kc_h + (size_t)t * KT * D, x.v_h + (size_t)t * KT * D, x.s_k, x.s_v, x.wave,
+                  x.lane, nvalid);
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  __syncthreads();
+  const float cs = x.c0 * x.sk_h[t / C::SUB];
+  Ops<BS, D> op;
+  load_ops<BS, D>(op, lo, x.s_k, x.s_v);
+  v16i s[C::NT];
+  qk<BS, D>(op.k, qb, s);
+  softmax_pv<BS, D, true>(acc, s, op.v, qb, x.kc_h + (size_t)t * KT * D, x.lane, cs, nvalid);
+}
+
+// Register budget: the sparse kernel is held to two waves per SIMD (256 VGPRs,
+// all accumulators in architectural VGPRs, no AGPR round trips); the refresh
+// kernel carries two output accumulators and runs one wave per SIMD.
+template <int BS, int D, bool REFRESH>
+__global__ __launch_bounds__((Cfg<BS, D>::THREADS))
+__attribute__((amdgpu_waves_per_eu(REFRESH ? 1 : 2, 8))) void attn_kernel(AttnArgs a, int L,
+                                                                         int nb,
+                                                                         uint32_t n_work) {
+  using C = Cfg<BS, D>;
+  __shared__ __attribute__((aligned(1024))) int8_t s_k[C::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint16_t s_v[C::V_BYTES / 2];
 
   const uint32_t work = xcd_contiguous(blockIdx.x, n_work);
   const uint32_t i = work % (uint32_t)nb;
@@ -254,87 +427,109 @@ __global__ __launch_bounds__((Cfg<BS, D>::THREADS)) void attn_kernel(AttnArgs a,
   const int g = lane >> 5, ql = lane & 31;
 
   const uint64_t head_off = bh * (uint64_t)L * D;
-  const int8_t* kc_h = a.k_codes + head_off;
-  const uint16_t* v_h = a.v + head_off;
-  const float* sk_h = a.k_scales + bh * (uint64_t)nb;
 
-  // this wave's 32 query rows, as the B operand of S^T = K Q^T
+  // this wave's 32 query rows, as the B operand of S^T = K Q^T (same channel
+  // order as the K operand: lane group g holds channels g*D/2 + 16c + 0..15)
   const int qrow = (int)i * BS + 32 * wave + ql;
   const bool qvalid = qrow < L;
   v4i qb[C::KS];
 #pragma unroll
   for (int c = 0; c < C::KS; ++c) {
     qb[c] = qvalid ? *reinterpret_cast<const v4i*>(a.q_codes + head_off + (size_t)qrow * D +
-                                                   32 * c + 16 * g)
+                                                   g * (D / 2) + 16 * c)
                    : v4i{0, 0, 0, 0};
   }
-  const float c0 = a.sm_scale * a.q_scales[bh * (uint64_t)nb + i] * kLog2e;
+  LaneOffs<BS, D> lo;
+  lo.init(lane);
+  Ctx<BS, D> x;
+  x.kc_h = a.k_codes + head_off;
+  x.v_h = a.v + head_off;
+  x.sk_h = a.k_scales + bh * (uint64_t)nb;
+  x.s_k = s_k;
+  x.s_v = s_v;
+  x.L = L;
+  x.wave = wave;
+  x.lane = lane;
+  x.c0 = a.sm_scale * a.q_scales[bh * (uint64_t)nb + i] * kLog2e;
 
   const int32_t* kl = a.kept_idx + (bh * (uint64_t)nb + i) * (uint64_t)a.kmax;
   const int kcnt = min(max(a.kept_cnt[bh * (uint64_t)nb + i], 0), a.kmax);
+  const int n_tiles = (L + KT - 1) / KT;
+  const int tail_t = (L % KT) ? n_tiles - 1 : -1;
 
   Acc<BS, D> acc_k;  // kept blocks (the sparse attention)
   acc_k.init();
   Acc<BS, D> acc_n;  // the other blocks (refresh step only)
   if (REFRESH) acc_n.init();
 
-  Stage<BS, D> st;
-  // iteration state: sparse step walks the kept list, refresh walks all blocks
-  int pos = 0;
-  int cur;
-  if (REFRESH) {
-    cur = 0;
-  } else {
-    pos = next_kept(kl, 0, kcnt, nb);
-    cur = pos < kcnt ? kl[pos] : -1;
-  }
-  if (cur >= 0) {
-    const int nv = min(BS, L - cur * BS);
-    load_stage<BS, D>(st, kc_h + (size_t)cur * BS * D, v_h + (size_t)cur * BS * D, tid, nv);
-  }
-  int kpos = 0;  // refresh: cursor into the kept list
-  while (cur >= 0) {
-    __syncthreads();
-    store_stage<BS, D>(st, s_k, s_v, tid);
-    __syncthreads();
-    int nxt;
-    if (REFRESH) {
-      nxt = cur + 1 < nb ? cur + 1 : -1;
-    } else {
-      pos = next_kept(kl, pos + 1, kcnt, nb);
-      nxt = pos < kcnt ? kl[pos] : -1;
-    }
-    if (nxt >= 0) {
-      const int nv = min(BS, L - nxt * BS);
-      load_stage<BS, D>(st, kc_h + (size_t)nxt * BS * D, v_h + (size_t)nxt * BS * D, tid, nv);
-    }
-    const int nvalid = min(BS, L - cur * BS);
-    const float cs = c0 * sk_h[cur];
-    if (REFRESH) {
-      while (kpos < kcnt && kl[kpos] < cur) ++kpos;
-      const bool kept = kpos < kcnt && kl[kpos] == cur;
-      if (kept) {
-        process_tile<BS, D>(acc_k, qb, s_k, s_v, lane, cs, nvalid);
-      } else {
-        process_tile<BS, D>(acc_n, qb, s_k, s_v, lane, cs, nvalid);
+  // kept blocks, in list order (ascending), each as SUB tiles
+  bool tail_in_kept = false;
+  {
+    ListWin w;
+    w.init(kl, kcnt, lane);
+    int pos = next_kept(w, 0, nb);
+    int sub = 0;
+    walk<BS, D>(x, qb, lo, acc_k, [&]() -> int {
+      while (pos < kcnt) {
+        const int t = w.get(pos) * C::SUB + sub;
+        if (++sub == C::SUB) {
+          sub = 0;
+          pos = next_kept(w, pos + 1, nb);
+        }
+        if (t >= n_tiles) continue;  // empty second half of a short last block
+        if (t == tail_t) {
+          tail_in_kept = true;
+          continue;
+        }
+        return t;
       }
-    } else {
-      process_tile<BS, D>(acc_k, qb, s_k, s_v, lane, cs, nvalid);
-    }
-    cur = nxt;
+      return -1;
+    });
+  }
+  if (tail_in_kept) tail_tile<BS, D>(x, qb, lo, acc_k, tail_t);
+  if (REFRESH) {
+    // every other block, ascending: with the kept ones, the full attention
+    ListWin w;
+    w.init(kl, kcnt, lane);
+    int j = 0, kpos = 0, sub = 0;
+    bool tail_in_rest = false;
+    walk<BS, D>(x, qb, lo, acc_n, [&]() -> int {
+      while (j < nb) {
+        if (sub == 0) {
+          while (kpos < kcnt && w.get(kpos) < j) ++kpos;
+          if (kpos < kcnt && w.get(kpos) == j) {
+            ++j;
+            continue;
+          }
+        }
+        const int t = j * C::SUB + sub;
+        if (++sub == C::SUB) {
+          sub = 0;
+          ++j;
+        }
+        if (t >= n_tiles) continue;
+        if (t == tail_t) {
+          tail_in_rest = true;
+          continue;
+        }
+        return t;
+      }
+      return -1;
+    });
+    if (tail_in_rest) tail_tile<BS, D>(x, qb, lo, acc_n, tail_t);
   }
 
   // ---- epilogue --------------------------------------------------------------
   const float lk = acc_k.l + __shfl_xor(acc_k.l, 32, 64);
   const float inv_k = lk > 0.0f ? 1.0f / lk : 0.0f;
-  float wk = 0.0f, wn = 0.0f, inv_f = 0.0f;
+  float wk = 0.0f, wn = 0.0f;
   if (REFRESH) {
     const float ln = acc_n.l + __shfl_xor(acc_n.l, 32, 64);
     const float m = fmaxf(acc_k.m, acc_n.m);
-    const float ak = __builtin_amdgcn_exp2f(acc_k.m - m);
-    const float an = __builtin_amdgcn_exp2f(acc_n.m - m);
+    const float ak = acc_k.started ? __builtin_amdgcn_exp2f(acc_k.m - m) : 0.0f;
+    const float an = acc_n.started ? __builtin_amdgcn_exp2f(acc_n.m - m) : 0.0f;
     const float lf = lk * ak + ln * an;
-    inv_f = lf > 0.0f ? 1.0f / lf : 0.0f;
+    const float inv_f = lf > 0.0f ? 1.0f / lf : 0.0f;
     wk = ak * inv_f;
     wn = an * inv_f;
   }
