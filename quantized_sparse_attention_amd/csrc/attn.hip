@@ -71,9 +71,13 @@ template <int D>
 __device__ __forceinline__ int kswz(int r) {
   return (r / (256 / D)) & (D / 16 - 1);
 }
+// A transpose read of the V^T operand touches, per 32 lanes, 4 consecutive
+// rows x 4 consecutive chunks; XOR-ing the chunk quad with the row (D = 128:
+// one row per 256-byte bank line) or with the bank-line index (D = 64: two
+// rows per line) puts the 16 chunks on distinct banks.
 template <int D>
 __device__ __forceinline__ int vswz(int r) {
-  return ((r / (128 / D)) & (D / 16 - 1)) << 1;
+  return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
 }
 
 // Enqueue the direct-to-LDS loads of one tile (rows past the sequence end
@@ -189,6 +193,17 @@ __device__ __forceinline__ float tile_max(const v16i (&s)[Cfg<BS, D>::NT], float
   return cs * (float)imax;
 }
 
+// The V^T operand of 16-key step st and channel tile dt from the LDS tile.
+template <int BS, int D>
+__device__ __forceinline__ v8bf v_operand(const LaneOffs<BS, D>& lo, const uint16_t* lv, int st,
+                                          int dt) {
+  const char* base = reinterpret_cast<const char*>(lv) + 16 * st * (2 * D) + lo.v[dt];
+  const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(base));
+  const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(base + 8 * (2 * D)));
+  const uint2 ul = __builtin_bit_cast(uint2, lo4), uh = __builtin_bit_cast(uint2, hi4);
+  return __builtin_bit_cast(v8bf, make_uint4(ul.x, ul.y, uh.x, uh.y));
+}
+
 // MFMA operands of one tile held in registers, so the LDS tile can be
 // refilled with the next tile while this one is computed.
 template <int BS, int D>
@@ -206,17 +221,10 @@ __device__ __forceinline__ void load_ops(Ops<BS, D>& op, const LaneOffs<BS, D>& 
 #pragma unroll
     for (int c = 0; c < C::KS; ++c)
       op.k[t][c] = *reinterpret_cast<const v4i*>(lk + 32 * t * D + lo.k[c]);
-  const char* lvb = reinterpret_cast<const char*>(lv);
 #pragma unroll
   for (int st = 0; st < C::PS; ++st)
 #pragma unroll
-    for (int dt = 0; dt < C::DT; ++dt) {
-      const char* base = lvb + 16 * st * (2 * D) + lo.v[dt];
-      const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(base));
-      const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(base + 8 * (2 * D)));
-      const uint2 ul = __builtin_bit_cast(uint2, lo4), uh = __builtin_bit_cast(uint2, hi4);
-      op.v[st][dt] = __builtin_bit_cast(v8bf, make_uint4(ul.x, ul.y, uh.x, uh.y));
-    }
+    for (int dt = 0; dt < C::DT; ++dt) op.v[st][dt] = v_operand<BS, D>(lo, lv, st, dt);
 }
 
 // S^T = K . Q^T for this wave's 32 query rows: s[t][r] holds
@@ -235,20 +243,20 @@ __device__ __forceinline__ void qk(const v4i (&kop)[Cfg<BS, D>::NT][Cfg<BS, D>::
   }
 }
 
-// Softmax update and O^T += V^T P^T for one tile whose scores s are in
-// registers.  TAIL: the tile is the short last one of the sequence (keys >=
-// nvalid are masked); every other tile runs without masking work.
-// kglob: the tile's K codes in global memory, used only to recompute the
-// scores when the running max has to move up (rare).
+// Softmax update for one tile whose scores s are in registers: P = exp2(S cs
+// - m) packed to bf16 in pk, running sum and (rarely) max updated.  TAIL: the
+// tile is the short last one of the sequence (keys >= nvalid are masked);
+// every other tile runs without masking work.  kglob: the tile's K codes in
+// global memory, used only to recompute the scores when the running max has
+// to move up (rare).
 template <int BS, int D, bool TAIL>
-__device__ __forceinline__ void softmax_pv(Acc<BS, D>& acc, const v16i (&s)[Cfg<BS, D>::NT],
-                                           const v8bf (&vop)[Cfg<BS, D>::PS][Cfg<BS, D>::DT],
-                                           const v4i (&qb)[Cfg<BS, D>::KS],
-                                           const int8_t* __restrict__ kglob, int lane, float cs,
-                                           int nvalid) {
+__device__ __forceinline__ void softmax_update(Acc<BS, D>& acc, const v16i (&s)[Cfg<BS, D>::NT],
+                                               uint32_t (&pk)[Cfg<BS, D>::NT][8],
+                                               const v4i (&qb)[Cfg<BS, D>::KS],
+                                               const int8_t* __restrict__ kglob, int lane,
+                                               float cs, int nvalid) {
   using C = Cfg<BS, D>;
   const int g = lane >> 5;
-  uint32_t pk[C::NT][8];
   if (!acc.started) {
     acc.m = tile_max<BS, D, TAIL>(s, cs, g, nvalid);
     acc.started = true;
@@ -284,15 +292,65 @@ __device__ __forceinline__ void softmax_pv(Acc<BS, D>& acc, const v16i (&s)[Cfg<
     rs = exp_pack<BS, D, TAIL>(s2, pk, cs, -acc.m, g, nvalid);
   }
   acc.l += rs;
+}
+
+template <int BS, int D>
+__device__ __forceinline__ v8bf pk_operand(const uint32_t (&pk)[Cfg<BS, D>::NT][8], int st) {
+  const int t = st >> 1, h = st & 1;
+  const uint4 bu = make_uint4(pk[t][4 * h], pk[t][4 * h + 1], pk[t][4 * h + 2], pk[t][4 * h + 3]);
+  return __builtin_bit_cast(v8bf, bu);
+}
+
+// O^T += V^T P^T with the V operands already in registers.
+template <int BS, int D>
+__device__ __forceinline__ void pv_regs(Acc<BS, D>& acc,
+                                        const v8bf (&vop)[Cfg<BS, D>::PS][Cfg<BS, D>::DT],
+                                        const uint32_t (&pk)[Cfg<BS, D>::NT][8]) {
+  using C = Cfg<BS, D>;
 #pragma unroll
   for (int st = 0; st < C::PS; ++st) {
-    const int t = st >> 1, h = st & 1;
-    const uint4 bu = make_uint4(pk[t][4 * h], pk[t][4 * h + 1], pk[t][4 * h + 2], pk[t][4 * h + 3]);
-    const v8bf b = __builtin_bit_cast(v8bf, bu);
+    const v8bf b = pk_operand<BS, D>(pk, st);
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt)
       acc.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vop[st][dt], b, acc.o[dt], 0, 0, 0);
   }
+}
+
+// O^T += V^T P^T reading the V operands from the LDS tile, one 16-key step
+// ahead of the MFMAs that consume them (the reads of step st+1 are in
+// flight while the MFMAs of step st run).
+template <int BS, int D>
+__device__ __forceinline__ void pv_lds(Acc<BS, D>& acc, const LaneOffs<BS, D>& lo,
+                                       const uint16_t* lv,
+                                       const uint32_t (&pk)[Cfg<BS, D>::NT][8]) {
+  using C = Cfg<BS, D>;
+  v8bf va[C::DT], vb[C::DT];
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) va[dt] = v_operand<BS, D>(lo, lv, 0, dt);
+#pragma unroll
+  for (int st = 0; st < C::PS; ++st) {
+    if (st + 1 < C::PS) {
+#pragma unroll
+      for (int dt = 0; dt < C::DT; ++dt) vb[dt] = v_operand<BS, D>(lo, lv, st + 1, dt);
+    }
+    const v8bf b = pk_operand<BS, D>(pk, st);
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt)
+      acc.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[dt], b, acc.o[dt], 0, 0, 0);
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) va[dt] = vb[dt];
+  }
+}
+
+template <int BS, int D, bool TAIL>
+__device__ __forceinline__ void softmax_pv(Acc<BS, D>& acc, const v16i (&s)[Cfg<BS, D>::NT],
+                                           const v8bf (&vop)[Cfg<BS, D>::PS][Cfg<BS, D>::DT],
+                                           const v4i (&qb)[Cfg<BS, D>::KS],
+                                           const int8_t* __restrict__ kglob, int lane, float cs,
+                                           int nvalid) {
+  uint32_t pk[Cfg<BS, D>::NT][8];
+  softmax_update<BS, D, TAIL>(acc, s, pk, qb, kglob, lane, cs, nvalid);
+  pv_regs<BS, D>(acc, vop, pk);
 }
 
 __device__ __forceinline__ float4 load_bf16x4(const uint16_t* p) {
@@ -348,8 +406,10 @@ struct Ctx {
   const int8_t* kc_h;
   const uint16_t* v_h;
   const float* sk_h;
-  int8_t* s_k;
+  int8_t* s_k;   // LDS tile buffer 0
   uint16_t* s_v;
+  int8_t* s_k1;  // LDS tile buffer 1 (double-buffered walk)
+  uint16_t* s_v1;
   int L;
   int wave, lane;
   float c0;
@@ -389,6 +449,87 @@ __device__ __forceinline__ void walk(const Ctx<BS, D>& x, const v4i (&qb)[Cfg<BS
   }
 }
 
+// vmcnt(n) wait: expcnt and lgkmcnt left at their maxima (no wait).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
+}
+
+// Double-buffered variant of walk(): two LDS tiles, the V operands read from
+// LDS during the PV MFMAs (no register copy), and the load of tile n+2 issued
+// into tile n's buffer as soon as every wave is done with it, so a tile's
+// loads have a whole iteration to land.  The loop is unrolled by two so each
+// buffer is a fixed LDS object.
+template <int BS, int D, typename Next>
+__device__ __forceinline__ void walk2(const Ctx<BS, D>& x, const v4i (&qb)[Cfg<BS, D>::KS],
+                                      const LaneOffs<BS, D>& lo, Acc<BS, D>& acc, Next&& next) {
+  using C = Cfg<BS, D>;
+  constexpr int DMA_PER_TILE = C::K_DMA + C::V_DMA;
+  auto dma = [&](int t, int8_t* lk, uint16_t* lv) {
+    dma_tile<BS, D>(x.kc_h + (size_t)t * KT * D, x.v_h + (size_t)t * KT * D, lk, lv, x.wave,
+                    x.lane, KT);
+  };
+  auto step = [&](int t, const int8_t* lk, const uint16_t* lv) {
+    t = __builtin_amdgcn_readfirstlane(t);
+    const float cs = x.c0 * x.sk_h[t / C::SUB];
+    v4i kop[C::NT][C::KS];
+#pragma unroll
+    for (int tt = 0; tt < C::NT; ++tt)
+#pragma unroll
+      for (int c = 0; c < C::KS; ++c)
+        kop[tt][c] = *reinterpret_cast<const v4i*>(lk + 32 * tt * D + lo.k[c]);
+    v16i sc[C::NT];
+    qk<BS, D>(kop, qb, sc);
+    uint32_t pk[C::NT][8];
+    softmax_update<BS, D, false>(acc, sc, pk, qb, x.kc_h + (size_t)t * KT * D, x.lane, cs, KT);
+    pv_lds<BS, D>(acc, lo, lv, pk);
+  };
+  int cur = next();
+  if (cur < 0) return;
+  __syncthreads();  // both LDS tiles are free
+  dma(cur, x.s_k, x.s_v);
+  int nxt = next();
+  if (nxt >= 0) {
+    dma(nxt, x.s_k1, x.s_v1);
+    wait_vmcnt<DMA_PER_TILE>();  // the first tile landed (the second may be in flight)
+  } else {
+    wait_vmcnt<0>();
+  }
+  __syncthreads();
+  while (true) {
+    step(cur, x.s_k, x.s_v);
+    wait_vmcnt<0>();  // the next tile landed in buffer 1
+    __syncthreads();  // and every wave is done with buffer 0
+    if (nxt < 0) break;
+    int nn = next();
+    if (nn >= 0) dma(nn, x.s_k, x.s_v);
+    cur = nxt;
+    nxt = nn;
+    step(cur, x.s_k1, x.s_v1);
+    wait_vmcnt<0>();
+    __syncthreads();
+    if (nxt < 0) break;
+    nn = next();
+    if (nn >= 0) dma(nn, x.s_k1, x.s_v1);
+    cur = nxt;
+    nxt = nn;
+  }
+}
+
+// The sparse kernel (two waves per SIMD, a single LDS tile per workgroup)
+// walks with the operands copied to registers; the refresh kernel (one wave
+// per SIMD, registers taken by two accumulators) double-buffers in LDS.
+template <int BS, int D, bool REFRESH, typename Next>
+__device__ __forceinline__ void walk_any(const Ctx<BS, D>& x, const v4i (&qb)[Cfg<BS, D>::KS],
+                                         const LaneOffs<BS, D>& lo, Acc<BS, D>& acc,
+                                         Next&& next) {
+  if (REFRESH)
+    walk2<BS, D>(x, qb, lo, acc, next);
+  else
+    walk<BS, D>(x, qb, lo, acc, next);
+}
+
 // The short last tile of the sequence (keys >= nvalid masked).
 template <int BS, int D>
 __device__ __forceinline__ void tail_tile(const Ctx<BS, D>& x, const v4i (&qb)[Cfg<BS, D>::KS],
@@ -413,12 +554,14 @@ __device__ __forceinline__ void tail_tile(const Ctx<BS, D>& x, const v4i (&qb)[C
 // kernel carries two output accumulators and runs one wave per SIMD.
 template <int BS, int D, bool REFRESH>
 __global__ __launch_bounds__((Cfg<BS, D>::THREADS))
-__attribute__((amdgpu_waves_per_eu(REFRESH ? 1 : 2, 8))) void attn_kernel(AttnArgs a, int L,
-                                                                         int nb,
-                                                                         uint32_t n_work) {
+__attribute__((amdgpu_waves_per_eu(REFRESH ? 1 : 2, 8))) void attn_kernel(AttnArgs a, int L, int nb,
+                                                                        uint32_t n_work) {
   using C = Cfg<BS, D>;
   __shared__ __attribute__((aligned(1024))) int8_t s_k[C::K_BYTES];
   __shared__ __attribute__((aligned(1024))) uint16_t s_v[C::V_BYTES / 2];
+  // second LDS tile of the refresh kernel's double-buffered walk
+  __shared__ __attribute__((aligned(1024))) int8_t s_k1[REFRESH ? C::K_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) uint16_t s_v1[REFRESH ? C::V_BYTES / 2 : 8];
 
   const uint32_t work = xcd_contiguous(blockIdx.x, n_work);
   const uint32_t i = work % (uint32_t)nb;
@@ -447,6 +590,8 @@ __attribute__((amdgpu_waves_per_eu(REFRESH ? 1 : 2, 8))) void attn_kernel(AttnAr
   x.sk_h = a.k_scales + bh * (uint64_t)nb;
   x.s_k = s_k;
   x.s_v = s_v;
+  x.s_k1 = s_k1;
+  x.s_v1 = s_v1;
   x.L = L;
   x.wave = wave;
   x.lane = lane;
@@ -469,7 +614,7 @@ __attribute__((amdgpu_waves_per_eu(REFRESH ? 1 : 2, 8))) void attn_kernel(AttnAr
     w.init(kl, kcnt, lane);
     int pos = next_kept(w, 0, nb);
     int sub = 0;
-    walk<BS, D>(x, qb, lo, acc_k, [&]() -> int {
+    walk_any<BS, D, REFRESH>(x, qb, lo, acc_k, [&]() -> int {
       while (pos < kcnt) {
         const int t = w.get(pos) * C::SUB + sub;
         if (++sub == C::SUB) {
@@ -493,7 +638,7 @@ __attribute__((amdgpu_waves_per_eu(REFRESH ? 1 : 2, 8))) void attn_kernel(AttnAr
     w.init(kl, kcnt, lane);
     int j = 0, kpos = 0, sub = 0;
     bool tail_in_rest = false;
-    walk<BS, D>(x, qb, lo, acc_n, [&]() -> int {
+    walk_any<BS, D, REFRESH>(x, qb, lo, acc_n, [&]() -> int {
       while (j < nb) {
         if (sub == 0) {
           while (kpos < kcnt && w.get(kpos) < j) ++kpos;
