@@ -126,8 +126,9 @@ int qsa_select_blocks(const qsa_dims* dims, const int32_t* pooled_q, const float
  * (sparse attention, technical summary §1; residual cache of §2B).
  *
  * For every query token t of block i, over the valid key tokens u of the
- * blocks in kept(i) (the first kept_cnt entries of the row; entries outside
- * [0, nb) are skipped):
+ * blocks in kept(i) -- the set of block indices in [0, nb) among the first
+ * kept_cnt entries of the row, in any order (a repeated entry counts once,
+ * entries outside [0, nb) are skipped):
  *   z_tu = sm_scale * scale_q[i] * scale_k[j(u)] * (q_codes[t] . k_codes[u])
  *   p    = softmax_u(z)   (fp32, online, max-subtracted)
  *   o_t  = sum_u p_tu * v[u]   (P rounded to bf16, fp32 accumulation)
@@ -140,6 +141,7 @@ int qsa_select_blocks(const qsa_dims* dims, const int32_t* pooled_q, const float
  *   sm_scale         in: finite, > 0 (usually 1/sqrt(D))
  *   r, dr            in: bf16 [B,H,L,D] or NULL
  *   out             out: bf16 [B,H,L,D]; must not alias any input
+ * QSA_ERR_SHAPE if nb > QSA_MAX_BLOCKS (both attention entry points).
  */
 int qsa_sparse_attn(const qsa_dims* dims, const int8_t* q_codes, const float* q_scales,
                     const int8_t* k_codes, const float* k_scales, const uint16_t* v,

@@ -30,7 +30,10 @@ R4  block saliency for the inference mask: the dot product of the
     [QS-ko] §2.1) -- score_ij = fl64(fl64(S_ij * (sq_i * sk_j)) / (n_i * n_j))
     with S_ij the exact integer dot of the pooled code sums.
 R5  kept(i) = band(i) union top-k(i); the top-k ranks all key blocks by score
-    descending, ties to the lowest block index; lists ascending.
+    descending, ties to the lowest block index; lists ascending.  kept(i) is
+    a set: attention over a given list uses each valid block index of its
+    first kept_cnt entries once (repeats and indices outside [0, nb) add
+    nothing).
 R6  attention is non-causal; logits are sm_scale * sq_i * sk_j * (int dot).
 R7  SSAR ([QS-es] §2B, [QS-ko] §2.2): the first-order residual is the
     difference of the attention OUTPUTS of full and sparse attention at a
@@ -232,7 +235,7 @@ def attention(q_codes, q_scales, k_codes, k_scales, v_bits, kept_idx, kept_cnt, 
     For each query block i the keys are the valid tokens of the blocks in
     kept(i); logits z = sm_scale * sq_i * sk_j * (q_codes . k_codes); softmax
     in fp64 (max-subtracted); O = P V with V the bf16 values widened to fp64.
-    A query block with an empty kept list outputs zeros.
+    A query block with an empty kept set outputs zeros.
 
     ``which``: optional iterable of (b, h, i); then only those query blocks
     are computed and a dict {(b, h, i): O_block} is returned.
@@ -244,7 +247,8 @@ def attention(q_codes, q_scales, k_codes, k_scales, v_bits, kept_idx, kept_cnt, 
     res = {}
     for (b, h, i) in sel:
         t0, t1 = i * block, min((i + 1) * block, L)
-        blocks = [int(j) for j in kept_idx[b, h, i, : kept_cnt[b, h, i]]]
+        blocks = sorted({int(j) for j in kept_idx[b, h, i, : kept_cnt[b, h, i]]
+                         if 0 <= j < nb})  # kept(i) as a set (R5)
         if not blocks:
             res[(b, h, i)] = np.zeros((t1 - t0, D))
             continue

@@ -8,8 +8,13 @@
 // steps).  Same content on the Korean page (ko/paper/2509.23681) §2.2.
 //
 // Layout of the work (gfx950, wave64):
-//  * one workgroup per (batch*head, query block i) with BS/32 waves; wave w
-//    owns query rows 32w..32w+31 of the block; its Q codes stay in registers;
+//  * one workgroup per (batch*head, group of QB consecutive query blocks),
+//    BS/32 waves per query block; a wave owns 32 query rows and keeps their
+//    Q codes in registers.  The kept sets of the group's blocks are turned
+//    into bitmaps over the key blocks in LDS and the group walks their union
+//    once, in ascending order: a key tile kept by several blocks of the group
+//    is loaded once (neighbouring query blocks keep overlapping key sets), and
+//    a wave computes only the tiles its own block keeps;
 //  * key blocks are walked as 64-key tiles (a 128-token block is two tiles).
 //    Per tile the K codes [64 x D] int8 and V [64 x D] bf16 go HBM/L2 -> LDS
 //    with 16-byte direct-to-LDS loads (no register staging), rows
@@ -37,6 +42,10 @@
 // exponential and MFMA; it merges them at the end like split-K attention.
 #include "qsa_internal.h"
 
+#ifndef QSA_ATTN_QB
+#define QSA_ATTN_QB 2
+#endif
+
 namespace qsa {
 namespace {
 
@@ -45,10 +54,18 @@ constexpr float kRsLimit = 18446744073709551616.0f;  // 2^64: bound on any P of 
 constexpr v2bf kOnes = {(__bf16)1.0f, (__bf16)1.0f};
 constexpr int KT = 64;  // keys per tile
 
+// A read-only fp32 array read at a wave-uniform index through the constant
+// address space, so it becomes a scalar load: it then waits on the scalar
+// counter only, not on the vector-memory counter that also tracks the tile
+// loads in flight.
+__device__ __forceinline__ float load_uniform(const float* p, int i) {
+  typedef __attribute__((address_space(4))) const float cf32;
+  return ((cf32*)p)[__builtin_amdgcn_readfirstlane(i)];
+}
+
 template <int BS, int D>
 struct Cfg {
-  static constexpr int WAVES = BS / 32;
-  static constexpr int THREADS = WAVES * 64;
+  static constexpr int WPB = BS / 32;  // waves per query block (32 rows each)
   static constexpr int SUB = BS / KT;  // tiles per key block
   static constexpr int NT = KT / 32;   // 32-key accumulator tiles per tile
   static constexpr int DT = D / 32;    // 32-channel output tiles
@@ -60,9 +77,16 @@ struct Cfg {
   static constexpr int V_CPR = D / 8;   // 16-byte chunks per V row
   static constexpr int K_ROWS_PER_KB = 1024 / D;
   static constexpr int V_ROWS_PER_KB = 512 / D;
-  static constexpr int K_DMA = K_BYTES / 1024 / WAVES;  // 1 KB loads per wave
-  static constexpr int V_DMA = V_BYTES / 1024 / WAVES;
-  static_assert(K_DMA >= 1 && V_DMA >= 1, "tile loads must cover every wave");
+};
+
+// Each of the NWV waves of a workgroup issues an equal share of a tile's 1 KB
+// direct-to-LDS loads.
+template <int D, int NWV>
+struct Dma {
+  static constexpr int K = KT * D / 1024 / NWV;
+  static constexpr int V = KT * D * 2 / 1024 / NWV;
+  static_assert(K >= 1 && V >= 1 && K * NWV * 1024 == KT * D && V * NWV * 1024 == KT * D * 2,
+                "tile loads must split evenly over the waves");
 };
 
 // Chunk swizzles: 16-byte chunk p of tile row r holds logical chunk p ^ swz(r).
@@ -82,14 +106,15 @@ __device__ __forceinline__ int vswz(int r) {
 
 // Enqueue the direct-to-LDS loads of one tile (rows past the sequence end
 // re-read the last valid row: finite values that the softmax masks).
-template <int BS, int D>
+template <int BS, int D, int NWV>
 __device__ __forceinline__ void dma_tile(const int8_t* __restrict__ kt,
                                          const uint16_t* __restrict__ vt, int8_t* lk,
                                          uint16_t* lv, int wave, int lane, int nvalid) {
   using C = Cfg<BS, D>;
+  using M = Dma<D, NWV>;
 #pragma unroll
-  for (int n = 0; n < C::K_DMA; ++n) {
-    const int kb = wave * C::K_DMA + n;
+  for (int n = 0; n < M::K; ++n) {
+    const int kb = wave * M::K + n;
     const int row = kb * C::K_ROWS_PER_KB + lane / C::K_CPR;
     const int p = lane % C::K_CPR;
     const int src = min(row, nvalid - 1);
@@ -97,8 +122,8 @@ __device__ __forceinline__ void dma_tile(const int8_t* __restrict__ kt,
     __builtin_amdgcn_global_load_lds(g, (lds_void_t*)(lk + kb * 1024), 16, 0, 0);
   }
 #pragma unroll
-  for (int n = 0; n < C::V_DMA; ++n) {
-    const int kb = wave * C::V_DMA + n;
+  for (int n = 0; n < M::V; ++n) {
+    const int kb = wave * M::V + n;
     const int row = kb * C::V_ROWS_PER_KB + lane / C::V_CPR;
     const int p = lane % C::V_CPR;
     const int src = min(row, nvalid - 1);
@@ -362,43 +387,105 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* p, float a, float b, floa
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
 }
 
-// A kept list read through a 64-entry register window: lane l holds entry
-// base + l, so sequential reads cost one coalesced load per 64 entries and a
-// v_readlane each (no memory round trip per key tile).
-struct ListWin {
-  const int32_t* kl;
-  int n;
-  int base;
-  int win;
-  int lane;
-  __device__ __forceinline__ void init(const int32_t* k, int cnt, int ln) {
-    kl = k;
-    n = cnt;
-    lane = ln;
-    base = -64;
-    win = 0;
-  }
-  // entry p (wave-uniform, 0 <= p < n)
-  __device__ __forceinline__ int get(int p) {
-    const int b = p & ~63;
-    if (b != base) {
-      base = b;
-      win = b + lane < n ? kl[b + lane] : 0;
+// Kept sets of the query blocks of a workgroup as bitmaps over the key blocks,
+// in LDS: bit j of row b is set when key block j is in kept(i) of the group's
+// b-th query block i.  The tile walks below read them a 32-bit word at a time.
+constexpr int kMaxWords = QSA_MAX_BLOCKS / 32;
+
+template <int QB, int THREADS>
+__device__ __forceinline__ void build_kept_bits(uint32_t (*bits)[kMaxWords], const AttnArgs& a,
+                                                uint64_t row0, int nq, int nb, int tid) {
+  const int nw = (nb + 31) >> 5;
+  for (int k = tid; k < QB * nw; k += THREADS) bits[k / nw][k % nw] = 0u;
+  __syncthreads();
+  for (int b = 0; b < nq; ++b) {
+    const int32_t* kl = a.kept_idx + (row0 + b) * (uint64_t)a.kmax;
+    const int cnt = min(max(a.kept_cnt[row0 + b], 0), a.kmax);
+    for (int p = tid; p < cnt; p += THREADS) {
+      const int j = kl[p];
+      if (j >= 0 && j < nb) atomicOr(&bits[b][j >> 5], 1u << (j & 31));
     }
-    return __builtin_amdgcn_readlane(win, p - b);
+  }
+  __syncthreads();
+}
+
+// Walk, in ascending order, over the 64-key tiles of the key blocks that at
+// least one query block of the group needs: the kept blocks (REST = false) or
+// the blocks outside the kept set (REST = true, the refresh step's other
+// half).  Every wave of the workgroup produces the same tile sequence; `keep`
+// tells a wave whether its own query block needs the tile.  The short last
+// tile of the sequence is not returned: tail_hit / tail_keep record it.
+template <int QB, int SUB, bool REST>
+struct BitWalk {
+  const uint32_t (*bits)[kMaxWords];
+  int nw, nq, myb, n_tiles, tail_t, last_bits;
+  int wi, base, j, sub;
+  uint32_t u, mine;
+  bool kj, tail_hit, tail_keep;
+
+  __device__ __forceinline__ void init(const uint32_t (*b)[kMaxWords], int nb, int nq_, int myb_,
+                                       int n_tiles_, int tail_t_) {
+    bits = b;
+    nw = (nb + 31) >> 5;
+    nq = nq_;
+    myb = myb_;
+    n_tiles = n_tiles_;
+    tail_t = tail_t_;
+    last_bits = nb - 32 * (nw - 1);
+    wi = 0;
+    base = 0;
+    j = 0;
+    sub = 0;
+    u = 0u;
+    mine = 0u;
+    kj = false;
+    tail_hit = false;
+    tail_keep = false;
+  }
+  __device__ __forceinline__ uint32_t row_word(int b, int w) const {
+    uint32_t v = bits[b][w];
+    if (REST) {
+      const uint32_t valid = w == nw - 1 && last_bits < 32 ? (1u << last_bits) - 1u : ~0u;
+      v = ~v & valid;
+    }
+    return v;
+  }
+  __device__ __forceinline__ void load_word() {
+    uint32_t un = 0u;
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+      if (b < nq) un |= row_word(b, wi);
+    u = __builtin_amdgcn_readfirstlane(un);
+    mine = myb >= 0 ? __builtin_amdgcn_readfirstlane(row_word(myb, wi)) : 0u;
+    base = wi << 5;
+    ++wi;
+  }
+  // next tile index (wave-uniform), -1 at the end
+  __device__ __forceinline__ int next(bool& keep) {
+    while (true) {
+      if (sub == 0) {
+        while (u == 0u) {
+          if (wi >= nw) return -1;
+          load_word();
+        }
+        const int bit = __builtin_ctz(u);
+        u &= u - 1u;
+        j = base + bit;
+        kj = (mine >> bit) & 1u;
+      }
+      const int t = j * SUB + sub;
+      if (++sub == SUB) sub = 0;
+      if (t >= n_tiles) continue;  // empty second half of a short last block
+      if (t == tail_t) {
+        tail_hit = true;
+        tail_keep = kj;
+        continue;
+      }
+      keep = kj;
+      return t;
+    }
   }
 };
-
-// Next usable position of a kept list at or after `pos` (entries outside
-// [0, nb) are skipped); returns the list length when none is left.
-__device__ __forceinline__ int next_kept(ListWin& w, int pos, int nb) {
-  while (pos < w.n) {
-    const int j = w.get(pos);
-    if (j >= 0 && j < nb) break;
-    ++pos;
-  }
-  return pos;
-}
 
 // Shared per-workgroup context of the tile loop.
 template <int BS, int D>
@@ -417,16 +504,19 @@ struct Ctx {
 
 // Run the online softmax of `acc` over the tiles produced by next() (64-key
 // tile indices, -1 at the end), with the next tile's loads in flight while
-// the current one is computed.  next() never returns the short last tile.
-template <int BS, int D, typename Next>
+// the current one is computed.  Every wave loads its share of each tile; a
+// wave computes only the tiles its query block keeps.  next() never returns
+// the short last tile.
+template <int BS, int D, int NWV, typename Next>
 __device__ __forceinline__ void walk(const Ctx<BS, D>& x, const v4i (&qb)[Cfg<BS, D>::KS],
                                      const LaneOffs<BS, D>& lo, Acc<BS, D>& acc, Next&& next) {
   using C = Cfg<BS, D>;
   auto dma = [&](int t) {
-    dma_tile<BS, D>(x.kc_h + (size_t)t * KT * D, x.v_h + (size_t)t * KT * D, x.s_k, x.s_v,
-                    x.wave, x.lane, KT);
+    dma_tile<BS, D, NWV>(x.kc_h + (size_t)t * KT * D, x.v_h + (size_t)t * KT * D, x.s_k, x.s_v,
+                         x.wave, x.lane, KT);
   };
-  int cur = next();
+  bool keep = false;
+  int cur = next(keep);
   if (cur < 0) return;
   __syncthreads();  // the LDS tile is free
   dma(cur);
@@ -434,18 +524,24 @@ __device__ __forceinline__ void walk(const Ctx<BS, D>& x, const v4i (&qb)[Cfg<BS
   __syncthreads();                     // and every other wave's
   while (cur >= 0) {
     cur = __builtin_amdgcn_readfirstlane(cur);  // wave-uniform: scalar loads
-    const float cs = x.c0 * x.sk_h[cur / C::SUB];
     Ops<BS, D> op;
-    load_ops<BS, D>(op, lo, x.s_k, x.s_v);
     v16i s[C::NT];
-    qk<BS, D>(op.k, qb, s);
+    float cs = 0.0f;
+    if (keep) {
+      cs = x.c0 * load_uniform(x.sk_h, cur / C::SUB);
+      load_ops<BS, D>(op, lo, x.s_k, x.s_v);
+      qk<BS, D>(op.k, qb, s);
+    }
     __syncthreads();  // every wave holds its operands: the LDS tile is free
-    const int nxt = next();
+    bool knext = false;
+    const int nxt = next(knext);
     if (nxt >= 0) dma(nxt);  // lands while this tile is computed
-    softmax_pv<BS, D, false>(acc, s, op.v, qb, x.kc_h + (size_t)cur * KT * D, x.lane, cs, KT);
+    if (keep)
+      softmax_pv<BS, D, false>(acc, s, op.v, qb, x.kc_h + (size_t)cur * KT * D, x.lane, cs, KT);
     __builtin_amdgcn_s_waitcnt(0x0f70);  // the next tile landed in LDS
     __syncthreads();
     cur = nxt;
+    keep = knext;
   }
 }
 
@@ -461,18 +557,19 @@ __device__ __forceinline__ void wait_vmcnt() {
 // into tile n's buffer as soon as every wave is done with it, so a tile's
 // loads have a whole iteration to land.  The loop is unrolled by two so each
 // buffer is a fixed LDS object.
-template <int BS, int D, typename Next>
+template <int BS, int D, int NWV, typename Next>
 __device__ __forceinline__ void walk2(const Ctx<BS, D>& x, const v4i (&qb)[Cfg<BS, D>::KS],
                                       const LaneOffs<BS, D>& lo, Acc<BS, D>& acc, Next&& next) {
   using C = Cfg<BS, D>;
-  constexpr int DMA_PER_TILE = C::K_DMA + C::V_DMA;
+  constexpr int DMA_PER_TILE = Dma<D, NWV>::K + Dma<D, NWV>::V;
   auto dma = [&](int t, int8_t* lk, uint16_t* lv) {
-    dma_tile<BS, D>(x.kc_h + (size_t)t * KT * D, x.v_h + (size_t)t * KT * D, lk, lv, x.wave,
-                    x.lane, KT);
+    dma_tile<BS, D, NWV>(x.kc_h + (size_t)t * KT * D, x.v_h + (size_t)t * KT * D, lk, lv, x.wave,
+                         x.lane, KT);
   };
-  auto step = [&](int t, const int8_t* lk, const uint16_t* lv) {
+  auto step = [&](int t, bool keep, const int8_t* lk, const uint16_t* lv) {
+    if (!keep) return;
     t = __builtin_amdgcn_readfirstlane(t);
-    const float cs = x.c0 * x.sk_h[t / C::SUB];
+    const float cs = x.c0 * load_uniform(x.sk_h, t / C::SUB);
     v4i kop[C::NT][C::KS];
 #pragma unroll
     for (int tt = 0; tt < C::NT; ++tt)
@@ -485,11 +582,12 @@ __device__ __forceinline__ void walk2(const Ctx<BS, D>& x, const v4i (&qb)[Cfg<B
     softmax_update<BS, D, false>(acc, sc, pk, qb, x.kc_h + (size_t)t * KT * D, x.lane, cs, KT);
     pv_lds<BS, D>(acc, lo, lv, pk);
   };
-  int cur = next();
+  bool kc = false, kn = false, knn = false;
+  int cur = next(kc);
   if (cur < 0) return;
   __syncthreads();  // both LDS tiles are free
   dma(cur, x.s_k, x.s_v);
-  int nxt = next();
+  int nxt = next(kn);
   if (nxt >= 0) {
     dma(nxt, x.s_k1, x.s_v1);
     wait_vmcnt<DMA_PER_TILE>();  // the first tile landed (the second may be in flight)
@@ -498,50 +596,57 @@ __device__ __forceinline__ void walk2(const Ctx<BS, D>& x, const v4i (&qb)[Cfg<B
   }
   __syncthreads();
   while (true) {
-    step(cur, x.s_k, x.s_v);
+    step(cur, kc, x.s_k, x.s_v);
     wait_vmcnt<0>();  // the next tile landed in buffer 1
     __syncthreads();  // and every wave is done with buffer 0
     if (nxt < 0) break;
-    int nn = next();
+    int nn = next(knn);
     if (nn >= 0) dma(nn, x.s_k, x.s_v);
     cur = nxt;
+    kc = kn;
     nxt = nn;
-    step(cur, x.s_k1, x.s_v1);
+    kn = knn;
+    step(cur, kc, x.s_k1, x.s_v1);
     wait_vmcnt<0>();
     __syncthreads();
     if (nxt < 0) break;
-    nn = next();
+    nn = next(knn);
     if (nn >= 0) dma(nn, x.s_k1, x.s_v1);
     cur = nxt;
+    kc = kn;
     nxt = nn;
+    kn = knn;
   }
 }
 
 // The sparse kernel (two waves per SIMD, a single LDS tile per workgroup)
 // walks with the operands copied to registers; the refresh kernel (one wave
 // per SIMD, registers taken by two accumulators) double-buffers in LDS.
-template <int BS, int D, bool REFRESH, typename Next>
+template <int BS, int D, int NWV, bool REFRESH, typename Next>
 __device__ __forceinline__ void walk_any(const Ctx<BS, D>& x, const v4i (&qb)[Cfg<BS, D>::KS],
                                          const LaneOffs<BS, D>& lo, Acc<BS, D>& acc,
                                          Next&& next) {
   if (REFRESH)
-    walk2<BS, D>(x, qb, lo, acc, next);
+    walk2<BS, D, NWV>(x, qb, lo, acc, next);
   else
-    walk<BS, D>(x, qb, lo, acc, next);
+    walk<BS, D, NWV>(x, qb, lo, acc, next);
 }
 
-// The short last tile of the sequence (keys >= nvalid masked).
-template <int BS, int D>
+// The short last tile of the sequence (keys >= nvalid masked); every wave
+// loads its share, the waves whose query block keeps it compute it.
+template <int BS, int D, int NWV>
 __device__ __forceinline__ void tail_tile(const Ctx<BS, D>& x, const v4i (&qb)[Cfg<BS, D>::KS],
-                                          const LaneOffs<BS, D>& lo, Acc<BS, D>& acc, int t) {
+                                          const LaneOffs<BS, D>& lo, Acc<BS, D>& acc, int t,
+                                          bool keep) {
   using C = Cfg<BS, D>;
   const int nvalid = x.L - t * KT;
   __syncthreads();
-  dma_tile<BS, D>(x.kc_h + (size_t)t * KT * D, x.v_h + (size_t)t * KT * D, x.s_k, x.s_v, x.wave,
-                  x.lane, nvalid);
+  dma_tile<BS, D, NWV>(x.kc_h + (size_t)t * KT * D, x.v_h + (size_t)t * KT * D, x.s_k, x.s_v,
+                       x.wave, x.lane, nvalid);
   __builtin_amdgcn_s_waitcnt(0x0f70);
   __syncthreads();
-  const float cs = x.c0 * x.sk_h[t / C::SUB];
+  if (!keep) return;
+  const float cs = x.c0 * load_uniform(x.sk_h, t / C::SUB);
   Ops<BS, D> op;
   load_ops<BS, D>(op, lo, x.s_k, x.s_v);
   v16i s[C::NT];
@@ -549,31 +654,42 @@ __device__ __forceinline__ void tail_tile(const Ctx<BS, D>& x, const v4i (&qb)[C
   softmax_pv<BS, D, true>(acc, s, op.v, qb, x.kc_h + (size_t)t * KT * D, x.lane, cs, nvalid);
 }
 
+// One workgroup per (batch*head, group of QB consecutive query blocks), with
+// BS/32 waves per query block.  The group walks the union of its blocks' kept
+// sets once, so a key tile kept by several of them is loaded once.
 // Register budget: the sparse kernel is held to two waves per SIMD (256 VGPRs,
 // all accumulators in architectural VGPRs, no AGPR round trips); the refresh
 // kernel carries two output accumulators and runs one wave per SIMD.
-template <int BS, int D, bool REFRESH>
-__global__ __launch_bounds__((Cfg<BS, D>::THREADS))
+template <int BS, int D, int QB, bool REFRESH>
+__global__ __launch_bounds__((QB * BS / 32 * 64))
 __attribute__((amdgpu_waves_per_eu(REFRESH ? 1 : 2, 8))) void attn_kernel(AttnArgs a, int L, int nb,
                                                                         uint32_t n_work) {
   using C = Cfg<BS, D>;
+  constexpr int NWV = QB * C::WPB;  // waves in the workgroup
+  constexpr int THREADS = 64 * NWV;
   __shared__ __attribute__((aligned(1024))) int8_t s_k[C::K_BYTES];
   __shared__ __attribute__((aligned(1024))) uint16_t s_v[C::V_BYTES / 2];
   // second LDS tile of the refresh kernel's double-buffered walk
   __shared__ __attribute__((aligned(1024))) int8_t s_k1[REFRESH ? C::K_BYTES : 16];
   __shared__ __attribute__((aligned(1024))) uint16_t s_v1[REFRESH ? C::V_BYTES / 2 : 8];
+  __shared__ uint32_t s_bits[QB][kMaxWords];
 
+  const uint32_t ng = (uint32_t)((nb + QB - 1) / QB);
   const uint32_t work = xcd_contiguous(blockIdx.x, n_work);
-  const uint32_t i = work % (uint32_t)nb;
-  const uint64_t bh = work / (uint32_t)nb;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t grp = work % ng;
+  const uint64_t bh = work / ng;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, ql = lane & 31;
+  const int qsub = wave / C::WPB;  // this wave's query block within the group
+  const int i = (int)grp * QB + qsub;
+  const int nq = min(QB, nb - (int)grp * QB);
 
   const uint64_t head_off = bh * (uint64_t)L * D;
 
   // this wave's 32 query rows, as the B operand of S^T = K Q^T (same channel
   // order as the K operand: lane group g holds channels g*D/2 + 16c + 0..15)
-  const int qrow = (int)i * BS + 32 * wave + ql;
+  const int qrow = i * BS + 32 * (wave % C::WPB) + ql;
   const bool qvalid = qrow < L;
   v4i qb[C::KS];
 #pragma unroll
@@ -582,6 +698,9 @@ __attribute__((amdgpu_waves_per_eu(REFRESH ? 1 : 2, 8))) void attn_kernel(AttnAr
                                                    g * (D / 2) + 16 * c)
                    : v4i{0, 0, 0, 0};
   }
+  // the Q operands are in registers before any tile load is issued: no wait
+  // for them is left for the compiler to place inside the tile loop
+  __builtin_amdgcn_s_waitcnt(0x0f70);
   LaneOffs<BS, D> lo;
   lo.init(lane);
   Ctx<BS, D> x;
@@ -595,73 +714,30 @@ __attribute__((amdgpu_waves_per_eu(REFRESH ? 1 : 2, 8))) void attn_kernel(AttnAr
   x.L = L;
   x.wave = wave;
   x.lane = lane;
-  x.c0 = a.sm_scale * a.q_scales[bh * (uint64_t)nb + i] * kLog2e;
+  x.c0 = i < nb ? a.sm_scale * a.q_scales[bh * (uint64_t)nb + i] * kLog2e : 0.0f;
 
-  const int32_t* kl = a.kept_idx + (bh * (uint64_t)nb + i) * (uint64_t)a.kmax;
-  const int kcnt = min(max(a.kept_cnt[bh * (uint64_t)nb + i], 0), a.kmax);
+  build_kept_bits<QB, THREADS>(s_bits, a, bh * (uint64_t)nb + grp * QB, nq, nb, tid);
   const int n_tiles = (L + KT - 1) / KT;
   const int tail_t = (L % KT) ? n_tiles - 1 : -1;
+  const int myb = i < nb ? qsub : -1;
 
   Acc<BS, D> acc_k;  // kept blocks (the sparse attention)
   acc_k.init();
   Acc<BS, D> acc_n;  // the other blocks (refresh step only)
   if (REFRESH) acc_n.init();
 
-  // kept blocks, in list order (ascending), each as SUB tiles
-  bool tail_in_kept = false;
   {
-    ListWin w;
-    w.init(kl, kcnt, lane);
-    int pos = next_kept(w, 0, nb);
-    int sub = 0;
-    walk_any<BS, D, REFRESH>(x, qb, lo, acc_k, [&]() -> int {
-      while (pos < kcnt) {
-        const int t = w.get(pos) * C::SUB + sub;
-        if (++sub == C::SUB) {
-          sub = 0;
-          pos = next_kept(w, pos + 1, nb);
-        }
-        if (t >= n_tiles) continue;  // empty second half of a short last block
-        if (t == tail_t) {
-          tail_in_kept = true;
-          continue;
-        }
-        return t;
-      }
-      return -1;
-    });
+    BitWalk<QB, C::SUB, false> w;
+    w.init(s_bits, nb, nq, myb, n_tiles, tail_t);
+    walk_any<BS, D, NWV, REFRESH>(x, qb, lo, acc_k, [&](bool& keep) { return w.next(keep); });
+    if (w.tail_hit) tail_tile<BS, D, NWV>(x, qb, lo, acc_k, tail_t, w.tail_keep);
   }
-  if (tail_in_kept) tail_tile<BS, D>(x, qb, lo, acc_k, tail_t);
   if (REFRESH) {
-    // every other block, ascending: with the kept ones, the full attention
-    ListWin w;
-    w.init(kl, kcnt, lane);
-    int j = 0, kpos = 0, sub = 0;
-    bool tail_in_rest = false;
-    walk_any<BS, D, REFRESH>(x, qb, lo, acc_n, [&]() -> int {
-      while (j < nb) {
-        if (sub == 0) {
-          while (kpos < kcnt && w.get(kpos) < j) ++kpos;
-          if (kpos < kcnt && w.get(kpos) == j) {
-            ++j;
-            continue;
-          }
-        }
-        const int t = j * C::SUB + sub;
-        if (++sub == C::SUB) {
-          sub = 0;
-          ++j;
-        }
-        if (t >= n_tiles) continue;
-        if (t == tail_t) {
-          tail_in_rest = true;
-          continue;
-        }
-        return t;
-      }
-      return -1;
-    });
-    if (tail_in_rest) tail_tile<BS, D>(x, qb, lo, acc_n, tail_t);
+    // every other block: with the kept ones, the full attention
+    BitWalk<QB, C::SUB, true> w;
+    w.init(s_bits, nb, nq, myb, n_tiles, tail_t);
+    walk_any<BS, D, NWV, REFRESH>(x, qb, lo, acc_n, [&](bool& keep) { return w.next(keep); });
+    if (w.tail_hit) tail_tile<BS, D, NWV>(x, qb, lo, acc_n, tail_t, w.tail_keep);
   }
 
   // ---- epilogue --------------------------------------------------------------
@@ -719,21 +795,28 @@ __attribute__((amdgpu_waves_per_eu(REFRESH ? 1 : 2, 8))) void attn_kernel(AttnAr
   }
 }
 
-template <int BS, int D, bool REFRESH>
+template <int BS, int D, int QB, bool REFRESH>
 hipError_t launch_t(const qsa_dims& d, const AttnArgs& a, hipStream_t s) {
   const int nb = (d.seq_len + BS - 1) / BS;
-  const uint32_t n_work = (uint32_t)((uint64_t)d.batch * d.heads * nb);
-  hipLaunchKernelGGL((attn_kernel<BS, D, REFRESH>), dim3(n_work), dim3(Cfg<BS, D>::THREADS), 0,
-                     s, a, d.seq_len, nb, n_work);
+  const uint32_t ng = (uint32_t)((nb + QB - 1) / QB);
+  const uint32_t n_work = (uint32_t)((uint64_t)d.batch * d.heads * ng);
+  hipLaunchKernelGGL((attn_kernel<BS, D, QB, REFRESH>), dim3(n_work), dim3(QB * BS / 32 * 64),
+                     0, s, a, d.seq_len, nb, n_work);
   return hipGetLastError();
 }
 
+// Query blocks per workgroup: the sparse kernel groups blocks so that key
+// tiles kept by several of them are loaded once (the waves of a group split
+// each tile's loads evenly, which bounds the group size); the refresh kernel
+// runs one block per workgroup.
 template <bool REFRESH>
 hipError_t dispatch(const qsa_dims& d, const AttnArgs& a, hipStream_t s) {
-  if (d.block == 64 && d.head_dim == 128) return launch_t<64, 128, REFRESH>(d, a, s);
-  if (d.block == 64 && d.head_dim == 64) return launch_t<64, 64, REFRESH>(d, a, s);
-  if (d.block == 128 && d.head_dim == 128) return launch_t<128, 128, REFRESH>(d, a, s);
-  return launch_t<128, 64, REFRESH>(d, a, s);
+  constexpr int Q64 = REFRESH ? 1 : QSA_ATTN_QB;
+  constexpr int Q64s = REFRESH ? 1 : (QSA_ATTN_QB < 2 ? QSA_ATTN_QB : 2);
+  if (d.block == 64 && d.head_dim == 128) return launch_t<64, 128, Q64, REFRESH>(d, a, s);
+  if (d.block == 64 && d.head_dim == 64) return launch_t<64, 64, Q64s, REFRESH>(d, a, s);
+  if (d.block == 128 && d.head_dim == 128) return launch_t<128, 128, Q64s, REFRESH>(d, a, s);
+  return launch_t<128, 64, 1, REFRESH>(d, a, s);
 }
 
 }  // namespace

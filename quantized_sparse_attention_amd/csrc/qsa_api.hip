@@ -97,6 +97,10 @@ int check_attn_common(const char* fn, const qsa_dims* dims, const int8_t* q_code
                       int32_t kmax, float sm_scale) {
   int st = check_dims(fn, dims);
   if (st) return st;
+  const long long nb = ((long long)dims->seq_len + dims->block - 1) / dims->block;
+  if (nb > QSA_MAX_BLOCKS)  // the kept sets are held as LDS bitmaps of this many bits
+    return fail(QSA_ERR_SHAPE, "%s: %lld blocks exceed QSA_MAX_BLOCKS=%d", fn, nb,
+                QSA_MAX_BLOCKS);
   REQUIRE_PTR(q_codes);
   REQUIRE_PTR(q_scales);
   REQUIRE_PTR(k_codes);

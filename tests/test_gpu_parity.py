@@ -289,6 +289,47 @@ def test_attention_edges():
     assert_close(out, want, what="edges")
 
 
+def _messy_lists(w, seed):
+    """Kept lists with repeats, entries outside [0, nb) and shuffled order."""
+    nb = w.n_blocks
+    rng = np.random.default_rng(seed)
+    kmax = 12
+    idx = np.full((w.batch, w.heads, nb, kmax), -1, np.int32)
+    cnt = np.zeros((w.batch, w.heads, nb), np.int32)
+    for b in range(w.batch):
+        for h in range(w.heads):
+            for i in range(nb):
+                base = list(rng.choice(nb, size=int(rng.integers(1, min(nb, 5) + 1)),
+                                       replace=False))
+                lst = base + [base[-1], -7, nb, 2 ** 30]
+                rng.shuffle(lst)
+                idx[b, h, i, :len(lst)] = lst
+                cnt[b, h, i] = len(lst)
+    return idx, cnt, kmax
+
+
+@pytest.mark.parametrize("name", ["tail64_d128", "batch2_h3", "d64_b128"])
+def test_kept_lists_are_sets(name):
+    """Both kernels take kept(i) as the set of its valid entries."""
+    w, x, o, g = _setup(name)
+    v = dev_bf16(x["v"])
+    idx, cnt, kmax = _messy_lists(w, 11)
+    di = torch.from_numpy(idx).cuda()
+    dc = torch.from_numpy(cnt).cuda()
+    out = B.qsa_sparse_attn(g["qc"], g["qs"], g["kc"], g["ks"], v, di, dc, w.block)
+    want = _oracle_attn(o, x, w, (idx, cnt))
+    assert_close(host_f64(out), want, what=f"{name} messy sparse")
+    r = torch.zeros_like(v)
+    dr = torch.zeros_like(v)
+    full = B.qsa_full_attn_residual(g["qc"], g["qs"], g["kc"], g["ks"], v, di, dc, w.block, r,
+                                    dr, 0)
+    o_full = _oracle_attn(o, x, w, oracle.full_kept_lists(w.batch, w.heads, w.n_blocks))
+    assert_close(host_f64(full), o_full, what=f"{name} messy full")
+    rho = o_full - want
+    err = host_f64(r) - rho
+    assert np.linalg.norm(err) / np.linalg.norm(o_full) <= 5e-3
+
+
 def test_deterministic():
     w, x, o, g = _setup("batch2_h3")
     v = dev_bf16(x["v"])

@@ -48,7 +48,9 @@ def _sdpa_reference(x, qc, sq, kc, sk, idx, cnt, block, sm):
         for h in range(H):
             for i in range(nb):
                 kept = np.zeros(nb, bool)
-                kept[idx[b, h, i, : cnt[b, h, i]]] = True
+                for j in idx[b, h, i, : cnt[b, h, i]]:
+                    if 0 <= j < nb:  # the valid entries, as a set
+                        kept[j] = True
                 mask[b, h, i * block: (i + 1) * block] = kept[tok_blk][None, :]
     out = torch.nn.functional.scaled_dot_product_attention(
         torch.from_numpy(qd), torch.from_numpy(kd), torch.from_numpy(v),
@@ -157,6 +159,43 @@ def test_empty_kept_list_gives_zeros():
     out = oracle.attention(qc, sq, kc, sk, x["v"], idx, cnt, w.block, oracle.default_sm_scale(64))
     assert np.all(out[0, 1, :64] == 0)
     assert np.any(out[0, 1, 64:] != 0)
+
+
+def test_kept_list_is_a_set():
+    """kept(i) is a set of key blocks (band union top-k): a list with repeats,
+    entries outside [0, nb) and any order gives the attention over the set
+    of its valid entries (masked SDPA in fp64 as the reference)."""
+    w = qsa_gen.get_workload("tiny").with_(grid=(1, 10, 30), block=64, head_dim=64)
+    x, qc, sq, kc, sk, idx, cnt = _pipeline(w, topk=2)
+    nb = w.n_blocks
+    rng = np.random.default_rng(5)
+    B, H = qc.shape[:2]
+    kmax = 9
+    messy = np.full((B, H, nb, kmax), -1, np.int32)
+    mcnt = np.zeros((B, H, nb), np.int32)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nb):
+                base = list(rng.choice(nb, size=int(rng.integers(1, 4)), replace=False))
+                lst = base + [base[0], -3, nb, 10 ** 6]
+                rng.shuffle(lst)
+                messy[b, h, i, :len(lst)] = lst
+                mcnt[b, h, i] = len(lst)
+    sm = oracle.default_sm_scale(64)
+    got = oracle.attention(qc, sq, kc, sk, x["v"], messy, mcnt, w.block, sm)
+    ref = _sdpa_reference(x, qc, sq, kc, sk, messy, mcnt, w.block, sm)
+    np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+    # and it equals the clean ascending list of the same set
+    clean = np.full_like(messy, -1)
+    ccnt = np.zeros_like(mcnt)
+    for b in range(B):
+        for h in range(H):
+            for i in range(nb):
+                st = sorted({int(j) for j in messy[b, h, i, :mcnt[b, h, i]] if 0 <= j < nb})
+                clean[b, h, i, :len(st)] = st
+                ccnt[b, h, i] = len(st)
+    want = oracle.attention(qc, sq, kc, sk, x["v"], clean, ccnt, w.block, sm)
+    np.testing.assert_array_equal(got, want)
 
 
 def test_sampled_blocks_match_full_run():
