@@ -150,6 +150,43 @@ int qsa_sparse_attn(const qsa_dims* dims, const int8_t* q_codes, const float* q_
                     void* stream);
 
 /*
+ * qsa_order_query_blocks -- a processing order of the query blocks of every
+ * (b, h) for qsa_sparse_attn_ordered.  Sparse attention gathers the key tiles
+ * of each query block's kept set (technical summary §1); blocks whose kept
+ * sets overlap can share those loads (in one workgroup and in one XCD's L2).
+ * The order puts such blocks next to each other.  The blocks of each (b, h)
+ * are cut into chunks of 256 consecutive blocks; each chunk is ordered by a
+ * greedy chain from its first block that always continues with the unused
+ * block of the chunk whose kept set shares the most bits with the current one
+ * in a 256-bit signature (bit j mod 256 for key block j), ties to the lowest
+ * index.  Chunks keep their natural order.  Deterministic.
+ *
+ *   kept_idx, kept_cnt in: as for qsa_sparse_attn (row stride kmax)
+ *   order             out: int32 [B,H,nb], a permutation of 0..nb-1 per (b, h)
+ */
+int qsa_order_query_blocks(const qsa_dims* dims, const int32_t* kept_idx,
+                           const int32_t* kept_cnt, int32_t kmax, int32_t* order,
+                           void* stream);
+
+/*
+ * qsa_sparse_attn_ordered -- qsa_sparse_attn with the query blocks of each
+ * (b, h) processed in the given order (a permutation, normally from
+ * qsa_order_query_blocks).  Every block is computed from its own kept set
+ * with the same arithmetic, so the outputs are bit-identical to
+ * qsa_sparse_attn's; only the sharing of key-tile loads changes.
+ *
+ *   order in: int32 [B,H,nb], a permutation of 0..nb-1 per (b, h).  Entries
+ *             outside [0, nb) are skipped; the output rows of a block that
+ *             the order does not list are left unwritten.
+ *   other arguments as qsa_sparse_attn.
+ */
+int qsa_sparse_attn_ordered(const qsa_dims* dims, const int8_t* q_codes, const float* q_scales,
+                            const int8_t* k_codes, const float* k_scales, const uint16_t* v,
+                            const int32_t* kept_idx, const int32_t* kept_cnt, int32_t kmax,
+                            const int32_t* order, float sm_scale, const uint16_t* r,
+                            const uint16_t* dr, uint16_t* out, void* stream);
+
+/*
  * qsa_full_attn_residual -- refresh step of the second-order sparse attention
  * reparameterisation (technical summary §2B): full attention over ALL key
  * blocks and sparse attention over kept(i), with the numerics of

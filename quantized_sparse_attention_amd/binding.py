@@ -29,7 +29,8 @@ QSA_MAX_BAND = 8
 QSA_MAX_BLOCKS = 16384
 
 EXPORTED = ("qsa_quantize", "qsa_select_blocks", "qsa_sparse_attn", "qsa_full_attn_residual",
-            "qsa_apply_residual", "qsa_status_string", "qsa_last_error_detail", "qsa_version")
+            "qsa_apply_residual", "qsa_order_query_blocks", "qsa_sparse_attn_ordered",
+            "qsa_status_string", "qsa_last_error_detail", "qsa_version")
 
 
 class QSAError(RuntimeError):
@@ -66,8 +67,11 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.qsa_full_attn_residual.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, i32, f32, i32, vp, vp,
                                            vp, vp]
     lib.qsa_apply_residual.argtypes = [pd, vp, vp, vp, vp, vp]
+    lib.qsa_order_query_blocks.argtypes = [pd, vp, vp, i32, vp, vp]
+    lib.qsa_sparse_attn_ordered.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, i32, vp, f32, vp, vp,
+                                            vp, vp]
     for f in ("qsa_quantize", "qsa_select_blocks", "qsa_sparse_attn", "qsa_full_attn_residual",
-              "qsa_apply_residual"):
+              "qsa_apply_residual", "qsa_order_query_blocks", "qsa_sparse_attn_ordered"):
         getattr(lib, f).restype = ctypes.c_int
     lib.qsa_status_string.argtypes = [ctypes.c_int]
     lib.qsa_status_string.restype = ctypes.c_char_p
@@ -202,6 +206,47 @@ def qsa_sparse_attn(q_codes, q_scales, k_codes, k_scales, v, kept_idx, kept_cnt,
         ctypes.byref(d), _ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(v),
         _ptr(kept_idx), _ptr(kept_cnt), int(kmax), ctypes.c_float(sm), _ptr(r), _ptr(dr),
         _ptr(out), _stream(stream)))
+    return out
+
+
+def qsa_order_query_blocks(kept_idx, kept_cnt, seq_len: int, block: int, head_dim: int,
+                           order=None, stream=None):
+    """int32 [B,H,nb] processing order grouping query blocks with overlapping kept sets."""
+    _need(kept_idx, "kept_idx", torch.int32)
+    if kept_idx.dim() != 4:
+        raise ValueError("kept_idx must be [B,H,nb,kmax]")
+    B, H, nb, kmax = kept_idx.shape
+    if nb != n_blocks(seq_len, block):
+        raise ValueError(f"kept_idx has {nb} rows, seq_len/block gives {n_blocks(seq_len, block)}")
+    _need(kept_cnt, "kept_cnt", torch.int32, (B, H, nb))
+    order = (torch.empty((B, H, nb), dtype=torch.int32, device=kept_idx.device) if order is None
+             else order)
+    _need(order, "order", torch.int32, (B, H, nb))
+    d = make_dims(B, H, seq_len, head_dim, block)
+    _check(load_library().qsa_order_query_blocks(ctypes.byref(d), _ptr(kept_idx), _ptr(kept_cnt),
+                                                 int(kmax), _ptr(order), _stream(stream)))
+    return order
+
+
+def qsa_sparse_attn_ordered(q_codes, q_scales, k_codes, k_scales, v, kept_idx, kept_cnt, order,
+                            block: int, sm_scale: float | None = None, r=None, dr=None, out=None,
+                            stream=None):
+    """qsa_sparse_attn with the query blocks processed in ``order`` (same outputs)."""
+    B, H, L, D, kmax = _attn_checks(q_codes, q_scales, k_codes, k_scales, v, kept_idx, kept_cnt,
+                                    block)
+    _need(order, "order", torch.int32, (B, H, n_blocks(L, block)))
+    if r is not None:
+        _need(r, "r", torch.bfloat16, (B, H, L, D))
+    if dr is not None:
+        _need(dr, "dr", torch.bfloat16, (B, H, L, D))
+    out = torch.empty_like(v) if out is None else out
+    _need(out, "out", torch.bfloat16, (B, H, L, D))
+    sm = default_sm_scale(D) if sm_scale is None else float(sm_scale)
+    d = make_dims(B, H, L, D, block)
+    _check(load_library().qsa_sparse_attn_ordered(
+        ctypes.byref(d), _ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(v),
+        _ptr(kept_idx), _ptr(kept_cnt), int(kmax), _ptr(order), ctypes.c_float(sm), _ptr(r),
+        _ptr(dr), _ptr(out), _stream(stream)))
     return out
 
 

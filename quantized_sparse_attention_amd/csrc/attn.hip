@@ -392,15 +392,19 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* p, float a, float b, floa
 // b-th query block i.  The tile walks below read them a 32-bit word at a time.
 constexpr int kMaxWords = QSA_MAX_BLOCKS / 32;
 
-template <int QB, int THREADS>
+template <int QB, int THREADS, typename BlockAt>
 __device__ __forceinline__ void build_kept_bits(uint32_t (*bits)[kMaxWords], const AttnArgs& a,
-                                                uint64_t row0, int nq, int nb, int tid) {
+                                                uint64_t row0, BlockAt&& block_at, int nq,
+                                                int nb, int tid) {
   const int nw = (nb + 31) >> 5;
   for (int k = tid; k < QB * nw; k += THREADS) bits[k / nw][k % nw] = 0u;
   __syncthreads();
   for (int b = 0; b < nq; ++b) {
-    const int32_t* kl = a.kept_idx + (row0 + b) * (uint64_t)a.kmax;
-    const int cnt = min(max(a.kept_cnt[row0 + b], 0), a.kmax);
+    const int blk = block_at(b);
+    if (blk < 0) continue;
+    const uint64_t row = row0 + blk;
+    const int32_t* kl = a.kept_idx + row * (uint64_t)a.kmax;
+    const int cnt = min(max(a.kept_cnt[row], 0), a.kmax);
     for (int p = tid; p < cnt; p += THREADS) {
       const int j = kl[p];
       if (j >= 0 && j < nb) atomicOr(&bits[b][j >> 5], 1u << (j & 31));
@@ -682,8 +686,19 @@ __attribute__((amdgpu_waves_per_eu(REFRESH ? 1 : 2, 8))) void attn_kernel(AttnAr
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int g = lane >> 5, ql = lane & 31;
   const int qsub = wave / C::WPB;  // this wave's query block within the group
-  const int i = (int)grp * QB + qsub;
   const int nq = min(QB, nb - (int)grp * QB);
+  const uint64_t row0 = bh * (uint64_t)nb;
+  // the group's query blocks: positions grp*QB .. grp*QB+nq-1 of the
+  // processing order (ascending unless an order is given)
+  // (an order entry outside [0, nb) names no block: -1)
+  auto block_at = [&](int b) -> int {
+    const int pos = (int)grp * QB + b;
+    if (!a.order) return pos;
+    const int v = a.order[row0 + pos];
+    return v >= 0 && v < nb ? v : -1;
+  };
+  int i = qsub < nq ? __builtin_amdgcn_readfirstlane(block_at(qsub)) : nb;
+  if (i < 0) i = nb;
 
   const uint64_t head_off = bh * (uint64_t)L * D;
 
@@ -716,7 +731,8 @@ __attribute__((amdgpu_waves_per_eu(REFRESH ? 1 : 2, 8))) void attn_kernel(AttnAr
   x.lane = lane;
   x.c0 = i < nb ? a.sm_scale * a.q_scales[bh * (uint64_t)nb + i] * kLog2e : 0.0f;
 
-  build_kept_bits<QB, THREADS>(s_bits, a, bh * (uint64_t)nb + grp * QB, nq, nb, tid);
+  build_kept_bits<QB, THREADS>(s_bits, a, row0, [&](int b) { return block_at(b); }, nq, nb,
+                               tid);
   const int n_tiles = (L + KT - 1) / KT;
   const int tail_t = (L % KT) ? n_tiles - 1 : -1;
   const int myb = i < nb ? qsub : -1;

@@ -222,6 +222,57 @@ int qsa_sparse_attn(const qsa_dims* dims, const int8_t* q_codes, const float* q_
   return launched(fn, qsa::launch_sparse_attn(*dims, a, static_cast<hipStream_t>(stream)));
 }
 
+int qsa_order_query_blocks(const qsa_dims* dims, const int32_t* kept_idx,
+                           const int32_t* kept_cnt, int32_t kmax, int32_t* order, void* stream) {
+  const char* fn = "qsa_order_query_blocks";
+  int st = check_dims(fn, dims);
+  if (st) return st;
+  const long long nb = ((long long)dims->seq_len + dims->block - 1) / dims->block;
+  if (nb > QSA_MAX_BLOCKS)
+    return fail(QSA_ERR_SHAPE, "%s: %lld blocks exceed QSA_MAX_BLOCKS=%d", fn, nb,
+                QSA_MAX_BLOCKS);
+  REQUIRE_PTR(kept_idx);
+  REQUIRE_PTR(kept_cnt);
+  REQUIRE_PTR(order);
+  if (kmax < 1) return fail(QSA_ERR_PARAM, "%s: kmax=%d must be >= 1", fn, kmax);
+  if ((st = check_device(fn))) return st;
+  (void)hipGetLastError();
+  return launched(fn, qsa::launch_order(*dims, kept_idx, kept_cnt, kmax, order,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int qsa_sparse_attn_ordered(const qsa_dims* dims, const int8_t* q_codes, const float* q_scales,
+                            const int8_t* k_codes, const float* k_scales, const uint16_t* v,
+                            const int32_t* kept_idx, const int32_t* kept_cnt, int32_t kmax,
+                            const int32_t* order, float sm_scale, const uint16_t* r,
+                            const uint16_t* dr, uint16_t* out, void* stream) {
+  const char* fn = "qsa_sparse_attn_ordered";
+  REQUIRE_PTR(order);
+  int st = check_attn_common(fn, dims, q_codes, q_scales, k_codes, k_scales, v, kept_idx,
+                             kept_cnt, kmax, sm_scale);
+  if (st) return st;
+  OPTIONAL_PTR(r);
+  OPTIONAL_PTR(dr);
+  REQUIRE_PTR(out);
+  if ((st = check_device(fn))) return st;
+  qsa::AttnArgs a{};
+  a.q_codes = q_codes;
+  a.q_scales = q_scales;
+  a.k_codes = k_codes;
+  a.k_scales = k_scales;
+  a.v = v;
+  a.kept_idx = kept_idx;
+  a.kept_cnt = kept_cnt;
+  a.order = order;
+  a.kmax = kmax;
+  a.sm_scale = sm_scale;
+  a.r_in = r;
+  a.dr_in = dr;
+  a.out = out;
+  (void)hipGetLastError();
+  return launched(fn, qsa::launch_sparse_attn(*dims, a, static_cast<hipStream_t>(stream)));
+}
+
 int qsa_full_attn_residual(const qsa_dims* dims, const int8_t* q_codes, const float* q_scales,
                            const int8_t* k_codes, const float* k_scales, const uint16_t* v,
                            const int32_t* kept_idx, const int32_t* kept_cnt, int32_t kmax,

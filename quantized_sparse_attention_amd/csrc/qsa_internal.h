@@ -67,6 +67,9 @@ struct AttnArgs {
   const uint16_t* v;
   const int32_t* kept_idx;
   const int32_t* kept_cnt;
+  // optional processing order of the query blocks, int32 [B,H,nb] (a
+  // permutation of 0..nb-1 per head), or NULL for ascending order
+  const int32_t* order;
   int32_t kmax;
   float sm_scale;
   // sparse step: optional residual inputs; refresh step: r in/out, dr out
@@ -80,6 +83,9 @@ struct AttnArgs {
 
 hipError_t launch_sparse_attn(const qsa_dims& d, const AttnArgs& a, hipStream_t s);
 hipError_t launch_full_attn_residual(const qsa_dims& d, const AttnArgs& a, hipStream_t s);
+
+hipError_t launch_order(const qsa_dims& d, const int32_t* kept_idx, const int32_t* kept_cnt,
+                        int32_t kmax, int32_t* order, hipStream_t s);
 
 hipError_t launch_apply_residual(const qsa_dims& d, const uint16_t* sparse_out,
                                  const uint16_t* r, const uint16_t* dr, uint16_t* out,

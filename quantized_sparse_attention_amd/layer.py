@@ -22,6 +22,9 @@ class QSAConfig:
     band: tuple = (0,)
     sm_scale: float | None = None
     order: int = 2  # 2: sparse + r + dr; 1: sparse + r (first-order reuse)
+    # process the query blocks of sparse steps in an order that groups blocks
+    # with overlapping kept sets (same outputs, more shared key-tile loads)
+    reorder: bool = True
 
 
 @dataclass
@@ -79,5 +82,10 @@ class QuantSparseAttention:
             return out
         if self.r is None:
             raise RuntimeError("sparse step before any full-attention refresh step")
+        dr = self.dr if c.order == 2 else None
+        if c.reorder:
+            order = B.qsa_order_query_blocks(idx, cnt, q.shape[2], c.block, q.shape[3])
+            return B.qsa_sparse_attn_ordered(qc, qs, kc, ks, v, idx, cnt, order, c.block,
+                                             c.sm_scale, r=self.r, dr=dr)
         return B.qsa_sparse_attn(qc, qs, kc, ks, v, idx, cnt, c.block, c.sm_scale, r=self.r,
-                                 dr=self.dr if c.order == 2 else None)
+                                 dr=dr)

@@ -101,6 +101,9 @@ def test_valid_arguments_reach_the_device_check(lib):
     assert lib.qsa_full_attn_residual(_d(), *P[:7], 2, ctypes.c_float(0.125), 1, P[7], P[8], P[9],
                                       None) == B.QSA_ERR_DEVICE
     assert lib.qsa_apply_residual(_d(), P[0], P[1], None, P[0], None) == B.QSA_ERR_DEVICE
+    assert lib.qsa_order_query_blocks(_d(), P[0], P[1], 2, P[2], None) == B.QSA_ERR_DEVICE
+    assert lib.qsa_sparse_attn_ordered(_d(), *P[:7], 2, P[8], ctypes.c_float(0.125), None, None,
+                                       P[7], None) == B.QSA_ERR_DEVICE
 
 
 def _sel(lib, topk=1, band=(0,), n_band=None, kmax=2, dims=None, ptrs=None):
@@ -146,6 +149,17 @@ def test_attention_validation(lib):
                                       None) == B.QSA_ERR_NULL
     assert lib.qsa_apply_residual(_d(), P[0], None, None, P[0], None) == B.QSA_ERR_NULL
     assert lib.qsa_apply_residual(_d(D=80), P[0], P[1], None, P[0], None) == B.QSA_ERR_SHAPE
+    assert lib.qsa_sparse_attn_ordered(_d(), *P[:7], 2, None, f(0.1), None, None, P[7],
+                                       None) == B.QSA_ERR_NULL
+    assert lib.qsa_sparse_attn_ordered(_d(), *P[:7], 2, P[8], f(0.0), None, None, P[7],
+                                       None) == B.QSA_ERR_PARAM
+    assert lib.qsa_order_query_blocks(_d(), P[0], P[1], 0, P[2], None) == B.QSA_ERR_PARAM
+    assert lib.qsa_order_query_blocks(_d(), P[0], None, 2, P[2], None) == B.QSA_ERR_NULL
+    assert lib.qsa_order_query_blocks(_d(), P[0], P[1], 2, ctypes.c_void_p(0x3004),
+                                      None) == B.QSA_ERR_ALIGN
+    big = _d(L=64 * (B.QSA_MAX_BLOCKS + 1))
+    assert lib.qsa_order_query_blocks(big, P[0], P[1], 2, P[2], None) == B.QSA_ERR_SHAPE
+    assert lib.qsa_sparse_attn(big, *P[:7], 2, f(0.1), None, None, P[7], None) == B.QSA_ERR_SHAPE
 
 
 def test_binding_refuses_cpu_tensors():

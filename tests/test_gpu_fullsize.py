@@ -52,7 +52,15 @@ def run(request):
     full = B.qsa_full_attn_residual(qc, qs, kc, ks, x["v"], idx, cnt, w.block, r, dr, 0)
     # a sparse step on the same inputs applying the cached residuals
     step = B.qsa_sparse_attn(qc, qs, kc, ks, x["v"], idx, cnt, w.block, r=r, dr=dr)
+    # the same step with the query blocks in the computed processing order
+    order = B.qsa_order_query_blocks(idx, cnt, w.seq_len, w.block, w.head_dim)
+    step_o = B.qsa_sparse_attn_ordered(qc, qs, kc, ks, x["v"], idx, cnt, order, w.block, r=r,
+                                       dr=dr)
     torch.cuda.synchronize()
+    srt, _ = torch.sort(order.long(), dim=-1)
+    order_ok = bool((srt == torch.arange(w.n_blocks, device=dev)).all())
+    ordered_same = torch.equal(step.view(torch.int16), step_o.view(torch.int16))
+    del step_o, order, srt
     heads = [0, w.heads // 2, w.heads - 1]
     host = {t: _bits(x[t][:, heads]) for t in "qkv"}
     g = {
@@ -68,6 +76,7 @@ def run(request):
         "dr_bits": _bits(dr[:, heads]),
         "finite": all(bool(torch.isfinite(t.float()).all()) for t in (sparse, full, r, step)),
         "idx_all": idx, "cnt_all": cnt,
+        "order_ok": order_ok, "ordered_same": ordered_same,
     }
     # the oracle's front end on the head subset
     oqc, osq, opq = oracle.quantize(host["q"], w.block)
@@ -133,6 +142,12 @@ def test_fullsize_kept_lists_valid_on_every_head(run):
 
 def test_fullsize_outputs_finite(run):
     assert run[3]["finite"]
+
+
+def test_fullsize_ordered_step_identical(run):
+    """The processing order is a permutation on every head and changes no output bit."""
+    assert run[3]["order_ok"]
+    assert run[3]["ordered_same"]
 
 
 def test_fullsize_sparse_sampled(run):

@@ -338,3 +338,100 @@ def test_deterministic():
     b = host_bits(B.qsa_sparse_attn(g["qc"], g["qs"], g["kc"], g["ks"], v, g["idx"], g["cnt"],
                                     w.block))
     assert np.array_equal(a, b)
+
+
+def _assert_permutation(order, nb):
+    srt, _ = torch.sort(order.long(), dim=-1)
+    assert bool((srt == torch.arange(nb, device=order.device)).all()), "order is not a permutation"
+
+
+@pytest.mark.parametrize("name", list(CFGS))
+def test_ordered_attention_is_identical(name):
+    """Processing the query blocks in the computed order changes no output bit."""
+    w, x, o, g = _setup(name)
+    v = dev_bf16(x["v"])
+    order = B.qsa_order_query_blocks(g["idx"], g["cnt"], w.seq_len, w.block, w.head_dim)
+    again = B.qsa_order_query_blocks(g["idx"], g["cnt"], w.seq_len, w.block, w.head_dim)
+    torch.cuda.synchronize()
+    _assert_permutation(order, w.n_blocks)
+    assert torch.equal(order, again), "order is not deterministic"
+    rng = np.random.default_rng(4)
+    r = dev_bf16(qsa_gen.f32_to_bf16_bits(rng.standard_normal(x["v"].shape).astype(np.float32)))
+    for rr in (None, r):
+        a = B.qsa_sparse_attn(g["qc"], g["qs"], g["kc"], g["ks"], v, g["idx"], g["cnt"], w.block,
+                              r=rr, dr=rr)
+        b = B.qsa_sparse_attn_ordered(g["qc"], g["qs"], g["kc"], g["ks"], v, g["idx"], g["cnt"],
+                                      order, w.block, r=rr, dr=rr)
+        assert np.array_equal(host_bits(a), host_bits(b))
+    # a reversed order, and kept lists with repeats / outside entries / any order
+    rev = torch.flip(order, dims=[-1]).contiguous()
+    c = B.qsa_sparse_attn_ordered(g["qc"], g["qs"], g["kc"], g["ks"], v, g["idx"], g["cnt"], rev,
+                                  w.block)
+    plain = B.qsa_sparse_attn(g["qc"], g["qs"], g["kc"], g["ks"], v, g["idx"], g["cnt"], w.block)
+    assert np.array_equal(host_bits(plain), host_bits(c))
+    idx, cnt, kmax = _messy_lists(w, 3)
+    di, dc = torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda()
+    om = B.qsa_order_query_blocks(di, dc, w.seq_len, w.block, w.head_dim)
+    _assert_permutation(om, w.n_blocks)
+    a = B.qsa_sparse_attn(g["qc"], g["qs"], g["kc"], g["ks"], v, di, dc, w.block)
+    b = B.qsa_sparse_attn_ordered(g["qc"], g["qs"], g["kc"], g["ks"], v, di, dc, om, w.block)
+    assert np.array_equal(host_bits(a), host_bits(b))
+
+
+def _reference_order(idx, cnt, nb, chunk=256, bits=256):
+    """The documented processing order, restated in numpy: per chunk of 256
+    blocks a greedy chain from the chunk's first block, always to the unused
+    block of the chunk whose 256-bit signature (bit j mod 256 for key block
+    j) shares the most bits with the current one, ties to the lowest index."""
+    Bn, H = cnt.shape[:2]
+    out = np.zeros((Bn, H, nb), np.int64)
+    for b in range(Bn):
+        for h in range(H):
+            sig = np.zeros((nb, bits), bool)
+            for i in range(nb):
+                js = [j for j in idx[b, h, i, :cnt[b, h, i]] if 0 <= j < nb]
+                sig[i, np.array(js, dtype=np.int64) % bits] = True
+            for c0 in range(0, nb, chunk):
+                n = min(chunk, nb - c0)
+                S = sig[c0:c0 + n].astype(np.int64)
+                M = S @ S.T
+                used = np.zeros(n, bool)
+                cur = 0
+                used[0] = True
+                seq = [0]
+                for _ in range(n - 1):
+                    sc = np.where(used, -1, M[cur])
+                    cur = int(np.argmax(sc))  # first maximum: lowest index
+                    used[cur] = True
+                    seq.append(cur)
+                out[b, h, c0:c0 + n] = c0 + np.array(seq)
+    return out
+
+
+@pytest.mark.parametrize("nb", [3, 257, 3000])
+def test_order_chunks(nb):
+    """The order permutes each chunk of 256 consecutive blocks within itself,
+    starts every chunk with its first block, and changes no output bit."""
+    D, blk, H = 64, 64, 2
+    L = nb * blk - 17  # a ragged last block
+    gen = torch.Generator(device="cuda").manual_seed(nb)
+    q = torch.randn((1, H, L, D), generator=gen, device="cuda").to(torch.bfloat16)
+    k = torch.randn((1, H, L, D), generator=gen, device="cuda").to(torch.bfloat16)
+    v = torch.randn((1, H, L, D), generator=gen, device="cuda").to(torch.bfloat16)
+    qc, qs, qp = B.qsa_quantize(q, blk)
+    kc, ks, kp = B.qsa_quantize(k, blk)
+    topk = min(3, nb)
+    idx, cnt = B.qsa_select_blocks(qp, qs, kp, ks, L, blk, topk, (0,), min(nb, topk + 1))
+    order = B.qsa_order_query_blocks(idx, cnt, L, blk, D)
+    torch.cuda.synchronize()
+    _assert_permutation(order, nb)
+    o = order.cpu().numpy()
+    for c0 in range(0, nb, 256):
+        seg = o[..., c0:c0 + 256]
+        assert np.all(seg[..., 0] == c0)
+        assert np.all(np.sort(seg, axis=-1) == np.arange(c0, min(nb, c0 + 256)))
+    ref = _reference_order(idx.cpu().numpy(), cnt.cpu().numpy(), nb)
+    assert np.array_equal(o, ref), "order differs from the documented greedy chain"
+    a = B.qsa_sparse_attn(qc, qs, kc, ks, v, idx, cnt, blk)
+    b = B.qsa_sparse_attn_ordered(qc, qs, kc, ks, v, idx, cnt, order, blk)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
