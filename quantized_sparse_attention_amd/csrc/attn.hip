@@ -414,22 +414,23 @@ __device__ __forceinline__ void build_kept_bits(uint32_t (*bits)[kMaxWords], con
 }
 
 // Walk, in ascending order, over the 64-key tiles of the key blocks that at
-// least one query block of the group needs: the kept blocks (REST = false) or
-// the blocks outside the kept set (REST = true, the refresh step's other
+// least one query block of the group needs: the kept blocks (rest = false) or
+// the blocks outside the kept set (rest = true, the refresh step's other
 // half).  Every wave of the workgroup produces the same tile sequence; `keep`
 // tells a wave whether its own query block needs the tile.  The short last
 // tile of the sequence is not returned: tail_hit / tail_keep record it.
-template <int QB, int SUB, bool REST>
+template <int QB, int SUB>
 struct BitWalk {
   const uint32_t (*bits)[kMaxWords];
   int nw, nq, myb, n_tiles, tail_t, last_bits;
   int wi, base, j, sub;
   uint32_t u, mine;
-  bool kj, tail_hit, tail_keep;
+  bool rest, kj, tail_hit, tail_keep;
 
   __device__ __forceinline__ void init(const uint32_t (*b)[kMaxWords], int nb, int nq_, int myb_,
-                                       int n_tiles_, int tail_t_) {
+                                       int n_tiles_, int tail_t_, bool rest_) {
     bits = b;
+    rest = rest_;
     nw = (nb + 31) >> 5;
     nq = nq_;
     myb = myb_;
@@ -448,7 +449,7 @@ struct BitWalk {
   }
   __device__ __forceinline__ uint32_t row_word(int b, int w) const {
     uint32_t v = bits[b][w];
-    if (REST) {
+    if (rest) {
       const uint32_t valid = w == nw - 1 && last_bits < 32 ? (1u << last_bits) - 1u : ~0u;
       v = ~v & valid;
     }
@@ -499,8 +500,6 @@ struct Ctx {
   const float* sk_h;
   int8_t* s_k;   // LDS tile buffer 0
   uint16_t* s_v;
-  int8_t* s_k1;  // LDS tile buffer 1 (double-buffered walk)
-  uint16_t* s_v1;
   int L;
   int wave, lane;
   float c0;
@@ -549,93 +548,6 @@ __device__ __forceinline__ void walk(const Ctx<BS, D>& x, const v4i (&qb)[Cfg<BS
   }
 }
 
-// vmcnt(n) wait: expcnt and lgkmcnt left at their maxima (no wait).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | 0xF00 | ((N >> 4) << 14));
-}
-
-// Double-buffered variant of walk(): two LDS tiles, the V operands read from
-// LDS during the PV MFMAs (no register copy), and the load of tile n+2 issued
-// into tile n's buffer as soon as every wave is done with it, so a tile's
-// loads have a whole iteration to land.  The loop is unrolled by two so each
-// buffer is a fixed LDS object.
-template <int BS, int D, int NWV, typename Next>
-__device__ __forceinline__ void walk2(const Ctx<BS, D>& x, const v4i (&qb)[Cfg<BS, D>::KS],
-                                      const LaneOffs<BS, D>& lo, Acc<BS, D>& acc, Next&& next) {
-  using C = Cfg<BS, D>;
-  constexpr int DMA_PER_TILE = Dma<D, NWV>::K + Dma<D, NWV>::V;
-  auto dma = [&](int t, int8_t* lk, uint16_t* lv) {
-    dma_tile<BS, D, NWV>(x.kc_h + (size_t)t * KT * D, x.v_h + (size_t)t * KT * D, lk, lv, x.wave,
-                         x.lane, KT);
-  };
-  auto step = [&](int t, bool keep, const int8_t* lk, const uint16_t* lv) {
-    if (!keep) return;
-    t = __builtin_amdgcn_readfirstlane(t);
-    const float cs = x.c0 * load_uniform(x.sk_h, t / C::SUB);
-    v4i kop[C::NT][C::KS];
-#pragma unroll
-    for (int tt = 0; tt < C::NT; ++tt)
-#pragma unroll
-      for (int c = 0; c < C::KS; ++c)
-        kop[tt][c] = *reinterpret_cast<const v4i*>(lk + 32 * tt * D + lo.k[c]);
-    v16i sc[C::NT];
-    qk<BS, D>(kop, qb, sc);
-    uint32_t pk[C::NT][8];
-    softmax_update<BS, D, false>(acc, sc, pk, qb, x.kc_h + (size_t)t * KT * D, x.lane, cs, KT);
-    pv_lds<BS, D>(acc, lo, lv, pk);
-  };
-  bool kc = false, kn = false, knn = false;
-  int cur = next(kc);
-  if (cur < 0) return;
-  __syncthreads();  // both LDS tiles are free
-  dma(cur, x.s_k, x.s_v);
-  int nxt = next(kn);
-  if (nxt >= 0) {
-    dma(nxt, x.s_k1, x.s_v1);
-    wait_vmcnt<DMA_PER_TILE>();  // the first tile landed (the second may be in flight)
-  } else {
-    wait_vmcnt<0>();
-  }
-  __syncthreads();
-  while (true) {
-    step(cur, kc, x.s_k, x.s_v);
-    wait_vmcnt<0>();  // the next tile landed in buffer 1
-    __syncthreads();  // and every wave is done with buffer 0
-    if (nxt < 0) break;
-    int nn = next(knn);
-    if (nn >= 0) dma(nn, x.s_k, x.s_v);
-    cur = nxt;
-    kc = kn;
-    nxt = nn;
-    kn = knn;
-    step(cur, kc, x.s_k1, x.s_v1);
-    wait_vmcnt<0>();
-    __syncthreads();
-    if (nxt < 0) break;
-    nn = next(knn);
-    if (nn >= 0) dma(nn, x.s_k1, x.s_v1);
-    cur = nxt;
-    kc = kn;
-    nxt = nn;
-    kn = knn;
-  }
-}
-
-// The sparse kernel (two waves per SIMD, a single LDS tile per workgroup)
-// walks with the operands copied to registers; the refresh kernel (one wave
-// per SIMD, registers taken by two accumulators) double-buffers in LDS.
-template <int BS, int D, int NWV, bool REFRESH, typename Next>
-__device__ __forceinline__ void walk_any(const Ctx<BS, D>& x, const v4i (&qb)[Cfg<BS, D>::KS],
-                                         const LaneOffs<BS, D>& lo, Acc<BS, D>& acc,
-                                         Next&& next) {
-  if (REFRESH)
-    walk2<BS, D, NWV>(x, qb, lo, acc, next);
-  else
-    walk<BS, D, NWV>(x, qb, lo, acc, next);
-}
-
 // The short last tile of the sequence (keys >= nvalid masked); every wave
 // loads its share, the waves whose query block keeps it compute it.
 template <int BS, int D, int NWV>
@@ -666,16 +578,13 @@ __device__ __forceinline__ void tail_tile(const Ctx<BS, D>& x, const v4i (&qb)[C
 // kernel carries two output accumulators and runs one wave per SIMD.
 template <int BS, int D, int QB, bool REFRESH>
 __global__ __launch_bounds__((QB * BS / 32 * 64))
-__attribute__((amdgpu_waves_per_eu(REFRESH ? 1 : 2, 8))) void attn_kernel(AttnArgs a, int L, int nb,
+__attribute__((amdgpu_waves_per_eu(2, 8))) void attn_kernel(AttnArgs a, int L, int nb,
                                                                         uint32_t n_work) {
   using C = Cfg<BS, D>;
   constexpr int NWV = QB * C::WPB;  // waves in the workgroup
   constexpr int THREADS = 64 * NWV;
   __shared__ __attribute__((aligned(1024))) int8_t s_k[C::K_BYTES];
   __shared__ __attribute__((aligned(1024))) uint16_t s_v[C::V_BYTES / 2];
-  // second LDS tile of the refresh kernel's double-buffered walk
-  __shared__ __attribute__((aligned(1024))) int8_t s_k1[REFRESH ? C::K_BYTES : 16];
-  __shared__ __attribute__((aligned(1024))) uint16_t s_v1[REFRESH ? C::V_BYTES / 2 : 8];
   __shared__ uint32_t s_bits[QB][kMaxWords];
 
   const uint32_t ng = (uint32_t)((nb + QB - 1) / QB);
@@ -724,8 +633,6 @@ __attribute__((amdgpu_waves_per_eu(REFRESH ? 1 : 2, 8))) void attn_kernel(AttnAr
   x.sk_h = a.k_scales + bh * (uint64_t)nb;
   x.s_k = s_k;
   x.s_v = s_v;
-  x.s_k1 = s_k1;
-  x.s_v1 = s_v1;
   x.L = L;
   x.wave = wave;
   x.lane = lane;
@@ -737,50 +644,54 @@ __attribute__((amdgpu_waves_per_eu(REFRESH ? 1 : 2, 8))) void attn_kernel(AttnAr
   const int tail_t = (L % KT) ? n_tiles - 1 : -1;
   const int myb = i < nb ? qsub : -1;
 
-  Acc<BS, D> acc_k;  // kept blocks (the sparse attention)
-  acc_k.init();
-  Acc<BS, D> acc_n;  // the other blocks (refresh step only)
-  if (REFRESH) acc_n.init();
-
-  {
-    BitWalk<QB, C::SUB, false> w;
-    w.init(s_bits, nb, nq, myb, n_tiles, tail_t);
-    walk_any<BS, D, NWV, REFRESH>(x, qb, lo, acc_k, [&](bool& keep) { return w.next(keep); });
-    if (w.tail_hit) tail_tile<BS, D, NWV>(x, qb, lo, acc_k, tail_t, w.tail_keep);
-  }
-  if (REFRESH) {
-    // every other block: with the kept ones, the full attention
-    BitWalk<QB, C::SUB, true> w;
-    w.init(s_bits, nb, nq, myb, n_tiles, tail_t);
-    walk_any<BS, D, NWV, REFRESH>(x, qb, lo, acc_n, [&](bool& keep) { return w.next(keep); });
-    if (w.tail_hit) tail_tile<BS, D, NWV>(x, qb, lo, acc_n, tail_t, w.tail_keep);
-  }
-
-  // ---- epilogue --------------------------------------------------------------
-  const float lk = acc_k.l + __shfl_xor(acc_k.l, 32, 64);
-  const float inv_k = lk > 0.0f ? 1.0f / lk : 0.0f;
-  float wk = 0.0f, wn = 0.0f;
-  if (REFRESH) {
-    const float ln = acc_n.l + __shfl_xor(acc_n.l, 32, 64);
-    const float m = fmaxf(acc_k.m, acc_n.m);
-    const float ak = acc_k.started ? __builtin_amdgcn_exp2f(acc_k.m - m) : 0.0f;
-    const float an = acc_n.started ? __builtin_amdgcn_exp2f(acc_n.m - m) : 0.0f;
-    const float lf = lk * ak + ln * an;
-    const float inv_f = lf > 0.0f ? 1.0f / lf : 0.0f;
-    wk = ak * inv_f;
-    wn = an * inv_f;
-  }
-  if (!qvalid) return;
+  // One online-softmax state.  It first runs over the kept blocks: that is
+  // the sparse attention.  The refresh step parks the sparse output and then
+  // continues the same state over every other block: the full attention.
+  Acc<BS, D> acc;
+  acc.init();
   const size_t row_off = head_off + (size_t)qrow * D;
+  float inv_k = 0.0f;
+#pragma unroll 1
+  for (int phase = 0; phase < (REFRESH ? 2 : 1); ++phase) {
+    BitWalk<QB, C::SUB> w;
+    w.init(s_bits, nb, nq, myb, n_tiles, tail_t, phase == 1);
+    walk<BS, D, NWV>(x, qb, lo, acc, [&](bool& keep) { return w.next(keep); });
+    if (w.tail_hit) tail_tile<BS, D, NWV>(x, qb, lo, acc, tail_t, w.tail_keep);
+    if (phase == 0) {
+      const float lk = acc.l + __shfl_xor(acc.l, 32, 64);
+      inv_k = lk > 0.0f ? 1.0f / lk : 0.0f;
+    }
+    if (REFRESH && phase == 0 && qvalid) {
+      // Park the sparse output in fp32 in this row's own output slots (upper
+      // halves in dr, lower halves in out, both written for good in the
+      // epilogue), so the state can go on to the full attention.
 #pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) {
+      for (int dt = 0; dt < C::DT; ++dt) {
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int d0 = 32 * dt + 8 * r4 + 4 * g;
-      float os[4];
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const int d0 = 32 * dt + 8 * r4 + 4 * g;
+          uint32_t u[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) os[e] = acc_k.o[dt][4 * r4 + e] * inv_k;
-      if (!REFRESH) {
+          for (int e = 0; e < 4; ++e) u[e] = __float_as_uint(acc.o[dt][4 * r4 + e] * inv_k);
+          *reinterpret_cast<uint2*>(a.dr_out + row_off + d0) = make_uint2(
+              (u[0] >> 16) | (u[1] & 0xffff0000u), (u[2] >> 16) | (u[3] & 0xffff0000u));
+          *reinterpret_cast<uint2*>(a.out + row_off + d0) =
+              make_uint2((u[0] & 0xffffu) | (u[1] << 16), (u[2] & 0xffffu) | (u[3] << 16));
+        }
+      }
+    }
+  }
+
+  if (!REFRESH) {
+    if (!qvalid) return;
+#pragma unroll
+    for (int dt = 0; dt < C::DT; ++dt) {
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = 32 * dt + 8 * r4 + 4 * g;
+        float os[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) os[e] = acc.o[dt][4 * r4 + e] * inv_k;
         if (a.r_in) {
           const float4 rv = load_bf16x4(a.r_in + row_off + d0);
           os[0] += rv.x; os[1] += rv.y; os[2] += rv.z; os[3] += rv.w;
@@ -790,23 +701,41 @@ __attribute__((amdgpu_waves_per_eu(REFRESH ? 1 : 2, 8))) void attn_kernel(AttnAr
           os[0] += dv.x; os[1] += dv.y; os[2] += dv.z; os[3] += dv.w;
         }
         store_bf16x4(a.out + row_off + d0, os[0], os[1], os[2], os[3]);
-      } else {
-        float of[4], rho[4], drv[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          of[e] = acc_k.o[dt][4 * r4 + e] * wk + acc_n.o[dt][4 * r4 + e] * wn;
-          rho[e] = of[e] - os[e];
-          drv[e] = 0.0f;
-        }
-        if (a.has_prev) {
-          const float4 rp = load_bf16x4(a.r_out + row_off + d0);
-          drv[0] = rho[0] - rp.x; drv[1] = rho[1] - rp.y;
-          drv[2] = rho[2] - rp.z; drv[3] = rho[3] - rp.w;
-        }
-        store_bf16x4(a.dr_out + row_off + d0, drv[0], drv[1], drv[2], drv[3]);
-        store_bf16x4(a.r_out + row_off + d0, rho[0], rho[1], rho[2], rho[3]);
-        store_bf16x4(a.out + row_off + d0, of[0], of[1], of[2], of[3]);
       }
+    }
+    return;
+  }
+
+  const float lf = acc.l + __shfl_xor(acc.l, 32, 64);
+  const float inv_f = lf > 0.0f ? 1.0f / lf : 0.0f;
+  if (!qvalid) return;
+#pragma unroll
+  for (int dt = 0; dt < C::DT; ++dt) {
+#pragma unroll
+    for (int r4 = 0; r4 < 4; ++r4) {
+      const int d0 = 32 * dt + 8 * r4 + 4 * g;
+      const uint2 hi = *reinterpret_cast<const uint2*>(a.dr_out + row_off + d0);
+      const uint2 lw = *reinterpret_cast<const uint2*>(a.out + row_off + d0);
+      float os[4];
+      os[0] = __uint_as_float((hi.x << 16) | (lw.x & 0xffffu));
+      os[1] = __uint_as_float((hi.x & 0xffff0000u) | (lw.x >> 16));
+      os[2] = __uint_as_float((hi.y << 16) | (lw.y & 0xffffu));
+      os[3] = __uint_as_float((hi.y & 0xffff0000u) | (lw.y >> 16));
+      float of[4], rho[4], drv[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        of[e] = acc.o[dt][4 * r4 + e] * inv_f;
+        rho[e] = of[e] - os[e];
+        drv[e] = 0.0f;
+      }
+      if (a.has_prev) {
+        const float4 rp = load_bf16x4(a.r_out + row_off + d0);
+        drv[0] = rho[0] - rp.x; drv[1] = rho[1] - rp.y;
+        drv[2] = rho[2] - rp.z; drv[3] = rho[3] - rp.w;
+      }
+      store_bf16x4(a.dr_out + row_off + d0, drv[0], drv[1], drv[2], drv[3]);
+      store_bf16x4(a.r_out + row_off + d0, rho[0], rho[1], rho[2], rho[3]);
+      store_bf16x4(a.out + row_off + d0, of[0], of[1], of[2], of[3]);
     }
   }
 }
@@ -827,8 +756,8 @@ hipError_t launch_t(const qsa_dims& d, const AttnArgs& a, hipStream_t s) {
 // runs one block per workgroup.
 template <bool REFRESH>
 hipError_t dispatch(const qsa_dims& d, const AttnArgs& a, hipStream_t s) {
-  constexpr int Q64 = REFRESH ? 1 : QSA_ATTN_QB;
-  constexpr int Q64s = REFRESH ? 1 : (QSA_ATTN_QB < 2 ? QSA_ATTN_QB : 2);
+  constexpr int Q64 = QSA_ATTN_QB;
+  constexpr int Q64s = QSA_ATTN_QB < 2 ? QSA_ATTN_QB : 2;
   if (d.block == 64 && d.head_dim == 128) return launch_t<64, 128, Q64, REFRESH>(d, a, s);
   if (d.block == 64 && d.head_dim == 64) return launch_t<64, 64, Q64s, REFRESH>(d, a, s);
   if (d.block == 128 && d.head_dim == 128) return launch_t<128, 128, Q64s, REFRESH>(d, a, s);
