@@ -114,8 +114,11 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
           const double S = (double)hh[r] * 16384.0 + (double)mid[r] * 128.0 + (double)ll[r];
           const double a = (double)sqh[i] * skj;
           const double b = S * a;
-          const double c = (double)min(bs, L - i * bs) * (double)nj;
-          s_keys[(uint64_t)row * nb + j] = order_key(b / c);
+          const int ci = min(bs, L - i * bs) * nj;
+          // a power of two (every pair of full blocks) divides exactly by a
+          // multiplication with its inverse: the same IEEE result as b / c
+          const double q = (ci & (ci - 1)) == 0 ? b * (1.0 / (double)ci) : b / (double)ci;
+          s_keys[(uint64_t)row * nb + j] = order_key(q);
         }
       }
     }
@@ -136,16 +139,21 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const bool do_select = active && k_eff > 0 && k_eff < nb;
     for (int pass = 0; pass < 8; ++pass) {
       const int shift = 56 - 8 * pass;
+      // The histogram is this wave's own: LDS operations of one wave are
+      // performed in order, so waiting for them (lgkmcnt) orders the zeroing,
+      // the counting and the reads without a workgroup barrier.
 #pragma unroll
       for (int e = 0; e < 4; ++e) s_hist[wave][lane * 4 + e] = 0;
-      __syncthreads();
+      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+      __builtin_amdgcn_wave_barrier();
       if (do_select) {
         for (int j = lane; j < nb; j += 64) {
           const uint64_t key = keys[j];
           if ((key & pmask) == prefix) atomicAdd(&s_hist[wave][(key >> shift) & 0xff], 1u);
         }
       }
-      __syncthreads();
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+      __builtin_amdgcn_wave_barrier();
       if (do_select) {
         uint32_t c[4];
 #pragma unroll
