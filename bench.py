@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0,
                    help="approximate CPU time budget of the oracle baseline sample")
+    p.add_argument("--rotate", action="store_true",
+                   help="quantise Hadamard-rotated Q/K rows (attention with sm_scale / D)")
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="before the run, copy a bf16 buffer of this many MiB once with a "
                         "plain elementwise kernel (reads and writes each byte once): the "
@@ -98,7 +100,7 @@ def dense_ops(B, H, L, D):
     return 2.0 * B * H * L * L * D
 
 
-def cpu_baseline(w, budget_s: float):
+def cpu_baseline(w, budget_s: float, rotate: bool = False):
     """Time the oracle on a bounded sample of one sparse layer step; scale to a layer."""
     import numpy as np
 
@@ -111,12 +113,15 @@ def cpu_baseline(w, budget_s: float):
         threads = os.cpu_count() or 1
     x = qsa_gen.make_qkv(w, 0, heads=[0])
     t0 = time.perf_counter()
-    qc, sq, pq = oracle.quantize(x["q"], w.block)
-    kc, sk, pk = oracle.quantize(x["k"], w.block)
+    quant = oracle.quantize_rotated if rotate else oracle.quantize
+    qc, sq, pq = quant(x["q"], w.block)
+    kc, sk, pk = quant(x["k"], w.block)
     sc = oracle.block_scores(pq, sq, pk, sk, w.seq_len, w.block)
     idx, cnt = oracle.select_blocks(sc, w.topk, w.band, w.kmax)
     t_front = time.perf_counter() - t0
     sm = oracle.default_sm_scale(w.head_dim)
+    if rotate:
+        sm = np.float32(sm / np.float32(w.head_dim))
     nb = w.n_blocks
     order = np.random.default_rng(0).permutation(nb)
     done = 0
@@ -189,26 +194,29 @@ def main():
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
 
+    quant = Bn.qsa_quantize_rotated if args.rotate else Bn.qsa_quantize
+    sm = Bn.default_sm_scale(D) / D if args.rotate else None
+
     def layer_step(s, kind, rec):
         x = inputs[s]
         idx, cnt = kept[s]
         e = [ev() for _ in range(5)]
         e[0].record(stream)
-        Bn.qsa_quantize(x["q"], bs, qc, qs, qp)
-        Bn.qsa_quantize(x["k"], bs, kc, ks, kp)
+        quant(x["q"], bs, qc, qs, qp)
+        quant(x["k"], bs, kc, ks, kp)
         e[1].record(stream)
         Bn.qsa_select_blocks(qp, qs, kp, ks, L, bs, w.topk, w.band, kmax, idx, cnt)
         e[2].record(stream)
         if kind == "F":
             Bn.qsa_full_attn_residual(qc, qs, kc, ks, x["v"], idx, cnt, bs, r, dr,
-                                      state["has_prev"], out_full=out)
+                                      state["has_prev"], sm, out_full=out)
             state["has_prev"] = True
             e[4].record(stream)
         else:
             Bn.qsa_order_query_blocks(idx, cnt, L, bs, D, order)
             e[4].record(stream)
-            Bn.qsa_sparse_attn_ordered(qc, qs, kc, ks, x["v"], idx, cnt, order, bs, r=r, dr=dr,
-                                       out=out)
+            Bn.qsa_sparse_attn_ordered(qc, qs, kc, ks, x["v"], idx, cnt, order, bs, sm, r=r,
+                                       dr=dr, out=out)
         e[3].record(stream)
         if rec is not None:
             rec.append((kind, s, e))
@@ -279,6 +287,7 @@ def main():
         "config": {"workload": w.name, "batch": B, "heads": H, "seq_len": L, "head_dim": D,
                    "block": bs, "topk": w.topk, "band": list(w.band),
                    "density_kept": round(density, 4), "schedule": schedule,
+                   "rotated_quantisation": bool(args.rotate),
                    "step": "one denoising cycle (%s) of one attention layer" % schedule},
         "effective_tops": round(achieved / 1e12, 1),
         "pct_mfma_peak": round(100 * tmin / t_attn, 1) if t_attn > 0 else None,
@@ -286,7 +295,7 @@ def main():
         "refresh_step_ms_per_layer": round(ms_refresh, 4),
         "cycle_avg_ms_per_layer": round(ms_per_step / len(schedule), 4),
         "kernels_ms": {
-            "qsa_quantize": round(t_q1 * 1e3, 4),
+            quant.__name__: round(t_q1 * 1e3, 4),
             "qsa_select_blocks": round(mean(t_sel), 4),
             "qsa_order_query_blocks": round(mean(t_order), 4),
             "qsa_sparse_attn_ordered": round(mean(t_sparse), 4),
@@ -309,14 +318,14 @@ def main():
                 "bound": "mfma", "achieved": round(2 * dops / t_ref / 1e12, 1) if t_ref else None,
                 "peak": round(ref_peak / 1e12, 1), "unit": "TFLOP/s",
                 "frac": round(2 * dops / t_ref / ref_peak, 4) if t_ref else None},
-            "qsa_quantize": {
+            quant.__name__: {
                 "bound": "hbm", "achieved": round(q_bytes / t_q1 / 1e9, 1) if t_q1 else None,
                 "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                 "frac": round(q_bytes / t_q1 / PEAK_HBM_BYTES, 4) if t_q1 else None},
         },
     }
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.rotate)
     print(json.dumps(res), flush=True)
 
 

@@ -89,6 +89,27 @@ int qsa_quantize(const qsa_dims* dims, const uint16_t* x, int8_t* codes, float* 
                  int32_t* pooled, void* stream);
 
 /*
+ * qsa_quantize_rotated -- qsa_quantize of the Hadamard-rotated rows: every
+ * token row x (D channels) is first replaced by y = x H_D, H_D the Sylvester
+ * Hadamard matrix (entries +-1, H_1 = [1], H_2n = [[H_n, H_n], [H_n, -H_n]]),
+ * computed in fp32 by the fast Walsh-Hadamard transform: stages h = 1, 2, 4,
+ * ..., D/2, each replacing every pair (j, j+h) of a 2h-aligned group by
+ * (v_j + v_{j+h}, v_j - v_{j+h}) with fp32 rounding; codes, scales and pooled
+ * sums are then those of qsa_quantize applied to y.  The rotation spreads
+ * extreme channels over all channels before quantisation (DVD-Quant,
+ * gist.science/es/paper/2505.18663, technical summary §2B, rotated
+ * quantisation).  H_D H_D^T = D I: before quantisation every q k^T and every
+ * pooled saliency product is scaled by exactly D, so attention on rotated
+ * codes uses sm_scale / D, and qsa_select_blocks on rotated pooled sums
+ * ranks key blocks as on unrotated ones up to quantisation error (near-equal
+ * scores may swap).
+ *
+ *   arguments, layouts and errors as qsa_quantize.
+ */
+int qsa_quantize_rotated(const qsa_dims* dims, const uint16_t* x, int8_t* codes, float* scales,
+                         int32_t* pooled, void* stream);
+
+/*
  * qsa_select_blocks -- block-sparse attention mask: for every query block i
  * keep its top-k key blocks by pooled saliency plus a fixed band of block
  * offsets (attention sparsification to ~15 % density, technical summary §1

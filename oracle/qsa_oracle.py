@@ -42,6 +42,13 @@ R7  SSAR ([QS-es] §2B, [QS-ko] §2.2): the first-order residual is the
     output sparse + r + dr.  Both residuals are stored in bf16.
 R8  the SVD projection of the second-order residual ([QS-es] §2B) is not
     part of this path.
+R9  rotated quantisation (DVD-Quant, gist.science/es/paper/2505.18663,
+    technical summary §2B: a Hadamard rotation spreads extreme channels
+    before quantisation, with scales computed online): every Q and K row x
+    becomes y = x H_D, H_D the unscaled Sylvester Hadamard matrix, computed
+    in fp32 by the fast Walsh-Hadamard transform with stages h = 1, 2, ...,
+    D/2; y is then quantised by R1/R2 (the per-block scale is the online
+    scale).  H_D H_D^T = D I, so attention on rotated codes uses sm_scale/D.
 """
 from __future__ import annotations
 
@@ -53,6 +60,8 @@ __all__ = [
     "default_sm_scale",
     "block_bounds",
     "quantize",
+    "fwht",
+    "quantize_rotated",
     "block_scores",
     "select_blocks",
     "attention",
@@ -120,7 +129,38 @@ def quantize(x_bits, block: int):
     Returns codes int8 [B, H, L, D], scales float32 [B, H, nb] and the pooled
     code sums int64 [B, H, nb, D] (sum of a block's codes per channel).
     """
-    x = _bf16_to_f32(x_bits)
+    return _quantize_values(_bf16_to_f32(x_bits), block)
+
+
+def fwht(x):
+    """Rows of x (float32, last axis D, a power of two) times the Sylvester
+    Hadamard matrix H_D, by the fast Walsh-Hadamard transform in float32 (R9).
+
+    Stage h = 1, 2, 4, ..., D/2 replaces every pair (j, j+h) of each
+    2h-aligned group by (v_j + v_{j+h}, v_j - v_{j+h}), rounding to float32.
+    """
+    y = np.array(x, dtype=np.float32, copy=True)
+    D = y.shape[-1]
+    lead = y.shape[:-1]
+    h = 1
+    while h < D:
+        g = y.reshape(lead + (D // (2 * h), 2, h))
+        a = g[..., 0, :].copy()
+        b = g[..., 1, :].copy()
+        g[..., 0, :] = a + b
+        g[..., 1, :] = a - b
+        y = g.reshape(lead + (D,))
+        h *= 2
+    return y
+
+
+def quantize_rotated(x_bits, block: int):
+    """quantize() of the rotated rows fwht(x) of bf16 x [B, H, L, D] (R9)."""
+    return _quantize_values(fwht(_bf16_to_f32(x_bits)), block)
+
+
+def _quantize_values(x, block: int):
+    """R1/R2/R3 quantisation of float32 values x [B, H, L, D]."""
     B, H, L, D = x.shape
     bounds = block_bounds(L, block)
     codes = np.zeros((B, H, L, D), dtype=np.int8)

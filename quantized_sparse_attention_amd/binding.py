@@ -30,6 +30,7 @@ QSA_MAX_BLOCKS = 16384
 
 EXPORTED = ("qsa_quantize", "qsa_select_blocks", "qsa_sparse_attn", "qsa_full_attn_residual",
             "qsa_apply_residual", "qsa_order_query_blocks", "qsa_sparse_attn_ordered",
+            "qsa_quantize_rotated",
             "qsa_status_string", "qsa_last_error_detail", "qsa_version")
 
 
@@ -62,6 +63,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     vp, i32, f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
     pd = ctypes.POINTER(qsa_dims)
     lib.qsa_quantize.argtypes = [pd, vp, vp, vp, vp, vp]
+    lib.qsa_quantize_rotated.argtypes = [pd, vp, vp, vp, vp, vp]
     lib.qsa_select_blocks.argtypes = [pd, vp, vp, vp, vp, i32, vp, i32, i32, vp, vp, vp]
     lib.qsa_sparse_attn.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp]
     lib.qsa_full_attn_residual.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, i32, f32, i32, vp, vp,
@@ -70,7 +72,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.qsa_order_query_blocks.argtypes = [pd, vp, vp, i32, vp, vp]
     lib.qsa_sparse_attn_ordered.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, i32, vp, f32, vp, vp,
                                             vp, vp]
-    for f in ("qsa_quantize", "qsa_select_blocks", "qsa_sparse_attn", "qsa_full_attn_residual",
+    for f in ("qsa_quantize", "qsa_quantize_rotated", "qsa_select_blocks", "qsa_sparse_attn", "qsa_full_attn_residual",
               "qsa_apply_residual", "qsa_order_query_blocks", "qsa_sparse_attn_ordered"):
         getattr(lib, f).restype = ctypes.c_int
     lib.qsa_status_string.argtypes = [ctypes.c_int]
@@ -122,8 +124,7 @@ def make_dims(B: int, H: int, L: int, D: int, block: int) -> qsa_dims:
     return qsa_dims(B, H, L, D, block)
 
 
-def qsa_quantize(x: torch.Tensor, block: int, codes=None, scales=None, pooled=None, stream=None):
-    """int8 codes, fp32 block scales and int32 pooled code sums of bf16 x [B,H,L,D]."""
+def _quantize(fn, x, block, codes, scales, pooled, stream):
     B, H, L, D = x.shape
     nb = n_blocks(L, block)
     _need(x, "x", torch.bfloat16)
@@ -136,9 +137,20 @@ def qsa_quantize(x: torch.Tensor, block: int, codes=None, scales=None, pooled=No
     _need(scales, "scales", torch.float32, (B, H, nb))
     _need(pooled, "pooled", torch.int32, (B, H, nb, D))
     d = make_dims(B, H, L, D, block)
-    _check(load_library().qsa_quantize(ctypes.byref(d), _ptr(x), _ptr(codes), _ptr(scales),
+    _check(getattr(load_library(), fn)(ctypes.byref(d), _ptr(x), _ptr(codes), _ptr(scales),
                                        _ptr(pooled), _stream(stream)))
     return codes, scales, pooled
+
+
+def qsa_quantize(x: torch.Tensor, block: int, codes=None, scales=None, pooled=None, stream=None):
+    """int8 codes, fp32 block scales and int32 pooled code sums of bf16 x [B,H,L,D]."""
+    return _quantize("qsa_quantize", x, block, codes, scales, pooled, stream)
+
+
+def qsa_quantize_rotated(x: torch.Tensor, block: int, codes=None, scales=None, pooled=None,
+                         stream=None):
+    """qsa_quantize of the Hadamard-rotated rows x H_D (attention then uses sm_scale / D)."""
+    return _quantize("qsa_quantize_rotated", x, block, codes, scales, pooled, stream)
 
 
 def qsa_select_blocks(pooled_q, scale_q, pooled_k, scale_k, seq_len: int, block: int, topk: int,

@@ -150,6 +150,21 @@ int qsa_quantize(const qsa_dims* dims, const uint16_t* x, int8_t* codes, float* 
                                            static_cast<hipStream_t>(stream)));
 }
 
+int qsa_quantize_rotated(const qsa_dims* dims, const uint16_t* x, int8_t* codes, float* scales,
+                         int32_t* pooled, void* stream) {
+  const char* fn = "qsa_quantize_rotated";
+  int st = check_dims(fn, dims);
+  if (st) return st;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(codes);
+  REQUIRE_PTR(scales);
+  REQUIRE_PTR(pooled);
+  if ((st = check_device(fn))) return st;
+  (void)hipGetLastError();
+  return launched(fn, qsa::launch_quantize_rotated(*dims, x, codes, scales, pooled,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 int qsa_select_blocks(const qsa_dims* dims, const int32_t* pooled_q, const float* scale_q,
                       const int32_t* pooled_k, const float* scale_k, int32_t topk,
                       const int32_t* band_offsets, int32_t n_band, int32_t kmax,

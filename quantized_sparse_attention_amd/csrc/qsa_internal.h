@@ -54,6 +54,9 @@ struct Band {
 hipError_t launch_quantize(const qsa_dims& d, const uint16_t* x, int8_t* codes, float* scales,
                            int32_t* pooled, hipStream_t s);
 
+hipError_t launch_quantize_rotated(const qsa_dims& d, const uint16_t* x, int8_t* codes,
+                                   float* scales, int32_t* pooled, hipStream_t s);
+
 hipError_t launch_select(const qsa_dims& d, const int32_t* pooled_q, const float* scale_q,
                          const int32_t* pooled_k, const float* scale_k, int32_t topk,
                          const Band& band, int32_t kmax, int32_t* kept_idx, int32_t* kept_cnt,

@@ -12,6 +12,17 @@
 // the round-half-even of an IEEE fp32 division x / scale.  The library is
 // compiled with correctly rounded fp32 division, no fast-math and no FP
 // contraction in this file, and fp32 denormals preserved.
+//
+// Rotated variant (Hadamard rotation of the activations before quantisation,
+// DVD-Quant gist.science/es/paper/2505.18663, technical summary §2B: it
+// spreads extreme channels over all channels): every token row x becomes
+// y = x H_D with H_D the Sylvester Hadamard matrix (entries +-1, unscaled),
+// computed in fp32 by the fast Walsh-Hadamard transform in a fixed order:
+// stages h = 1, 2, 4, ..., D/2, each replacing every pair (j, j+h) of a
+// 2h-aligned group by (v_j + v_{j+h}, v_j - v_{j+h}); then y is quantised as
+// above.  Since H_D H_D^T = D I, (q H)(k H)^T = D (q k^T): attention on
+// rotated codes uses sm_scale / D.  A lane holds 8 consecutive channels, so
+// stages h < 8 run in registers and h >= 8 exchange with the lane h/8 away.
 #include "qsa_internal.h"
 
 #pragma clang fp contract(off)
@@ -33,7 +44,32 @@ __device__ __forceinline__ int code_of(float x, float s) {
   return (int)q;
 }
 
-template <int BS, int D>
+// In-place fast Walsh-Hadamard transform of one token row held 8 channels
+// per lane by CPR consecutive lanes (lane l holds channels 8 (l % CPR) + e).
+template <int CPR>
+__device__ __forceinline__ void fwht_row(float (&v)[8], int lane) {
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      if (e & h) continue;
+      const float a = v[e], b = v[e + h];
+      v[e] = a + b;
+      v[e + h] = a - b;
+    }
+  }
+#pragma unroll
+  for (int m = 1; m < CPR; m <<= 1) {  // h = 8 m: the partner lane is lane ^ m
+    const bool upper = (lane & m) != 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float o = __shfl_xor(v[e], m, 64);
+      v[e] = upper ? o - v[e] : v[e] + o;  // lower: v_j + v_{j+h}; upper: v_j - v_{j+h}
+    }
+  }
+}
+
+template <int BS, int D, bool ROT>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x,
                                                        int8_t* __restrict__ codes,
                                                        float* __restrict__ scales,
@@ -59,22 +95,22 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   const uint16_t* xb = x + (bh * (uint64_t)L + (uint64_t)t0) * D + cc * 8;
   int8_t* cb = codes + (bh * (uint64_t)L + (uint64_t)t0) * D + cc * 8;
 
-  uint4 raw[PASSES];
+  float y[PASSES][8];
   float amax = 0.0f;
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int row = r0 + p * RPP;
-    if (row < n) {
-      raw[p] = *reinterpret_cast<const uint4*>(xb + (size_t)row * D);
-    } else {
-      raw[p] = make_uint4(0, 0, 0, 0);
-    }
-    const uint32_t w[4] = {raw[p].x, raw[p].y, raw[p].z, raw[p].w};
+    uint4 raw = make_uint4(0, 0, 0, 0);
+    if (row < n) raw = *reinterpret_cast<const uint4*>(xb + (size_t)row * D);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      amax = fmaxf(amax, fabsf(bf16_lo(w[e])));
-      amax = fmaxf(amax, fabsf(bf16_hi(w[e])));
+      y[p][2 * e] = bf16_lo(w[e]);
+      y[p][2 * e + 1] = bf16_hi(w[e]);
     }
+    if (ROT) fwht_row<CPR>(y[p], lane);  // rows past the end are zero: they stay zero
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[p][e]));
   }
   amax = wave_max(amax);
   if (lane == 0) s_amax[wave] = amax;
@@ -90,13 +126,9 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   for (int p = 0; p < PASSES; ++p) {
     const int row = r0 + p * RPP;
     if (row < n) {
-      const uint32_t w[4] = {raw[p].x, raw[p].y, raw[p].z, raw[p].w};
       int c[8];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        c[2 * e] = s > 0.0f ? code_of(bf16_lo(w[e]), s) : 0;
-        c[2 * e + 1] = s > 0.0f ? code_of(bf16_hi(w[e]), s) : 0;
-      }
+      for (int e = 0; e < 8; ++e) c[e] = s > 0.0f ? code_of(y[p][e], s) : 0;
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -127,24 +159,38 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   if (tid == 0) scales[blk] = s;
 }
 
-template <int BS, int D>
+template <int BS, int D, bool ROT>
 hipError_t launch_t(const qsa_dims& d, const uint16_t* x, int8_t* codes, float* scales,
                     int32_t* pooled, hipStream_t s) {
   const int nb = (d.seq_len + BS - 1) / BS;
   const uint64_t n_wg = (uint64_t)d.batch * d.heads * nb;
-  hipLaunchKernelGGL((quantize_kernel<BS, D>), dim3((uint32_t)n_wg), dim3(256), 0, s, x, codes,
-                     scales, pooled, d.seq_len, nb);
+  hipLaunchKernelGGL((quantize_kernel<BS, D, ROT>), dim3((uint32_t)n_wg), dim3(256), 0, s, x,
+                     codes, scales, pooled, d.seq_len, nb);
   return hipGetLastError();
+}
+
+template <bool ROT>
+hipError_t dispatch(const qsa_dims& d, const uint16_t* x, int8_t* codes, float* scales,
+                    int32_t* pooled, hipStream_t s) {
+  if (d.block == 64 && d.head_dim == 128)
+    return launch_t<64, 128, ROT>(d, x, codes, scales, pooled, s);
+  if (d.block == 64 && d.head_dim == 64)
+    return launch_t<64, 64, ROT>(d, x, codes, scales, pooled, s);
+  if (d.block == 128 && d.head_dim == 128)
+    return launch_t<128, 128, ROT>(d, x, codes, scales, pooled, s);
+  return launch_t<128, 64, ROT>(d, x, codes, scales, pooled, s);
 }
 
 }  // namespace
 
 hipError_t launch_quantize(const qsa_dims& d, const uint16_t* x, int8_t* codes, float* scales,
                            int32_t* pooled, hipStream_t s) {
-  if (d.block == 64 && d.head_dim == 128) return launch_t<64, 128>(d, x, codes, scales, pooled, s);
-  if (d.block == 64 && d.head_dim == 64) return launch_t<64, 64>(d, x, codes, scales, pooled, s);
-  if (d.block == 128 && d.head_dim == 128) return launch_t<128, 128>(d, x, codes, scales, pooled, s);
-  return launch_t<128, 64>(d, x, codes, scales, pooled, s);
+  return dispatch<false>(d, x, codes, scales, pooled, s);
+}
+
+hipError_t launch_quantize_rotated(const qsa_dims& d, const uint16_t* x, int8_t* codes,
+                                   float* scales, int32_t* pooled, hipStream_t s) {
+  return dispatch<true>(d, x, codes, scales, pooled, s);
 }
 
 }  // namespace qsa

@@ -25,6 +25,10 @@ class QSAConfig:
     # process the query blocks of sparse steps in an order that groups blocks
     # with overlapping kept sets (same outputs, more shared key-tile loads)
     reorder: bool = True
+    # quantise Hadamard-rotated Q and K rows (DVD-Quant,
+    # gist.science/es/paper/2505.18663, technical summary §2B); attention then
+    # runs with sm_scale / head_dim
+    rotate: bool = False
 
 
 @dataclass
@@ -61,10 +65,18 @@ class QuantSparseAttention:
     def load_state_dict(self, sd):
         self.r, self.dr, self.has_prev = sd["r"], sd["dr"], bool(sd["has_prev"])
 
+    def _sm_scale(self, head_dim: int):
+        c = self.cfg
+        if not c.rotate:
+            return c.sm_scale
+        sm = B.default_sm_scale(head_dim) if c.sm_scale is None else float(c.sm_scale)
+        return sm / head_dim  # exact: head_dim is a power of two
+
     def _front(self, q, k):
         c = self.cfg
-        qc, qs, qp = B.qsa_quantize(q, c.block)
-        kc, ks, kp = B.qsa_quantize(k, c.block)
+        quant = B.qsa_quantize_rotated if c.rotate else B.qsa_quantize
+        qc, qs, qp = quant(q, c.block)
+        kc, ks, kp = quant(k, c.block)
         idx, cnt = B.qsa_select_blocks(qp, qs, kp, ks, q.shape[2], c.block, c.topk, c.band)
         self.last = StepBuffers(qc, qs, qp, kc, ks, kp, idx, cnt)
         return qc, qs, kc, ks, idx, cnt
@@ -72,12 +84,13 @@ class QuantSparseAttention:
     def step(self, q, k, v, refresh: bool) -> torch.Tensor:
         c = self.cfg
         qc, qs, kc, ks, idx, cnt = self._front(q, k)
+        sm = self._sm_scale(q.shape[3])
         if refresh:
             if self.r is None:
                 self.r = torch.zeros_like(v)
                 self.dr = torch.zeros_like(v)
             out = B.qsa_full_attn_residual(qc, qs, kc, ks, v, idx, cnt, c.block, self.r, self.dr,
-                                           self.has_prev, c.sm_scale)
+                                           self.has_prev, sm)
             self.has_prev = True
             return out
         if self.r is None:
@@ -86,6 +99,6 @@ class QuantSparseAttention:
         if c.reorder:
             order = B.qsa_order_query_blocks(idx, cnt, q.shape[2], c.block, q.shape[3])
             return B.qsa_sparse_attn_ordered(qc, qs, kc, ks, v, idx, cnt, order, c.block,
-                                             c.sm_scale, r=self.r, dr=dr)
-        return B.qsa_sparse_attn(qc, qs, kc, ks, v, idx, cnt, c.block, c.sm_scale, r=self.r,
+                                             sm, r=self.r, dr=dr)
+        return B.qsa_sparse_attn(qc, qs, kc, ks, v, idx, cnt, c.block, sm, r=self.r,
                                  dr=dr)

@@ -56,6 +56,7 @@ def run(request):
     order = B.qsa_order_query_blocks(idx, cnt, w.seq_len, w.block, w.head_dim)
     step_o = B.qsa_sparse_attn_ordered(qc, qs, kc, ks, x["v"], idx, cnt, order, w.block, r=r,
                                        dr=dr)
+    rot = [*B.qsa_quantize_rotated(x["q"], w.block), *B.qsa_quantize_rotated(x["k"], w.block)]
     torch.cuda.synchronize()
     srt, _ = torch.sort(order.long(), dim=-1)
     order_ok = bool((srt == torch.arange(w.n_blocks, device=dev)).all())
@@ -77,13 +78,17 @@ def run(request):
         "finite": all(bool(torch.isfinite(t.float()).all()) for t in (sparse, full, r, step)),
         "idx_all": idx, "cnt_all": cnt,
         "order_ok": order_ok, "ordered_same": ordered_same,
+        "rot": [t[:, heads].cpu().numpy() for t in rot],
     }
+    del rot
     # the oracle's front end on the head subset
     oqc, osq, opq = oracle.quantize(host["q"], w.block)
     okc, osk, opk = oracle.quantize(host["k"], w.block)
     sc = oracle.block_scores(opq, osq, opk, osk, w.seq_len, w.block)
     oidx, ocnt = oracle.select_blocks(sc, w.topk, w.band, w.kmax)
-    o = dict(qc=oqc, sq=osq, pq=opq, kc=okc, sk=osk, pk=opk, idx=oidx, cnt=ocnt)
+    o = dict(qc=oqc, sq=osq, pq=opq, kc=okc, sk=osk, pk=opk, idx=oidx, cnt=ocnt,
+             rot=[*oracle.quantize_rotated(host["q"], w.block),
+                  *oracle.quantize_rotated(host["k"], w.block)])
     del x, qc, kc, qp, kp, sparse, full, r, dr, step
     yield w, heads, host, g, o
     torch.cuda.empty_cache()
@@ -117,6 +122,13 @@ def test_fullsize_front_end_bit_exact(run):
     assert np.array_equal(g["qp"], o["pq"]) and np.array_equal(g["kp"], o["pk"]), "pooled"
     assert np.array_equal(g["cnt"], o["cnt"]), "kept counts"
     assert np.array_equal(g["idx"], o["idx"]), "kept lists"
+
+
+def test_fullsize_rotated_quantize_bit_exact(run):
+    w, heads, host, g, o = run
+    for name, got, want in zip(("q codes", "q scales", "q pooled", "k codes", "k scales",
+                                "k pooled"), g["rot"], o["rot"]):
+        assert np.array_equal(got, want), name
 
 
 def test_fullsize_kept_lists_valid_on_every_head(run):

@@ -145,20 +145,33 @@ def test_refresh_sparse_part_matches_sparse_kernel(name):
     assert rel_l2(recon, host_f64(full)) < 4e-3
 
 
-@pytest.mark.parametrize("schedule", ["FSS", "FSFS", "FSSFSS"])
-@pytest.mark.parametrize("order", [2, 1])
-def test_schedule_against_oracle_state_machine(schedule, order):
+def _rotated_front(x, w, topk, band):
+    qc, sq, pq = oracle.quantize_rotated(x["q"], w.block)
+    kc, sk, pk = oracle.quantize_rotated(x["k"], w.block)
+    sc = oracle.block_scores(pq, sq, pk, sk, w.seq_len, w.block)
+    idx, cnt = oracle.select_blocks(sc, topk, band, min(w.n_blocks, topk + len(band)))
+    return dict(qc=qc, sq=sq, kc=kc, sk=sk, idx=idx, cnt=cnt)
+
+
+@pytest.mark.parametrize("schedule,order,rotate",
+                         [(s, o, False) for s in ("FSS", "FSFS", "FSSFSS") for o in (2, 1)]
+                         + [("FSFS", 2, True)])
+def test_schedule_against_oracle_state_machine(schedule, order, rotate):
     from quantized_sparse_attention_amd import QSAConfig, QuantSparseAttention
     w = TINY.with_(grid=(2, 8, 24), head_dim=64)  # 384 tokens, 6 blocks
     topk, band = 2, (0,)
     steps = qsa_gen.make_qkv_steps(w, len(schedule))
-    layer = QuantSparseAttention(QSAConfig(block=w.block, topk=topk, band=band, order=order))
+    layer = QuantSparseAttention(QSAConfig(block=w.block, topk=topk, band=band, order=order,
+                                           rotate=rotate))
     st = oracle.ResidualState(steps[0]["v"].shape)
     sm = oracle.default_sm_scale(w.head_dim)
+    if rotate:
+        sm = np.float32(sm / np.float32(w.head_dim))
     for s, kind in enumerate(schedule):
         x = steps[s]
         out = layer.step(dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"]), kind == "F")
-        o = oracle_front(x, w, topk=topk, band=band)
+        o = (_rotated_front(x, w, topk, band) if rotate
+             else oracle_front(x, w, topk=topk, band=band))
         o_sp = oracle.attention(o["qc"], o["sq"], o["kc"], o["sk"], x["v"], o["idx"], o["cnt"],
                                 w.block, sm)
         if kind == "F":
@@ -435,3 +448,43 @@ def test_order_chunks(nb):
     a = B.qsa_sparse_attn(qc, qs, kc, ks, v, idx, cnt, blk)
     b = B.qsa_sparse_attn_ordered(qc, qs, kc, ks, v, idx, cnt, order, blk)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("name", list(CFGS))
+def test_rotated_quantize_bit_exact(name):
+    w, _ = CFGS[name]
+    x = qsa_gen.make_qkv(w, 0)
+    for t in ("q", "k"):
+        c, s, p = B.qsa_quantize_rotated(dev_bf16(x[t]), w.block)
+        oc, os_, op = oracle.quantize_rotated(x[t], w.block)
+        assert np.array_equal(c.cpu().numpy(), oc), t
+        assert np.array_equal(s.cpu().numpy().view(np.uint32), os_.view(np.uint32)), t
+        assert np.array_equal(p.cpu().numpy(), op), t
+
+
+@pytest.mark.parametrize("name", ["tiny", "tail64_d128", "tail128_d128", "d64_b128",
+                                  "batch2_h3"])
+def test_rotated_pipeline_parity(name):
+    """Rotated codes through selection and sparse attention with sm_scale / D:
+    kept lists bit-exact, outputs within the output tolerance."""
+    w, kw = CFGS[name]
+    x = qsa_gen.make_qkv(w, 0)
+    topk = kw.get("topk", w.topk)
+    band = tuple(kw.get("band", w.band))
+    kmax = min(w.n_blocks, topk + len(band))
+    qc, sq, pq = oracle.quantize_rotated(x["q"], w.block)
+    kc, sk, pk = oracle.quantize_rotated(x["k"], w.block)
+    idx, cnt = oracle.select_blocks(oracle.block_scores(pq, sq, pk, sk, w.seq_len, w.block),
+                                    topk, band, kmax)
+    sm = np.float32(oracle.default_sm_scale(w.head_dim) / np.float32(w.head_dim))
+    want = oracle.attention(qc, sq, kc, sk, x["v"], idx, cnt, w.block, sm)
+
+    gq = B.qsa_quantize_rotated(dev_bf16(x["q"]), w.block)
+    gk = B.qsa_quantize_rotated(dev_bf16(x["k"]), w.block)
+    gidx, gcnt = B.qsa_select_blocks(gq[2], gq[1], gk[2], gk[1], w.seq_len, w.block, topk, band,
+                                     kmax)
+    assert np.array_equal(gcnt.cpu().numpy(), cnt)
+    assert np.array_equal(gidx.cpu().numpy(), idx)
+    out = B.qsa_sparse_attn(gq[0], gq[1], gk[0], gk[1], dev_bf16(x["v"]), gidx, gcnt, w.block,
+                            sm_scale=float(sm))
+    assert_close(host_f64(out), want, what=f"{name} rotated sparse")

@@ -12,6 +12,7 @@ from oracle import qsa_oracle as Q
 from tests import test_oracle_attention as TA
 from tests import test_oracle_quantize as TQ
 from tests import test_oracle_residual as TR
+from tests import test_oracle_rotation as TH
 from tests import test_oracle_select as TS
 
 
@@ -63,6 +64,37 @@ def _refresh_flipped(state, o_full, o_sparse):
     return ORIG_REFRESH(state, o_sparse, o_full)
 
 
+def _fwht_swapped_sign(x):
+    # pairs become (a + b, b - a): H with its lower-right blocks negated twice over
+    y = np.array(x, dtype=np.float32, copy=True)
+    D = y.shape[-1]
+    h = 1
+    while h < D:
+        g = y.reshape(y.shape[:-1] + (D // (2 * h), 2, h))
+        a, b = g[..., 0, :].copy(), g[..., 1, :].copy()
+        g[..., 0, :], g[..., 1, :] = a + b, b - a
+        y = g.reshape(y.shape)
+        h *= 2
+    return y
+
+
+def _fwht_last_stage_dropped(x):
+    y = np.array(x, dtype=np.float32, copy=True)
+    D = y.shape[-1]
+    h = 1
+    while h < D // 2:
+        g = y.reshape(y.shape[:-1] + (D // (2 * h), 2, h))
+        a, b = g[..., 0, :].copy(), g[..., 1, :].copy()
+        g[..., 0, :], g[..., 1, :] = a + b, a - b
+        y = g.reshape(y.shape)
+        h *= 2
+    return y
+
+
+def _quantize_rotated_unrotated(x_bits, block):
+    return ORIG_QUANTIZE(x_bits, block)
+
+
 ORIG_QUANTIZE = Q.quantize
 ORIG_SCORES = Q.block_scores
 ORIG_SELECT = Q.select_blocks
@@ -78,6 +110,11 @@ CASES = [
      lambda: TA.test_sparse_attention_equals_masked_sdpa((1, 10, 30), 64, 64, 2, (0,))),
     ("attention", _attention_transposed_v, lambda: TA.test_hand_examples_outputs("H2_band0")),
     ("refresh_step", _refresh_flipped, lambda: TR.test_refresh_and_sparse_step_hand_values()),
+    ("fwht", _fwht_swapped_sign, lambda: TH.test_fwht_equals_sylvester_product_exactly(8)),
+    ("fwht", _fwht_last_stage_dropped, lambda: TH.test_fwht_algebra(64)),
+    ("fwht", _fwht_last_stage_dropped, lambda: TH.test_rotated_quantisation_of_exactly_rotatable_rows()),
+    ("quantize_rotated", _quantize_rotated_unrotated,
+     lambda: TH.test_rotated_quantisation_of_exactly_rotatable_rows()),
 ]
 
 
