@@ -40,8 +40,14 @@ R7  SSAR ([QS-es] §2B, [QS-ko] §2.2): the first-order residual is the
     refresh step; the second-order residual is the change of that residual
     between consecutive refresh steps (0 at the first refresh); sparse steps
     output sparse + r + dr.  Both residuals are stored in bf16.
-R8  the SVD projection of the second-order residual ([QS-es] §2B) is not
-    part of this path.
+R8  SVD projection of the second-order residual ([QS-es] §2B, [QS-ko]
+    §2.2: the residual is projected onto its dominant principal components,
+    with no storage beyond the residual cache).  When a rank r is given, at
+    every refresh step the second-order residual of each (batch, head), a
+    [L, D] tokens-by-channels matrix X, is replaced by its best rank-r
+    approximation X V_r V_r^T, V_r the r right singular vectors of largest
+    singular value (the top-r eigenvectors of X^T X), in the same bf16
+    cache.  The pages give no rank; without one nothing is projected.
 R9  rotated quantisation (DVD-Quant, gist.science/es/paper/2505.18663,
     technical summary §2B: a Hadamard rotation spreads extreme channels
     before quantisation, with scales computed online): every Q and K row x
@@ -62,6 +68,7 @@ __all__ = [
     "quantize",
     "fwht",
     "quantize_rotated",
+    "project_residual",
     "block_scores",
     "select_blocks",
     "attention",
@@ -316,15 +323,45 @@ class ResidualState:
         self.has_prev = False
 
 
-def refresh_step(state: ResidualState, o_full, o_sparse):
-    """Full-attention refresh step (R7).
+def project_residual(dr_bits, rank: int):
+    """Best rank-``rank`` approximation of every (b, h) slice of the bf16
+    second-order residual [B, H, L, D] (R8), in fp64.
+
+    X = dr[b, h] ([L, D]); G = X^T X; V_r = the eigenvectors of G of the
+    ``rank`` largest eigenvalues (the right singular vectors of X of largest
+    singular value); result X V_r V_r^T.  Returns (projected [B, H, L, D]
+    fp64, eigenvalues [B, H, rank] descending).  The projection is unique
+    when the rank-th and next eigenvalues differ.
+    """
+    x = bf16_to_f64(dr_bits)
+    B, H, L, D = x.shape
+    if not 1 <= rank <= D:
+        raise ValueError("rank must be in [1, D]")
+    out = np.empty_like(x)
+    vals = np.empty((B, H, rank), dtype=np.float64)
+    for b in range(B):
+        for h in range(H):
+            X = x[b, h]
+            w, V = np.linalg.eigh(X.T @ X)
+            top = np.argsort(-w, kind="stable")[:rank]
+            Vr = V[:, top]
+            out[b, h] = (X @ Vr) @ Vr.T
+            vals[b, h] = w[top]
+    return out, vals
+
+
+def refresh_step(state: ResidualState, o_full, o_sparse, rank: int | None = None):
+    """Full-attention refresh step (R7, and R8 when ``rank`` is given).
 
     rho = O_full - O_sparse (fp64); dr = bf16(rho - r_prev) if a previous
-    refresh exists, else 0; r = bf16(rho).  Returns O_full.
+    refresh exists, else 0; with a rank, dr = bf16(rank-r projection of dr);
+    r = bf16(rho).  Returns O_full.
     """
     rho = np.asarray(o_full, np.float64) - np.asarray(o_sparse, np.float64)
     if state.has_prev:
         state.dr = f64_to_bf16(rho - bf16_to_f64(state.r))
+        if rank is not None:
+            state.dr = f64_to_bf16(project_residual(state.dr, rank)[0])
     else:
         state.dr = np.zeros(rho.shape, dtype=np.uint16)
     state.r = f64_to_bf16(rho)

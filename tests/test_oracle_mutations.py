@@ -13,6 +13,7 @@ from tests import test_oracle_attention as TA
 from tests import test_oracle_quantize as TQ
 from tests import test_oracle_residual as TR
 from tests import test_oracle_rotation as TH
+from tests import test_oracle_projection as TP
 from tests import test_oracle_select as TS
 
 
@@ -95,6 +96,30 @@ def _quantize_rotated_unrotated(x_bits, block):
     return ORIG_QUANTIZE(x_bits, block)
 
 
+def _project_with(pick, scale_basis=False):
+    def bad(dr_bits, rank):
+        x = Q.bf16_to_f64(dr_bits)
+        out = np.empty_like(x)
+        vals = np.empty(x.shape[:2] + (rank,))
+        for b in range(x.shape[0]):
+            for h in range(x.shape[1]):
+                w, V = np.linalg.eigh(x[b, h].T @ x[b, h])
+                top = pick(w)[:rank]
+                Vr = V[:, top] * (np.sqrt(np.maximum(w[top], 0)) if scale_basis else 1.0)
+                out[b, h] = (x[b, h] @ Vr) @ Vr.T
+                vals[b, h] = w[top]
+        return out, vals
+    return bad
+
+
+_project_smallest = _project_with(lambda w: np.argsort(w, kind="stable"))
+_project_unnormalised = _project_with(lambda w: np.argsort(-w, kind="stable"), scale_basis=True)
+
+
+def _refresh_unprojected(state, o_full, o_sparse, rank=None):
+    return ORIG_REFRESH(state, o_full, o_sparse)
+
+
 ORIG_QUANTIZE = Q.quantize
 ORIG_SCORES = Q.block_scores
 ORIG_SELECT = Q.select_blocks
@@ -115,6 +140,14 @@ CASES = [
     ("fwht", _fwht_last_stage_dropped, lambda: TH.test_rotated_quantisation_of_exactly_rotatable_rows()),
     ("quantize_rotated", _quantize_rotated_unrotated,
      lambda: TH.test_rotated_quantisation_of_exactly_rotatable_rows()),
+    ("project_residual", _project_smallest, lambda: TP.test_hand_example_rank_one()),
+    ("project_residual", _project_smallest,
+     lambda: TP.test_projection_equals_truncated_svd(200, 64, 8)),
+    ("project_residual", _project_unnormalised, lambda: TP.test_hand_example_axis_aligned()),
+    ("project_residual", _project_unnormalised,
+     lambda: TP.test_eckart_young_energy_and_orthogonality()),
+    ("refresh_step", _refresh_unprojected,
+     lambda: TP.test_refresh_step_projects_only_the_second_order_residual()),
 ]
 
 
