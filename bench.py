@@ -49,6 +49,8 @@ def parse():
                    help="approximate CPU time budget of the oracle baseline sample")
     p.add_argument("--rotate", action="store_true",
                    help="quantise Hadamard-rotated Q/K rows (attention with sm_scale / D)")
+    p.add_argument("--rank", type=int, default=None,
+                   help="project the second-order residual to this rank at refresh steps")
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="before the run, copy a bf16 buffer of this many MiB once with a "
                         "plain elementwise kernel (reads and writes each byte once): the "
@@ -190,6 +192,10 @@ def main():
     r = torch.zeros((B, H, L, D), dtype=torch.bfloat16, device=dev)
     dr = torch.zeros_like(r)
     state = {"has_prev": False}
+    if args.rank is not None:
+        proj_work = mk((Bn.qsa_project_work_bytes(B, H, L, D, args.rank),), torch.uint8)
+        proj_basis = mk((B, H, D, args.rank), torch.float32)
+        proj_vals = mk((B, H, args.rank), torch.float32)
     stream = torch.cuda.current_stream()
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -200,7 +206,8 @@ def main():
     def layer_step(s, kind, rec):
         x = inputs[s]
         idx, cnt = kept[s]
-        e = [ev() for _ in range(5)]
+        e = [ev() for _ in range(6)]
+        projected = False
         e[0].record(stream)
         quant(x["q"], bs, qc, qs, qp)
         quant(x["k"], bs, kc, ks, kp)
@@ -210,8 +217,12 @@ def main():
         if kind == "F":
             Bn.qsa_full_attn_residual(qc, qs, kc, ks, x["v"], idx, cnt, bs, r, dr,
                                       state["has_prev"], sm, out_full=out)
-            state["has_prev"] = True
             e[4].record(stream)
+            projected = args.rank is not None and state["has_prev"]
+            if projected:
+                Bn.qsa_project_residual(dr, args.rank, proj_basis, proj_vals, proj_work)
+            e[5].record(stream)
+            state["has_prev"] = True
         else:
             Bn.qsa_order_query_blocks(idx, cnt, L, bs, D, order)
             e[4].record(stream)
@@ -219,7 +230,7 @@ def main():
                                        dr=dr, out=out)
         e[3].record(stream)
         if rec is not None:
-            rec.append((kind, s, e))
+            rec.append((kind, s, e, projected))
 
     for _ in range(args.warmup):
         for s, kind in enumerate(schedule):
@@ -240,14 +251,17 @@ def main():
         return sum(xs) / len(xs) if xs else float("nan")
 
     t_quant, t_sel, t_sparse, t_full, t_order, step_sp, step_f = [], [], [], [], [], [], []
-    for kind, s, e in recs:
+    t_proj = []
+    for kind, s, e, projected in recs:
         t_quant.append(e[0].elapsed_time(e[1]))
         t_sel.append(e[1].elapsed_time(e[2]))
         if kind == "S":
             t_order.append(e[2].elapsed_time(e[4]))
             t_sparse.append(e[4].elapsed_time(e[3]))  # the attention launch alone
         else:
-            t_full.append(e[2].elapsed_time(e[3]))
+            t_full.append(e[2].elapsed_time(e[4]))
+            if projected:
+                t_proj.append(e[4].elapsed_time(e[5]))
         (step_sp if kind == "S" else step_f).append(e[0].elapsed_time(e[3]))
 
     # kept-tile work of the sparse steps (exact, from this run's kept lists)
@@ -288,6 +302,7 @@ def main():
                    "block": bs, "topk": w.topk, "band": list(w.band),
                    "density_kept": round(density, 4), "schedule": schedule,
                    "rotated_quantisation": bool(args.rotate),
+                   "residual_rank": args.rank,
                    "step": "one denoising cycle (%s) of one attention layer" % schedule},
         "effective_tops": round(achieved / 1e12, 1),
         "pct_mfma_peak": round(100 * tmin / t_attn, 1) if t_attn > 0 else None,
@@ -300,6 +315,7 @@ def main():
             "qsa_order_query_blocks": round(mean(t_order), 4),
             "qsa_sparse_attn_ordered": round(mean(t_sparse), 4),
             "qsa_full_attn_residual": round(mean(t_full), 4),
+            **({"qsa_project_residual": round(mean(t_proj), 4)} if t_proj else {}),
         },
         "roofline": {
             "kernel": "qsa_sparse_attn_ordered",

@@ -20,8 +20,9 @@
  *     patterns.  nb = ceil(seq_len / block) token blocks per (batch, head);
  *     the last block is shorter when block does not divide seq_len.
  *   - Every tensor pointer must be 16-byte aligned (QSA_ERR_ALIGN).
- *   - The caller owns all memory.  The library allocates nothing, keeps no
- *     state between calls and needs no workspace; calls are re-entrant.
+ *   - The caller owns all memory.  The library allocates nothing and keeps no
+ *     state between calls; calls are re-entrant.  Only qsa_project_residual
+ *     needs scratch memory, which its caller passes in (qsa_project_work_bytes).
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and runs asynchronously.  Argument errors are detected on the host
  *     before anything is enqueued; device faults surface at the caller's next
@@ -66,6 +67,8 @@ typedef struct qsa_dims {
 #define QSA_MAX_BLOCKS 16384
 /* Largest number of band offsets. */
 #define QSA_MAX_BAND 8
+/* Largest rank of qsa_project_residual. */
+#define QSA_MAX_RANK 64
 
 /*
  * qsa_quantize -- per-block symmetric int8 quantisation of Q or K with pooled
@@ -239,6 +242,42 @@ int qsa_full_attn_residual(const qsa_dims* dims, const int8_t* q_codes, const fl
  */
 int qsa_apply_residual(const qsa_dims* dims, const uint16_t* sparse_out, const uint16_t* r,
                        const uint16_t* dr, uint16_t* out, void* stream);
+
+/*
+ * qsa_project_residual -- rank-r projection of the second-order residual onto
+ * its dominant principal components, in place (technical summary §2B: an SVD
+ * projects the second-order residual onto its dominant, temporally stable
+ * components; Korean summary §2.2: with no storage beyond the residual
+ * cache).  Normally called right after a refresh step (qsa_full_attn_residual
+ * with has_prev = 1) on its dr output.
+ *
+ * For every (b, h) slice X = dr[b,h] ([L, D], tokens by channels):
+ *   G        = X^T X, bf16 products summed in fp32 over token chunks, the
+ *              chunk sums added in a fixed order (deterministic)
+ *   V, lam   = eigenvectors and eigenvalues of G by cyclic Jacobi rotations
+ *              in fp32, until every off-diagonal entry is <= 2^-22 ||G||_F
+ *              (at most 16 sweeps)
+ *   V_r      = the eigenvectors of the `rank` largest eigenvalues (ties to the
+ *              lower index), orthonormal columns
+ *   dr[b,h]  = bf16((X V_r) V_r^T), fp32 arithmetic
+ * The result is the best rank-r approximation of X (Eckart-Young); it is
+ * unique when the rank-th and next eigenvalues differ.
+ *
+ *   dr       in/out: bf16 [B,H,L,D]
+ *   rank         in: 1 <= rank <= min(D, QSA_MAX_RANK)
+ *   basis       out: fp32 [B,H,D,rank], column k = the k-th eigenvector
+ *   eigvals     out: fp32 [B,H,rank], descending
+ *   work     in/out: device scratch of at least qsa_project_work_bytes(dims, rank)
+ *                    bytes; contents undefined on return
+ *   work_bytes   in: its size
+ * QSA_ERR_PARAM if rank is out of range or work_bytes too small.
+ * QSA_ERR_SHAPE if B*H > 65535.  dr, basis, eigvals and work must not overlap.
+ */
+int qsa_project_residual(const qsa_dims* dims, uint16_t* dr, int32_t rank, float* basis,
+                         float* eigvals, void* work, uint64_t work_bytes, void* stream);
+
+/* Bytes of scratch qsa_project_residual needs (0 for invalid dims or rank). */
+uint64_t qsa_project_work_bytes(const qsa_dims* dims, int32_t rank);
 
 /* Static text of a status code. */
 const char* qsa_status_string(int status);

@@ -27,10 +27,11 @@ QSA_ERR_DEVICE = -5
 QSA_ERR_LAUNCH = -6
 QSA_MAX_BAND = 8
 QSA_MAX_BLOCKS = 16384
+QSA_MAX_RANK = 64
 
 EXPORTED = ("qsa_quantize", "qsa_select_blocks", "qsa_sparse_attn", "qsa_full_attn_residual",
             "qsa_apply_residual", "qsa_order_query_blocks", "qsa_sparse_attn_ordered",
-            "qsa_quantize_rotated",
+            "qsa_quantize_rotated", "qsa_project_residual", "qsa_project_work_bytes",
             "qsa_status_string", "qsa_last_error_detail", "qsa_version")
 
 
@@ -72,8 +73,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.qsa_order_query_blocks.argtypes = [pd, vp, vp, i32, vp, vp]
     lib.qsa_sparse_attn_ordered.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, i32, vp, f32, vp, vp,
                                             vp, vp]
-    for f in ("qsa_quantize", "qsa_quantize_rotated", "qsa_select_blocks", "qsa_sparse_attn", "qsa_full_attn_residual",
-              "qsa_apply_residual", "qsa_order_query_blocks", "qsa_sparse_attn_ordered"):
+    lib.qsa_project_residual.argtypes = [pd, vp, i32, vp, vp, vp, ctypes.c_uint64, vp]
+    lib.qsa_project_work_bytes.argtypes = [pd, i32]
+    lib.qsa_project_work_bytes.restype = ctypes.c_uint64
+    for f in ("qsa_quantize", "qsa_quantize_rotated", "qsa_select_blocks", "qsa_sparse_attn",
+              "qsa_full_attn_residual", "qsa_apply_residual", "qsa_order_query_blocks",
+              "qsa_sparse_attn_ordered", "qsa_project_residual"):
         getattr(lib, f).restype = ctypes.c_int
     lib.qsa_status_string.argtypes = [ctypes.c_int]
     lib.qsa_status_string.restype = ctypes.c_char_p
@@ -294,3 +299,34 @@ def qsa_apply_residual(sparse_out, r, dr=None, out=None, block: int = 64, stream
     _check(load_library().qsa_apply_residual(ctypes.byref(d), _ptr(sparse_out), _ptr(r), _ptr(dr),
                                              _ptr(out), _stream(stream)))
     return out
+
+
+def qsa_project_work_bytes(B: int, H: int, L: int, D: int, rank: int) -> int:
+    """Scratch bytes qsa_project_residual needs (0 for invalid sizes)."""
+    d = make_dims(B, H, L, D, 64)
+    return int(load_library().qsa_project_work_bytes(ctypes.byref(d), int(rank)))
+
+
+def qsa_project_residual(dr: torch.Tensor, rank: int, basis=None, eigvals=None, work=None,
+                         stream=None):
+    """Rank-``rank`` projection of the bf16 second-order residual dr [B,H,L,D]
+    onto its dominant principal components, in place.  Returns (basis fp32
+    [B,H,D,rank], eigvals fp32 [B,H,rank] descending)."""
+    _need(dr, "dr", torch.bfloat16)
+    B, H, L, D = dr.shape
+    dev = dr.device
+    basis = (torch.empty((B, H, D, rank), dtype=torch.float32, device=dev) if basis is None
+             else basis)
+    eigvals = (torch.empty((B, H, rank), dtype=torch.float32, device=dev) if eigvals is None
+               else eigvals)
+    _need(basis, "basis", torch.float32, (B, H, D, rank))
+    _need(eigvals, "eigvals", torch.float32, (B, H, rank))
+    need = qsa_project_work_bytes(B, H, L, D, rank)
+    if work is None:
+        work = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _need(work, "work", torch.uint8)
+    d = make_dims(B, H, L, D, 64)
+    _check(load_library().qsa_project_residual(ctypes.byref(d), _ptr(dr), int(rank), _ptr(basis),
+                                               _ptr(eigvals), _ptr(work),
+                                               ctypes.c_uint64(work.numel()), _stream(stream)))
+    return basis, eigvals

@@ -1,0 +1,404 @@
+// Rank-r projection of the second-order residual onto its dominant principal
+// components.
+//
+// QuantSparse (gist.science/es/paper/2509.23681, technical summary §2B;
+// gist.science/ko/paper/2509.23681, §2.2): the second-order residual is
+// projected by an SVD onto its dominant, temporally stable components, with
+// no storage beyond the residual cache.  For every (batch, head) slice
+// X [L, D] of the bf16 residual the result is X V_r V_r^T, V_r the r
+// eigenvectors of largest eigenvalue of the Gram matrix G = X^T X (the right
+// singular vectors of X of largest singular value), written back in place.
+//
+// Three kernels:
+//  1. gram_kernel: partial Gram matrices over token chunks with the bf16
+//     MFMA (v_mfma_f32_32x32x16_bf16; bf16 products are exact in fp32, sums
+//     in fp32).  The X tile sits row-major in LDS; the transposing LDS read
+//     ds_read_b64_tr_b16 yields, per lane, 8 tokens of one channel -- the
+//     A operand for a 32-channel row tile of G and, unchanged, the B operand
+//     for a 32-channel column tile (both use the same token order).
+//  2. jacobi_kernel: one workgroup per slice sums the partials in a fixed
+//     order (deterministic), then diagonalises G by the cyclic Jacobi method
+//     (Golub and Van Loan, Matrix Computations, §8.5: symmetric Schur
+//     rotations; parallel round-robin ordering, D/2 disjoint rotations per
+//     round, D-1 rounds per sweep) in fp32 with G and the eigenvector matrix
+//     in LDS.  Eigenvalues are ranked descending (ties: lower index).
+//  3. project_kernel: one lane per token row: c = x V_r, then x V_r V_r^T in
+//     fp32, rounded to bf16 in place.
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxSweeps = 16;
+
+// ---------------------------------------------------------------------------
+// 1. partial Gram matrices
+// ---------------------------------------------------------------------------
+
+// Chunk swizzle of the row-major bf16 X tile (16-byte chunks): the transposing
+// read touches 4 consecutive rows x 4 consecutive chunks per 32 lanes; XOR-ing
+// the chunk quad with the row spreads them over distinct banks.
+template <int D>
+__device__ __forceinline__ int xswz(int r) {
+  return D == 128 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void gram_kernel(const uint16_t* __restrict__ x,
+                                                        float* __restrict__ partial, int L,
+                                                        int chunk) {
+  constexpr int DT = D / 32;          // 32-channel tiles
+  constexpr int CPR = D / 8;          // 16-byte chunks per row
+  constexpr int ROWS = 64;            // tokens per LDS tile
+  constexpr int NLD = ROWS * CPR / kThreads;
+  constexpr int TPW = DT * DT / 4;    // output tiles per wave
+  static_assert(NLD >= 1 && TPW >= 1, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[ROWS * D];
+
+  const int s = blockIdx.x, S = gridDim.x;
+  const uint64_t bh = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int t_begin = s * chunk, t_end = min(L, t_begin + chunk);
+  const uint16_t* xb = x + bh * (uint64_t)L * D;
+
+  // output tiles of this wave: row tile ti, column tiles tj0 + u (D = 128:
+  // one row of 4 tiles; D = 64: one tile)
+  const int ti = (wave * TPW) / DT, tj0 = (wave * TPW) % DT;
+  v16f acc[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[u][r] = 0.0f;
+
+  // per-lane byte offsets of the transposing reads (see the operand layout
+  // above): 16-lane group G, lane j in it; out lane l then holds tokens
+  // {4g + e, 8 + 4g + e : e < 4} (g = l / 32) of channel 32 dt + l % 32
+  const int G = lane >> 4, j = lane & 15;
+  const int r0 = 4 * (G >> 1) + (j >> 2);
+  auto lane_off = [&](int dt) {
+    const int c = 4 * dt + 2 * (G & 1) + ((j & 3) >> 1);
+    return r0 * (2 * D) + ((c ^ xswz<D>(r0)) << 4) + 8 * (j & 1);
+  };
+  const int off_a = lane_off(ti);
+  int off_b[TPW];
+#pragma unroll
+  for (int u = 0; u < TPW; ++u) off_b[u] = lane_off(tj0 + u);
+  auto operand = [&](int st, int off) {
+    const char* base = reinterpret_cast<const char*>(s_x) + 16 * st * (2 * D) + off;
+    const v4s lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(base));
+    const v4s hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t*)(base + 8 * (2 * D)));
+    const uint2 ul = __builtin_bit_cast(uint2, lo4), uh = __builtin_bit_cast(uint2, hi4);
+    return __builtin_bit_cast(v8bf, make_uint4(ul.x, ul.y, uh.x, uh.y));
+  };
+
+  uint4 nxt[NLD];
+  auto load = [&](int t0) {
+#pragma unroll
+    for (int n = 0; n < NLD; ++n) {
+      const int q = tid + kThreads * n;
+      const int row = q / CPR, c = q % CPR;
+      const int t = t0 + row;
+      nxt[n] = t < t_end ? *reinterpret_cast<const uint4*>(xb + (size_t)t * D + c * 8)
+                         : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int n = 0; n < NLD; ++n) {
+      const int q = tid + kThreads * n;
+      const int row = q / CPR, c = q % CPR;
+      *reinterpret_cast<uint4*>(reinterpret_cast<char*>(s_x) + row * (2 * D) +
+                                ((c ^ xswz<D>(row)) << 4)) = nxt[n];
+    }
+  };
+
+  if (t_begin < t_end) load(t_begin);
+  for (int t0 = t_begin; t0 < t_end; t0 += ROWS) {
+    __syncthreads();  // the previous tile's reads are done
+    store();
+    __syncthreads();
+    if (t0 + ROWS < t_end) load(t0 + ROWS);  // in flight during the MFMAs
+#pragma unroll
+    for (int st = 0; st < ROWS / 16; ++st) {
+      const v8bf a_op = operand(st, off_a);
+#pragma unroll
+      for (int u = 0; u < TPW; ++u)
+        acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_op, operand(st, off_b[u]), acc[u],
+                                                         0, 0, 0);
+    }
+  }
+
+  // accumulator element r of lane l is G[32 ti + 8 (r/4) + 4 (l/32) + r%4][32 tj + l%32]
+  float* pb = partial + (bh * (uint64_t)S + s) * (uint64_t)(D * D);
+#pragma unroll
+  for (int u = 0; u < TPW; ++u)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int m = 32 * ti + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      const int n = 32 * (tj0 + u) + (lane & 31);
+      pb[m * D + n] = acc[u][r];
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 2. cyclic Jacobi eigensolver, one workgroup per slice
+// ---------------------------------------------------------------------------
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void jacobi_kernel(const float* __restrict__ partial,
+                                                          int S, int rank, int rp,
+                                                          float* __restrict__ eigvals,
+                                                          float* __restrict__ basis,
+                                                          float* __restrict__ wbasis) {
+  constexpr int LD = D + 1;  // padded rows: column walks hit distinct banks
+  constexpr int NP = D / 2;  // disjoint rotations per round
+  __shared__ float a[D * LD];
+  __shared__ float v[D * LD];
+  __shared__ float rc[NP], rs[NP];
+  __shared__ int rp_[NP], rq_[NP];
+  __shared__ float red[kThreads / 64];
+  __shared__ int done;
+
+  const uint64_t bh = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  // G = sum of the partials in chunk order; upper triangle mirrored
+  const float* pb = partial + bh * (uint64_t)S * (D * D);
+  float fro = 0.0f;
+  for (int e = tid; e < D * D; e += kThreads) {
+    const int i = e / D, k = e % D;
+    if (k < i) continue;
+    float g = 0.0f;
+    for (int s = 0; s < S; ++s) g += pb[(size_t)s * (D * D) + e];
+    a[i * LD + k] = g;
+    a[k * LD + i] = g;
+    fro += (i == k ? 1.0f : 2.0f) * g * g;
+    v[i * LD + k] = i == k ? 1.0f : 0.0f;
+    v[k * LD + i] = i == k ? 1.0f : 0.0f;
+  }
+  for (int o = 32; o >= 1; o >>= 1) fro += __shfl_xor(fro, o, 64);
+  if (lane == 0) red[wave] = fro;
+  __syncthreads();
+  // rotations stop once every off-diagonal entry is below 2^-22 ||G||_F, a
+  // few fp32 roundings of the largest entries
+  const float tol = sqrtf(red[0] + red[1] + red[2] + red[3]) * 0x1p-22f;
+
+  for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
+    float big = 0.0f;  // largest |a_pq| met in this sweep (wave 0)
+    for (int t = 0; t < D - 1; ++t) {
+      if (tid < NP) {
+        int p, q;
+        if (tid == 0) {
+          p = t;
+          q = D - 1;
+        } else {
+          const int u = (t + tid) % (D - 1), w = (t - tid + (D - 1)) % (D - 1);
+          p = min(u, w);
+          q = max(u, w);
+        }
+        const float apq = a[p * LD + q];
+        big = fmaxf(big, fabsf(apq));
+        float c = 1.0f, sn = 0.0f;
+        if (fabsf(apq) > tol) {
+          // symmetric Schur rotation: J = [[c, s], [-s, c]] zeroes a_pq
+          const float tau = (a[q * LD + q] - a[p * LD + p]) / (2.0f * apq);
+          const float tt = (tau >= 0.0f ? 1.0f : -1.0f) /
+                           (fabsf(tau) + sqrtf(__builtin_fmaf(tau, tau, 1.0f)));
+          c = 1.0f / sqrtf(__builtin_fmaf(tt, tt, 1.0f));
+          sn = tt * c;
+        }
+        rp_[tid] = p;
+        rq_[tid] = q;
+        rc[tid] = c;
+        rs[tid] = sn;
+      }
+      __syncthreads();
+      // rows: A <- J^T A
+      for (int e = tid; e < NP * D; e += kThreads) {
+        const int k = e / D, col = e % D;
+        const float c = rc[k], sn = rs[k];
+        if (sn == 0.0f) continue;
+        const int p = rp_[k], q = rq_[k];
+        const float ap = a[p * LD + col], aq = a[q * LD + col];
+        a[p * LD + col] = c * ap - sn * aq;
+        a[q * LD + col] = sn * ap + c * aq;
+      }
+      __syncthreads();
+      // columns: A <- A J, V <- V J; the rotated pair's off-diagonal is 0
+      for (int e = tid; e < NP * D; e += kThreads) {
+        const int k = e / D, row = e % D;
+        const float c = rc[k], sn = rs[k];
+        if (sn == 0.0f) continue;
+        const int p = rp_[k], q = rq_[k];
+        const float ap = a[row * LD + p], aq = a[row * LD + q];
+        float np_ = c * ap - sn * aq, nq = sn * ap + c * aq;
+        if (row == p) nq = 0.0f;
+        if (row == q) np_ = 0.0f;
+        a[row * LD + p] = np_;
+        a[row * LD + q] = nq;
+        const float vp = v[row * LD + p], vq = v[row * LD + q];
+        v[row * LD + p] = c * vp - sn * vq;
+        v[row * LD + q] = sn * vp + c * vq;
+      }
+      __syncthreads();
+    }
+    if (wave == 0) {
+      for (int o = 32; o >= 1; o >>= 1) big = fmaxf(big, __shfl_xor(big, o, 64));
+      if (lane == 0) done = big <= tol;
+    }
+    __syncthreads();
+    const bool stop = done;
+    __syncthreads();  // every thread has read the flag before wave 0 rewrites it
+    if (stop) break;
+  }
+
+  // rank eigenvalues descending, ties to the lower index; write the top ones
+  for (int i = tid; i < D; i += kThreads) {
+    const float di = a[i * LD + i];
+    int rk = 0;
+    for (int k = 0; k < D; ++k) {
+      const float dk = a[k * LD + k];
+      rk += (dk > di) || (dk == di && k < i);
+    }
+    float* wb = wbasis + bh * (uint64_t)(D * rp);
+    if (rk < rank) {
+      eigvals[bh * (uint64_t)rank + rk] = di;
+      float* ub = basis + bh * (uint64_t)(D * rank);
+      for (int d = 0; d < D; ++d) {
+        ub[d * rank + rk] = v[d * LD + i];
+        wb[d * rp + rk] = v[d * LD + i];
+      }
+    } else if (rk < rp) {
+      for (int d = 0; d < D; ++d) wb[d * rp + rk] = 0.0f;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. projection of every row onto the kept directions, in place
+// ---------------------------------------------------------------------------
+
+template <int D, int RP>
+__global__ __launch_bounds__(kThreads) void project_kernel(uint16_t* __restrict__ x,
+                                                           const float* __restrict__ wbasis,
+                                                           int L) {
+  __shared__ __attribute__((aligned(16))) float s_b[D * RP];
+  const uint64_t bh = blockIdx.y;
+  const int tid = threadIdx.x;
+  const float* wb = wbasis + bh * (uint64_t)(D * RP);
+  for (int e = tid * 4; e < D * RP; e += kThreads * 4)
+    *reinterpret_cast<float4*>(&s_b[e]) = *reinterpret_cast<const float4*>(&wb[e]);
+  __syncthreads();
+
+  const int row = blockIdx.x * kThreads + tid;
+  if (row >= L) return;
+  uint16_t* xr = x + (bh * (uint64_t)L + row) * D;
+
+  float c[RP];
+#pragma unroll
+  for (int k = 0; k < RP; ++k) c[k] = 0.0f;
+#pragma unroll 1
+  for (int d0 = 0; d0 < D; d0 += 8) {
+    const uint4 raw = *reinterpret_cast<const uint4*>(xr + d0);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float xe = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+      const float4* brow = reinterpret_cast<const float4*>(&s_b[(d0 + e) * RP]);
+#pragma unroll
+      for (int k4 = 0; k4 < RP / 4; ++k4) {
+        const float4 b = brow[k4];
+        c[4 * k4 + 0] = __builtin_fmaf(xe, b.x, c[4 * k4 + 0]);
+        c[4 * k4 + 1] = __builtin_fmaf(xe, b.y, c[4 * k4 + 1]);
+        c[4 * k4 + 2] = __builtin_fmaf(xe, b.z, c[4 * k4 + 2]);
+        c[4 * k4 + 3] = __builtin_fmaf(xe, b.w, c[4 * k4 + 3]);
+      }
+    }
+  }
+#pragma unroll 1
+  for (int d0 = 0; d0 < D; d0 += 8) {
+    float o[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float4* brow = reinterpret_cast<const float4*>(&s_b[(d0 + e) * RP]);
+      float acc = 0.0f;
+#pragma unroll
+      for (int k4 = 0; k4 < RP / 4; ++k4) {
+        const float4 b = brow[k4];
+        acc = __builtin_fmaf(c[4 * k4 + 0], b.x, acc);
+        acc = __builtin_fmaf(c[4 * k4 + 1], b.y, acc);
+        acc = __builtin_fmaf(c[4 * k4 + 2], b.z, acc);
+        acc = __builtin_fmaf(c[4 * k4 + 3], b.w, acc);
+      }
+      o[e] = acc;
+    }
+    *reinterpret_cast<uint4*>(xr + d0) =
+        make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
+                   pack_bf16x2(o[6], o[7]));
+  }
+}
+
+template <int D>
+hipError_t launch_d(const qsa_dims& d, uint16_t* dr, int rank, float* basis, float* eigvals,
+                    float* partial, float* wbasis, hipStream_t st) {
+  const ProjectPlan pl = project_plan(d, rank);
+  const uint32_t bh = (uint32_t)(d.batch * d.heads);
+  hipLaunchKernelGGL((gram_kernel<D>), dim3((uint32_t)pl.chunks, bh), dim3(kThreads), 0, st, dr,
+                     partial, d.seq_len, pl.chunk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((jacobi_kernel<D>), dim3(bh), dim3(kThreads), 0, st, partial, pl.chunks,
+                     rank, pl.rank_pad, eigvals, basis, wbasis);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const dim3 grid((uint32_t)((d.seq_len + kThreads - 1) / kThreads), bh);
+  switch (pl.rank_pad) {
+    case 8:
+      hipLaunchKernelGGL((project_kernel<D, 8>), grid, dim3(kThreads), 0, st, dr, wbasis,
+                         d.seq_len);
+      break;
+    case 16:
+      hipLaunchKernelGGL((project_kernel<D, 16>), grid, dim3(kThreads), 0, st, dr, wbasis,
+                         d.seq_len);
+      break;
+    case 32:
+      hipLaunchKernelGGL((project_kernel<D, 32>), grid, dim3(kThreads), 0, st, dr, wbasis,
+                         d.seq_len);
+      break;
+    default:
+      hipLaunchKernelGGL((project_kernel<D, 64>), grid, dim3(kThreads), 0, st, dr, wbasis,
+                         d.seq_len);
+      break;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+ProjectPlan project_plan(const qsa_dims& d, int rank) {
+  ProjectPlan p;
+  const int64_t L = d.seq_len;
+  int chunks = (int)((L + 2047) / 2048);
+  chunks = chunks < 1 ? 1 : (chunks > 32 ? 32 : chunks);
+  int64_t chunk = (L + chunks - 1) / chunks;
+  chunk = (chunk + 63) / 64 * 64;
+  p.chunk = (int)chunk;
+  p.chunks = (int)((L + chunk - 1) / chunk);
+  if (p.chunks < 1) p.chunks = 1;
+  p.rank_pad = rank <= 8 ? 8 : rank <= 16 ? 16 : rank <= 32 ? 32 : 64;
+  const uint64_t bh = (uint64_t)d.batch * d.heads;
+  p.partial_floats = bh * p.chunks * (uint64_t)d.head_dim * d.head_dim;
+  p.wbasis_floats = bh * (uint64_t)d.head_dim * QSA_MAX_RANK;
+  return p;
+}
+
+hipError_t launch_project_residual(const qsa_dims& d, uint16_t* dr, int rank, float* basis,
+                                   float* eigvals, float* work, hipStream_t s) {
+  const ProjectPlan pl = project_plan(d, rank);
+  float* partial = work;
+  float* wbasis = work + pl.partial_floats;
+  if (d.head_dim == 128) return launch_d<128>(d, dr, rank, basis, eigvals, partial, wbasis, s);
+  return launch_d<64>(d, dr, rank, basis, eigvals, partial, wbasis, s);
+}
+
+}  // namespace qsa

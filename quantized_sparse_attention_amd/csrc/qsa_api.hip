@@ -336,4 +336,37 @@ int qsa_apply_residual(const qsa_dims* dims, const uint16_t* sparse_out, const u
                                                  static_cast<hipStream_t>(stream)));
 }
 
+uint64_t qsa_project_work_bytes(const qsa_dims* dims, int32_t rank) {
+  if (check_dims("qsa_project_work_bytes", dims) != QSA_OK) return 0;
+  if (rank < 1 || rank > dims->head_dim || rank > QSA_MAX_RANK) return 0;
+  const qsa::ProjectPlan p = qsa::project_plan(*dims, rank);
+  return (p.partial_floats + p.wbasis_floats) * sizeof(float);
+}
+
+int qsa_project_residual(const qsa_dims* dims, uint16_t* dr, int32_t rank, float* basis,
+                         float* eigvals, void* work, uint64_t work_bytes, void* stream) {
+  const char* fn = "qsa_project_residual";
+  int st = check_dims(fn, dims);
+  if (st) return st;
+  REQUIRE_PTR(dr);
+  REQUIRE_PTR(basis);
+  REQUIRE_PTR(eigvals);
+  REQUIRE_PTR(work);
+  if (rank < 1 || rank > dims->head_dim || rank > QSA_MAX_RANK)
+    return fail(QSA_ERR_PARAM, "%s: rank=%d must be in [1, min(D=%d, %d)]", fn, rank,
+                dims->head_dim, QSA_MAX_RANK);
+  if ((int64_t)dims->batch * dims->heads > 65535)
+    return fail(QSA_ERR_SHAPE, "%s: batch*heads=%lld exceeds 65535", fn,
+                (long long)dims->batch * dims->heads);
+  const uint64_t need = qsa_project_work_bytes(dims, rank);
+  if (work_bytes < need)
+    return fail(QSA_ERR_PARAM, "%s: work_bytes=%llu is less than the %llu needed", fn,
+                (unsigned long long)work_bytes, (unsigned long long)need);
+  if ((st = check_device(fn))) return st;
+  (void)hipGetLastError();
+  return launched(fn, qsa::launch_project_residual(*dims, dr, rank, basis, eigvals,
+                                                   static_cast<float*>(work),
+                                                   static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

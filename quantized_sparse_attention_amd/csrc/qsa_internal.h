@@ -90,6 +90,21 @@ hipError_t launch_full_attn_residual(const qsa_dims& d, const AttnArgs& a, hipSt
 hipError_t launch_order(const qsa_dims& d, const int32_t* kept_idx, const int32_t* kept_cnt,
                         int32_t kmax, int32_t* order, hipStream_t s);
 
+// Chunking of qsa_project_residual's Gram matrices and its scratch layout:
+// partial Gram matrices fp32 [B*H][chunks][D][D], then the zero-padded
+// working basis fp32 [B*H][D][rank_pad] (room for QSA_MAX_RANK columns).
+struct ProjectPlan {
+  int chunk;      // tokens per chunk, a multiple of 64
+  int chunks;     // chunks per (b, h)
+  int rank_pad;   // rank rounded up to 8, 16, 32 or 64
+  uint64_t partial_floats;
+  uint64_t wbasis_floats;
+};
+ProjectPlan project_plan(const qsa_dims& d, int rank);
+
+hipError_t launch_project_residual(const qsa_dims& d, uint16_t* dr, int rank, float* basis,
+                                   float* eigvals, float* work, hipStream_t s);
+
 hipError_t launch_apply_residual(const qsa_dims& d, const uint16_t* sparse_out,
                                  const uint16_t* r, const uint16_t* dr, uint16_t* out,
                                  hipStream_t s);

@@ -29,6 +29,9 @@ class QSAConfig:
     # gist.science/es/paper/2505.18663, technical summary §2B); attention then
     # runs with sm_scale / head_dim
     rotate: bool = False
+    # rank of the SVD projection of the second-order residual at refresh steps
+    # (technical summary §2B); None keeps the full residual
+    rank: int | None = None
 
 
 @dataclass
@@ -54,6 +57,9 @@ class QuantSparseAttention:
         self.dr = None
         self.has_prev = False
         self.last = StepBuffers()
+        self.work = None      # scratch of the residual projection
+        self.basis = None     # its last basis [B,H,D,rank] and eigenvalues
+        self.eigvals = None
 
     def reset(self):
         self.r = self.dr = None
@@ -91,6 +97,12 @@ class QuantSparseAttention:
                 self.dr = torch.zeros_like(v)
             out = B.qsa_full_attn_residual(qc, qs, kc, ks, v, idx, cnt, c.block, self.r, self.dr,
                                            self.has_prev, sm)
+            if c.rank is not None and self.has_prev:
+                Bn, H, L, D = v.shape
+                need = B.qsa_project_work_bytes(Bn, H, L, D, c.rank)
+                if self.work is None or self.work.numel() < need:
+                    self.work = torch.empty(need, dtype=torch.uint8, device=v.device)
+                self.basis, self.eigvals = B.qsa_project_residual(self.dr, c.rank, work=self.work)
             self.has_prev = True
             return out
         if self.r is None:

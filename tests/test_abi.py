@@ -169,3 +169,32 @@ def test_binding_refuses_cpu_tensors():
         B.qsa_quantize(x, 64)
     with pytest.raises(TypeError):
         B.qsa_quantize(x.float(), 64)
+
+
+def test_project_residual_validation(lib):
+    u64 = ctypes.c_uint64
+    need = lib.qsa_project_work_bytes(_d(L=1000, D=128), 32)
+    # partial Gram matrices (2 heads x 1 chunk of 1000 tokens x 128 x 128) + padded basis
+    assert need == 4 * (2 * 1 * 128 * 128 + 2 * 128 * B.QSA_MAX_RANK)
+    assert lib.qsa_project_work_bytes(_d(D=64), 65) == 0
+    assert lib.qsa_project_work_bytes(_d(D=64), 0) == 0
+    assert lib.qsa_project_work_bytes(None, 4) == 0
+
+    def pr(rank=8, dims=None, ptrs=None, wb=None):
+        p = ptrs or P[:4]
+        dd = dims or _d()
+        w = lib.qsa_project_work_bytes(dd, max(1, min(rank, 64))) if wb is None else wb
+        return lib.qsa_project_residual(dd, p[0], rank, p[1], p[2], p[3], u64(w), None)
+
+    assert pr(rank=0) == B.QSA_ERR_PARAM
+    assert pr(rank=65, dims=_d(D=128)) == B.QSA_ERR_PARAM
+    assert pr(rank=65, dims=_d(D=64)) == B.QSA_ERR_PARAM
+    assert pr(wb=16) == B.QSA_ERR_PARAM
+    assert b"work_bytes" in lib.qsa_last_error_detail()
+    assert pr(ptrs=[None] + P[1:4]) == B.QSA_ERR_NULL
+    assert pr(ptrs=P[:3] + [None]) == B.QSA_ERR_NULL
+    assert pr(ptrs=P[:1] + [ctypes.c_void_p(0x1004)] + P[2:4]) == B.QSA_ERR_ALIGN
+    assert pr(dims=_d(B_=300, H=300)) == B.QSA_ERR_SHAPE
+    assert pr(dims=_d(D=96)) == B.QSA_ERR_SHAPE
+    if NO_GPU:
+        assert pr() == B.QSA_ERR_DEVICE
