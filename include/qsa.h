@@ -22,7 +22,7 @@
  *   - Every tensor pointer must be 16-byte aligned (QSA_ERR_ALIGN).
  *   - The caller owns all memory.  The library allocates nothing and keeps no
  *     state between calls; calls are re-entrant.  Only qsa_project_residual
- *     needs scratch memory, which its caller passes in (qsa_project_work_bytes).
+ *     and qsa_l1_change need scratch memory, which their caller passes in.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and runs asynchronously.  Argument errors are detected on the host
  *     before anything is enqueued; device faults surface at the caller's next
@@ -69,6 +69,8 @@ typedef struct qsa_dims {
 #define QSA_MAX_BAND 8
 /* Largest rank of qsa_project_residual. */
 #define QSA_MAX_RANK 64
+/* Scratch bytes of qsa_l1_change. */
+#define QSA_L1_WORK_BYTES 16384
 
 /*
  * qsa_quantize -- per-block symmetric int8 quantisation of Q or K with pooled
@@ -278,6 +280,26 @@ int qsa_project_residual(const qsa_dims* dims, uint16_t* dr, int32_t rank, float
 
 /* Bytes of scratch qsa_project_residual needs (0 for invalid dims or rank). */
 uint64_t qsa_project_work_bytes(const qsa_dims* dims, int32_t rank);
+
+/*
+ * qsa_l1_change -- the two sums of the normalised L1 change between a layer's
+ * consecutive outputs, for an adaptive refresh trigger (DVD-Quant,
+ * gist.science/es/paper/2505.18663, technical summary §2C: the normalised L1
+ * distance between consecutive output features accumulates against a
+ * threshold; here it decides when the next step recomputes full attention):
+ *   sums[0] = sum |cur - prev|,  sums[1] = sum |prev|
+ * over all B*H*L*D elements.  Each term is formed in fp64 from the bf16
+ * values and the terms are summed in fp64 in a fixed order (deterministic;
+ * within ~2e-13 relative of an exactly rounded sum at 4e8 elements).  The
+ * caller forms d = sums[0] / sums[1] and accumulates it.
+ *
+ *   prev, cur in: bf16 [B,H,L,D]
+ *   sums     out: DEVICE fp64 [2]
+ *   work  in/out: device scratch of at least QSA_L1_WORK_BYTES bytes
+ * QSA_ERR_PARAM if work_bytes < QSA_L1_WORK_BYTES.
+ */
+int qsa_l1_change(const qsa_dims* dims, const uint16_t* prev, const uint16_t* cur, double* sums,
+                  void* work, uint64_t work_bytes, void* stream);
 
 /* Static text of a status code. */
 const char* qsa_status_string(int status);

@@ -55,6 +55,15 @@ R9  rotated quantisation (DVD-Quant, gist.science/es/paper/2505.18663,
     in fp32 by the fast Walsh-Hadamard transform with stages h = 1, 2, ...,
     D/2; y is then quantised by R1/R2 (the per-block scale is the online
     scale).  H_D H_D^T = D I, so attention on rotated codes uses sm_scale/D.
+R10 adaptive refresh (DVD-Quant, gist.science/es/paper/2505.18663,
+    technical summary §2C: the normalised L1 distance between consecutive
+    output features accumulates; once it passes a threshold delta the
+    expensive mode is used and the count restarts), read as a refresh
+    trigger: after every step t >= 1 of a layer, d_t = sum|O_t - O_{t-1}| /
+    sum|O_{t-1}| over all elements of the layer's bf16 attention outputs
+    (fp64); c += d_t; if c > delta the next step is a refresh step and c
+    restarts at 0.  The first step is a refresh step (no cache yet).  A zero
+    denominator gives d = 0 when the outputs agree, else +inf.
 """
 from __future__ import annotations
 
@@ -69,6 +78,8 @@ __all__ = [
     "fwht",
     "quantize_rotated",
     "project_residual",
+    "l1_change",
+    "RefreshTrigger",
     "block_scores",
     "select_blocks",
     "attention",
@@ -377,3 +388,41 @@ def sparse_step(state: ResidualState, o_sparse, order: int = 2):
     if order == 2:
         out = out + bf16_to_f64(state.dr)
     return out
+
+
+# ---------------------------------------------------------------------------
+# adaptive refresh trigger (R10)
+# ---------------------------------------------------------------------------
+
+def l1_change(prev_bits, cur_bits):
+    """(sum |cur - prev|, sum |prev|) over all elements of two bf16 tensors, fp64."""
+    p = bf16_to_f64(prev_bits)
+    c = bf16_to_f64(cur_bits)
+    return float(np.abs(c - p).sum()), float(np.abs(p).sum())
+
+
+class RefreshTrigger:
+    """Cumulative normalised-L1 refresh trigger of one layer (R10)."""
+
+    def __init__(self, delta: float):
+        self.delta = float(delta)
+        self.c = 0.0
+        self.refresh_next = True  # the first step fills the residual cache
+
+    def update(self, num: float | None = None, den: float | None = None) -> bool:
+        """Account the step just computed, given its (sum|O_t - O_{t-1}|,
+        sum|O_{t-1}|), or no sums for the layer's first step (no previous
+        output: the next step is sparse).  Returns whether the next step is a
+        refresh step."""
+        if num is None:
+            self.refresh_next = False
+            return False
+        if den > 0:
+            d = num / den
+        else:
+            d = 0.0 if num == 0 else float("inf")
+        self.c += d
+        self.refresh_next = self.c > self.delta
+        if self.refresh_next:
+            self.c = 0.0
+        return self.refresh_next

@@ -28,10 +28,12 @@ QSA_ERR_LAUNCH = -6
 QSA_MAX_BAND = 8
 QSA_MAX_BLOCKS = 16384
 QSA_MAX_RANK = 64
+QSA_L1_WORK_BYTES = 16384
 
 EXPORTED = ("qsa_quantize", "qsa_select_blocks", "qsa_sparse_attn", "qsa_full_attn_residual",
             "qsa_apply_residual", "qsa_order_query_blocks", "qsa_sparse_attn_ordered",
             "qsa_quantize_rotated", "qsa_project_residual", "qsa_project_work_bytes",
+            "qsa_l1_change",
             "qsa_status_string", "qsa_last_error_detail", "qsa_version")
 
 
@@ -74,11 +76,12 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.qsa_sparse_attn_ordered.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, i32, vp, f32, vp, vp,
                                             vp, vp]
     lib.qsa_project_residual.argtypes = [pd, vp, i32, vp, vp, vp, ctypes.c_uint64, vp]
+    lib.qsa_l1_change.argtypes = [pd, vp, vp, vp, vp, ctypes.c_uint64, vp]
     lib.qsa_project_work_bytes.argtypes = [pd, i32]
     lib.qsa_project_work_bytes.restype = ctypes.c_uint64
     for f in ("qsa_quantize", "qsa_quantize_rotated", "qsa_select_blocks", "qsa_sparse_attn",
               "qsa_full_attn_residual", "qsa_apply_residual", "qsa_order_query_blocks",
-              "qsa_sparse_attn_ordered", "qsa_project_residual"):
+              "qsa_sparse_attn_ordered", "qsa_project_residual", "qsa_l1_change"):
         getattr(lib, f).restype = ctypes.c_int
     lib.qsa_status_string.argtypes = [ctypes.c_int]
     lib.qsa_status_string.restype = ctypes.c_char_p
@@ -330,3 +333,20 @@ def qsa_project_residual(dr: torch.Tensor, rank: int, basis=None, eigvals=None, 
                                                _ptr(eigvals), _ptr(work),
                                                ctypes.c_uint64(work.numel()), _stream(stream)))
     return basis, eigvals
+
+
+def qsa_l1_change(prev: torch.Tensor, cur: torch.Tensor, sums=None, work=None, stream=None):
+    """Device fp64 [2]: (sum |cur - prev|, sum |prev|) of two bf16 [B,H,L,D] tensors."""
+    _need(prev, "prev", torch.bfloat16)
+    _need(cur, "cur", torch.bfloat16, tuple(prev.shape))
+    Bn, H, L, D = prev.shape
+    dev = prev.device
+    sums = torch.empty(2, dtype=torch.float64, device=dev) if sums is None else sums
+    work = torch.empty(QSA_L1_WORK_BYTES, dtype=torch.uint8, device=dev) if work is None else work
+    _need(sums, "sums", torch.float64, (2,))
+    _need(work, "work", torch.uint8)
+    d = make_dims(Bn, H, L, D, 64)
+    _check(load_library().qsa_l1_change(ctypes.byref(d), _ptr(prev), _ptr(cur), _ptr(sums),
+                                        _ptr(work), ctypes.c_uint64(work.numel()),
+                                        _stream(stream)))
+    return sums

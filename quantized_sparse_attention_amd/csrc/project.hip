@@ -16,12 +16,14 @@
 //     ds_read_b64_tr_b16 yields, per lane, 8 tokens of one channel -- the
 //     A operand for a 32-channel row tile of G and, unchanged, the B operand
 //     for a 32-channel column tile (both use the same token order).
-//  2. jacobi_kernel: one workgroup per slice sums the partials in a fixed
-//     order (deterministic), then diagonalises G by the cyclic Jacobi method
-//     (Golub and Van Loan, Matrix Computations, §8.5: symmetric Schur
-//     rotations; parallel round-robin ordering, D/2 disjoint rotations per
-//     round, D-1 rounds per sweep) in fp32 with G and the eigenvector matrix
-//     in LDS.  Eigenvalues are ranked descending (ties: lower index).
+//  2. jacobi_kernel: one 1024-thread workgroup per slice sums the partials
+//     in a fixed order (deterministic), then diagonalises G by the cyclic
+//     Jacobi method (Golub and Van Loan, Matrix Computations, §8.5:
+//     symmetric Schur rotations; parallel round-robin ordering, D/2 disjoint
+//     rotations per round, D-1 rounds per sweep) in fp32 with G and the
+//     eigenvector matrix in LDS.  Each thread issues all LDS reads of its
+//     items before any write, so LDS latency overlaps across items.
+//     Eigenvalues are ranked descending (ties: lower index).
 //  3. project_kernel: one lane per token row: c = x V_r, then x V_r V_r^T in
 //     fp32, rounded to bf16 in place.
 #include "qsa_internal.h"
@@ -30,6 +32,7 @@ namespace qsa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kJacobiThreads = 1024;
 constexpr int kMaxSweeps = 16;
 
 // ---------------------------------------------------------------------------
@@ -145,19 +148,26 @@ __global__ __launch_bounds__(kThreads) void gram_kernel(const uint16_t* __restri
 // 2. cyclic Jacobi eigensolver, one workgroup per slice
 // ---------------------------------------------------------------------------
 
+// One rotation of a round: rows/columns p < q, J = [[c, s], [-s, c]].
+struct Rot {
+  float c, s;
+  int p, q;
+};
+
 template <int D>
-__global__ __launch_bounds__(kThreads) void jacobi_kernel(const float* __restrict__ partial,
-                                                          int S, int rank, int rp,
-                                                          float* __restrict__ eigvals,
-                                                          float* __restrict__ basis,
-                                                          float* __restrict__ wbasis) {
-  constexpr int LD = D + 1;  // padded rows: column walks hit distinct banks
-  constexpr int NP = D / 2;  // disjoint rotations per round
+__global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(
+    const float* __restrict__ partial, int S, int rank, int rp, float* __restrict__ eigvals,
+    float* __restrict__ basis, float* __restrict__ wbasis) {
+  constexpr int T = kJacobiThreads;
+  constexpr int LD = D + 1;        // padded rows: column walks hit distinct banks
+  constexpr int NP = D / 2;        // disjoint rotations per round
+  constexpr int IT = NP * D / T;   // (pair, row-or-column) items per thread
+  constexpr int KS = T / D;        // pair stride between a thread's items
+  static_assert(IT * T == NP * D && KS * D == T, "item split");
   __shared__ float a[D * LD];
   __shared__ float v[D * LD];
-  __shared__ float rc[NP], rs[NP];
-  __shared__ int rp_[NP], rq_[NP];
-  __shared__ float red[kThreads / 64];
+  __shared__ Rot rot[NP];
+  __shared__ float red[T / 64];
   __shared__ int done;
 
   const uint64_t bh = blockIdx.x;
@@ -166,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void jacobi_kernel(const float* __restric
   // G = sum of the partials in chunk order; upper triangle mirrored
   const float* pb = partial + bh * (uint64_t)S * (D * D);
   float fro = 0.0f;
-  for (int e = tid; e < D * D; e += kThreads) {
+  for (int e = tid; e < D * D; e += T) {
     const int i = e / D, k = e % D;
     if (k < i) continue;
     float g = 0.0f;
@@ -180,12 +190,18 @@ __global__ __launch_bounds__(kThreads) void jacobi_kernel(const float* __restric
   for (int o = 32; o >= 1; o >>= 1) fro += __shfl_xor(fro, o, 64);
   if (lane == 0) red[wave] = fro;
   __syncthreads();
+  float tot = 0.0f;
+#pragma unroll
+  for (int w = 0; w < T / 64; ++w) tot += red[w];
   // rotations stop once every off-diagonal entry is below 2^-22 ||G||_F, a
   // few fp32 roundings of the largest entries
-  const float tol = sqrtf(red[0] + red[1] + red[2] + red[3]) * 0x1p-22f;
+  const float tol = sqrtf(tot) * 0x1p-22f;
+
+  // this thread's items: pair k = k0 + KS n, row or column index = idx
+  const int k0 = tid / D, idx = tid % D;
 
   for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
-    float big = 0.0f;  // largest |a_pq| met in this sweep (wave 0)
+    float big = 0.0f;  // largest |a_pq| met in this sweep (threads < NP)
     for (int t = 0; t < D - 1; ++t) {
       if (tid < NP) {
         int p, q;
@@ -208,38 +224,50 @@ __global__ __launch_bounds__(kThreads) void jacobi_kernel(const float* __restric
           c = 1.0f / sqrtf(__builtin_fmaf(tt, tt, 1.0f));
           sn = tt * c;
         }
-        rp_[tid] = p;
-        rq_[tid] = q;
-        rc[tid] = c;
-        rs[tid] = sn;
+        rot[tid] = Rot{c, sn, p, q};
       }
       __syncthreads();
-      // rows: A <- J^T A
-      for (int e = tid; e < NP * D; e += kThreads) {
-        const int k = e / D, col = e % D;
-        const float c = rc[k], sn = rs[k];
-        if (sn == 0.0f) continue;
-        const int p = rp_[k], q = rq_[k];
-        const float ap = a[p * LD + col], aq = a[q * LD + col];
-        a[p * LD + col] = c * ap - sn * aq;
-        a[q * LD + col] = sn * ap + c * aq;
+      Rot r[IT];
+#pragma unroll
+      for (int n = 0; n < IT; ++n) r[n] = rot[k0 + KS * n];
+      // rows: A <- J^T A (all reads of a pair's rows before its writes)
+      {
+        float ap[IT], aq[IT];
+#pragma unroll
+        for (int n = 0; n < IT; ++n) {
+          ap[n] = a[r[n].p * LD + idx];
+          aq[n] = a[r[n].q * LD + idx];
+        }
+#pragma unroll
+        for (int n = 0; n < IT; ++n) {
+          if (r[n].s == 0.0f) continue;
+          a[r[n].p * LD + idx] = r[n].c * ap[n] - r[n].s * aq[n];
+          a[r[n].q * LD + idx] = r[n].s * ap[n] + r[n].c * aq[n];
+        }
       }
       __syncthreads();
       // columns: A <- A J, V <- V J; the rotated pair's off-diagonal is 0
-      for (int e = tid; e < NP * D; e += kThreads) {
-        const int k = e / D, row = e % D;
-        const float c = rc[k], sn = rs[k];
-        if (sn == 0.0f) continue;
-        const int p = rp_[k], q = rq_[k];
-        const float ap = a[row * LD + p], aq = a[row * LD + q];
-        float np_ = c * ap - sn * aq, nq = sn * ap + c * aq;
-        if (row == p) nq = 0.0f;
-        if (row == q) np_ = 0.0f;
-        a[row * LD + p] = np_;
-        a[row * LD + q] = nq;
-        const float vp = v[row * LD + p], vq = v[row * LD + q];
-        v[row * LD + p] = c * vp - sn * vq;
-        v[row * LD + q] = sn * vp + c * vq;
+      {
+        float ap[IT], aq[IT], vp[IT], vq[IT];
+#pragma unroll
+        for (int n = 0; n < IT; ++n) {
+          ap[n] = a[idx * LD + r[n].p];
+          aq[n] = a[idx * LD + r[n].q];
+          vp[n] = v[idx * LD + r[n].p];
+          vq[n] = v[idx * LD + r[n].q];
+        }
+#pragma unroll
+        for (int n = 0; n < IT; ++n) {
+          if (r[n].s == 0.0f) continue;
+          const float c = r[n].c, sn = r[n].s;
+          float np_ = c * ap[n] - sn * aq[n], nq = sn * ap[n] + c * aq[n];
+          if (idx == r[n].p) nq = 0.0f;
+          if (idx == r[n].q) np_ = 0.0f;
+          a[idx * LD + r[n].p] = np_;
+          a[idx * LD + r[n].q] = nq;
+          v[idx * LD + r[n].p] = c * vp[n] - sn * vq[n];
+          v[idx * LD + r[n].q] = sn * vp[n] + c * vq[n];
+        }
       }
       __syncthreads();
     }
@@ -254,7 +282,7 @@ __global__ __launch_bounds__(kThreads) void jacobi_kernel(const float* __restric
   }
 
   // rank eigenvalues descending, ties to the lower index; write the top ones
-  for (int i = tid; i < D; i += kThreads) {
+  for (int i = tid; i < D; i += T) {
     const float di = a[i * LD + i];
     int rk = 0;
     for (int k = 0; k < D; ++k) {
@@ -348,7 +376,7 @@ hipError_t launch_d(const qsa_dims& d, uint16_t* dr, int rank, float* basis, flo
                      partial, d.seq_len, pl.chunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((jacobi_kernel<D>), dim3(bh), dim3(kThreads), 0, st, partial, pl.chunks,
+  hipLaunchKernelGGL((jacobi_kernel<D>), dim3(bh), dim3(kJacobiThreads), 0, st, partial, pl.chunks,
                      rank, pl.rank_pad, eigvals, basis, wbasis);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const dim3 grid((uint32_t)((d.seq_len + kThreads - 1) / kThreads), bh);

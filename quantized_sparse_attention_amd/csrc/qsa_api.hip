@@ -369,4 +369,23 @@ int qsa_project_residual(const qsa_dims* dims, uint16_t* dr, int32_t rank, float
                                                    static_cast<hipStream_t>(stream)));
 }
 
+int qsa_l1_change(const qsa_dims* dims, const uint16_t* prev, const uint16_t* cur, double* sums,
+                  void* work, uint64_t work_bytes, void* stream) {
+  const char* fn = "qsa_l1_change";
+  int st = check_dims(fn, dims);
+  if (st) return st;
+  REQUIRE_PTR(prev);
+  REQUIRE_PTR(cur);
+  REQUIRE_PTR(sums);
+  REQUIRE_PTR(work);
+  if (work_bytes < QSA_L1_WORK_BYTES)
+    return fail(QSA_ERR_PARAM, "%s: work_bytes=%llu is less than %d", fn,
+                (unsigned long long)work_bytes, QSA_L1_WORK_BYTES);
+  if ((st = check_device(fn))) return st;
+  const uint64_t n = (uint64_t)dims->batch * dims->heads * dims->seq_len * dims->head_dim;
+  (void)hipGetLastError();
+  return launched(fn, qsa::launch_l1_change(n, prev, cur, sums, static_cast<double*>(work),
+                                            static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

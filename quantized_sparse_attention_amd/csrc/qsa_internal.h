@@ -105,6 +105,12 @@ ProjectPlan project_plan(const qsa_dims& d, int rank);
 hipError_t launch_project_residual(const qsa_dims& d, uint16_t* dr, int rank, float* basis,
                                    float* eigvals, float* work, hipStream_t s);
 
+// qsa_l1_change: per-block partial sums (2 doubles per block) in the scratch
+constexpr int kL1MaxBlocks = QSA_L1_WORK_BYTES / 16;
+int l1_change_blocks(uint64_t n_elements);
+hipError_t launch_l1_change(uint64_t n_elements, const uint16_t* prev, const uint16_t* cur,
+                            double* sums, double* work, hipStream_t s);
+
 hipError_t launch_apply_residual(const qsa_dims& d, const uint16_t* sparse_out,
                                  const uint16_t* r, const uint16_t* dr, uint16_t* out,
                                  hipStream_t s);

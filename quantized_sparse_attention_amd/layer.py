@@ -32,6 +32,11 @@ class QSAConfig:
     # rank of the SVD projection of the second-order residual at refresh steps
     # (technical summary §2B); None keeps the full residual
     rank: int | None = None
+    # adaptive refresh: with a threshold, step(..., refresh=None) refreshes
+    # once the accumulated normalised L1 change of this layer's consecutive
+    # outputs passes it (DVD-Quant, gist.science/es/paper/2505.18663,
+    # technical summary §2C); None keeps caller-chosen refresh steps
+    adaptive_delta: float | None = None
 
 
 @dataclass
@@ -60,16 +65,31 @@ class QuantSparseAttention:
         self.work = None      # scratch of the residual projection
         self.basis = None     # its last basis [B,H,D,rank] and eigenvalues
         self.eigvals = None
+        # adaptive refresh trigger state
+        self.prev_out = None
+        self.change = 0.0       # accumulated normalised L1 change
+        self.refresh_next = True
+        self.last_sums = None   # (sum|O_t - O_t-1|, sum|O_t-1|) of the last step
+        self.l1_work = None
+        self.l1_sums = None
 
     def reset(self):
         self.r = self.dr = None
         self.has_prev = False
+        self.prev_out = None
+        self.change = 0.0
+        self.refresh_next = True
 
     def state_dict(self):
-        return {"r": self.r, "dr": self.dr, "has_prev": self.has_prev}
+        return {"r": self.r, "dr": self.dr, "has_prev": self.has_prev,
+                "prev_out": self.prev_out, "change": self.change,
+                "refresh_next": self.refresh_next}
 
     def load_state_dict(self, sd):
         self.r, self.dr, self.has_prev = sd["r"], sd["dr"], bool(sd["has_prev"])
+        self.prev_out = sd.get("prev_out")
+        self.change = float(sd.get("change", 0.0))
+        self.refresh_next = bool(sd.get("refresh_next", self.r is None))
 
     def _sm_scale(self, head_dim: int):
         c = self.cfg
@@ -87,7 +107,40 @@ class QuantSparseAttention:
         self.last = StepBuffers(qc, qs, qp, kc, ks, kp, idx, cnt)
         return qc, qs, kc, ks, idx, cnt
 
-    def step(self, q, k, v, refresh: bool) -> torch.Tensor:
+    def step(self, q, k, v, refresh: bool | None = None) -> torch.Tensor:
+        """One denoising step of this layer.  ``refresh=None`` lets the
+        adaptive trigger decide (needs ``adaptive_delta``)."""
+        c = self.cfg
+        if refresh is None:
+            if c.adaptive_delta is None:
+                raise ValueError("refresh=None needs QSAConfig.adaptive_delta")
+            refresh = self.refresh_next or self.r is None
+        out = self._step(q, k, v, refresh)
+        if c.adaptive_delta is not None:
+            self._account(out)
+        return out
+
+    def _account(self, out):
+        """Accumulate the normalised L1 change of consecutive outputs and set
+        whether the next step refreshes (one small device-to-host copy)."""
+        if self.prev_out is None:
+            self.prev_out = out.clone()
+            self.refresh_next = False
+            self.last_sums = None
+            return
+        if self.l1_work is None:
+            self.l1_work = torch.empty(B.QSA_L1_WORK_BYTES, dtype=torch.uint8, device=out.device)
+            self.l1_sums = torch.empty(2, dtype=torch.float64, device=out.device)
+        num, den = B.qsa_l1_change(self.prev_out, out, self.l1_sums, self.l1_work).tolist()
+        self.last_sums = (num, den)
+        d = num / den if den > 0 else (0.0 if num == 0 else float("inf"))
+        self.change += d
+        self.refresh_next = self.change > self.cfg.adaptive_delta
+        if self.refresh_next:
+            self.change = 0.0
+        self.prev_out.copy_(out)
+
+    def _step(self, q, k, v, refresh: bool) -> torch.Tensor:
         c = self.cfg
         qc, qs, kc, ks, idx, cnt = self._front(q, k)
         sm = self._sm_scale(q.shape[3])

@@ -38,7 +38,7 @@ def lib():
 def _declared():
     txt = open(HEADER).read()
     txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
-    return sorted(set(re.findall(r"\b(qsa_[a-z_]+)\s*\(", txt)))
+    return sorted(set(re.findall(r"\b(qsa_[a-z0-9_]+)\s*\(", txt)))
 
 
 def test_header_declares_the_entry_points():
@@ -198,3 +198,19 @@ def test_project_residual_validation(lib):
     assert pr(dims=_d(D=96)) == B.QSA_ERR_SHAPE
     if NO_GPU:
         assert pr() == B.QSA_ERR_DEVICE
+
+
+def test_l1_change_validation(lib):
+    u64 = ctypes.c_uint64
+
+    def l1(dims=None, ptrs=None, wb=B.QSA_L1_WORK_BYTES):
+        p = ptrs or P[:4]
+        return lib.qsa_l1_change(dims or _d(), p[0], p[1], p[2], p[3], u64(wb), None)
+
+    assert l1(wb=B.QSA_L1_WORK_BYTES - 1) == B.QSA_ERR_PARAM
+    assert l1(ptrs=[None] + P[1:4]) == B.QSA_ERR_NULL
+    assert l1(ptrs=P[:2] + [None, P[3]]) == B.QSA_ERR_NULL
+    assert l1(ptrs=P[:2] + [ctypes.c_void_p(0x3008), P[3]]) == B.QSA_ERR_ALIGN
+    assert l1(dims=_d(D=32)) == B.QSA_ERR_SHAPE
+    if NO_GPU:
+        assert l1() == B.QSA_ERR_DEVICE

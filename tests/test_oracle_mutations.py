@@ -14,6 +14,7 @@ from tests import test_oracle_quantize as TQ
 from tests import test_oracle_residual as TR
 from tests import test_oracle_rotation as TH
 from tests import test_oracle_projection as TP
+from tests import test_oracle_trigger as TT
 from tests import test_oracle_select as TS
 
 
@@ -120,11 +121,37 @@ def _refresh_unprojected(state, o_full, o_sparse, rank=None):
     return ORIG_REFRESH(state, o_full, o_sparse)
 
 
+def _l1_over_current(prev_bits, cur_bits):
+    num, _ = ORIG_L1(prev_bits, cur_bits)
+    return num, float(np.abs(Q.bf16_to_f64(cur_bits)).sum())
+
+
+class _TriggerNoReset(Q.RefreshTrigger):
+    def update(self, num=None, den=None):
+        if num is None:
+            return super().update()
+        self.c += num / den if den > 0 else (0.0 if num == 0 else float("inf"))
+        self.refresh_next = self.c > self.delta
+        return self.refresh_next
+
+
+class _TriggerAtOrAbove(Q.RefreshTrigger):
+    def update(self, num=None, den=None):
+        if num is None:
+            return super().update()
+        self.c += num / den if den > 0 else (0.0 if num == 0 else float("inf"))
+        self.refresh_next = self.c >= self.delta
+        if self.refresh_next:
+            self.c = 0.0
+        return self.refresh_next
+
+
 ORIG_QUANTIZE = Q.quantize
 ORIG_SCORES = Q.block_scores
 ORIG_SELECT = Q.select_blocks
 ORIG_ATTN = Q.attention
 ORIG_REFRESH = Q.refresh_step
+ORIG_L1 = Q.l1_change
 
 CASES = [
     ("quantize", _floor_quantize, lambda: TQ.test_half_integer_ties_round_to_even()),
@@ -148,6 +175,9 @@ CASES = [
      lambda: TP.test_eckart_young_energy_and_orthogonality()),
     ("refresh_step", _refresh_unprojected,
      lambda: TP.test_refresh_step_projects_only_the_second_order_residual()),
+    ("l1_change", _l1_over_current, lambda: TT.test_l1_change_closed_forms()),
+    ("RefreshTrigger", _TriggerNoReset, lambda: TT.test_trigger_hand_sequence()),
+    ("RefreshTrigger", _TriggerAtOrAbove, lambda: TT.test_trigger_hand_sequence()),
 ]
 
 
