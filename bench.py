@@ -51,6 +51,8 @@ def parse():
                    help="quantise Hadamard-rotated Q/K rows (attention with sm_scale / D)")
     p.add_argument("--rank", type=int, default=None,
                    help="project the second-order residual to this rank at refresh steps")
+    p.add_argument("--l1-change", action="store_true",
+                   help="also run the adaptive-refresh L1 change after every step (timed apart)")
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="before the run, copy a bf16 buffer of this many MiB once with a "
                         "plain elementwise kernel (reads and writes each byte once): the "
@@ -192,6 +194,10 @@ def main():
     r = torch.zeros((B, H, L, D), dtype=torch.bfloat16, device=dev)
     dr = torch.zeros_like(r)
     state = {"has_prev": False}
+    if args.l1_change:
+        prev_out = torch.zeros_like(r)
+        l1_sums = mk((2,), torch.float64)
+        l1_work = mk((Bn.QSA_L1_WORK_BYTES,), torch.uint8)
     if args.rank is not None:
         proj_work = mk((Bn.qsa_project_work_bytes(B, H, L, D, args.rank),), torch.uint8)
         proj_basis = mk((B, H, D, args.rank), torch.float32)
@@ -206,7 +212,7 @@ def main():
     def layer_step(s, kind, rec):
         x = inputs[s]
         idx, cnt = kept[s]
-        e = [ev() for _ in range(6)]
+        e = [ev() for _ in range(8)]
         projected = False
         e[0].record(stream)
         quant(x["q"], bs, qc, qs, qp)
@@ -229,6 +235,11 @@ def main():
             Bn.qsa_sparse_attn_ordered(qc, qs, kc, ks, x["v"], idx, cnt, order, bs, sm, r=r,
                                        dr=dr, out=out)
         e[3].record(stream)
+        if args.l1_change:
+            e[6].record(stream)
+            Bn.qsa_l1_change(prev_out, out, l1_sums, l1_work)
+            e[7].record(stream)
+            prev_out.copy_(out)
         if rec is not None:
             rec.append((kind, s, e, projected))
 
@@ -251,8 +262,10 @@ def main():
         return sum(xs) / len(xs) if xs else float("nan")
 
     t_quant, t_sel, t_sparse, t_full, t_order, step_sp, step_f = [], [], [], [], [], [], []
-    t_proj = []
+    t_proj, t_l1 = [], []
     for kind, s, e, projected in recs:
+        if args.l1_change:
+            t_l1.append(e[6].elapsed_time(e[7]))
         t_quant.append(e[0].elapsed_time(e[1]))
         t_sel.append(e[1].elapsed_time(e[2]))
         if kind == "S":
@@ -316,6 +329,7 @@ def main():
             "qsa_sparse_attn_ordered": round(mean(t_sparse), 4),
             "qsa_full_attn_residual": round(mean(t_full), 4),
             **({"qsa_project_residual": round(mean(t_proj), 4)} if t_proj else {}),
+            **({"qsa_l1_change": round(mean(t_l1), 4)} if t_l1 else {}),
         },
         "roofline": {
             "kernel": "qsa_sparse_attn_ordered",
