@@ -64,6 +64,17 @@ R10 adaptive refresh (DVD-Quant, gist.science/es/paper/2505.18663,
     (fp64); c += d_t; if c > delta the next step is a refresh step and c
     restarts at 0.  The first step is a refresh step (no cache yet).  A zero
     denominator gives d = 0 when the outputs agree, else +inf.
+R11 SQuad two-pass attention (SQuad, gist.science/es/paper/2608.16585,
+    technical summary, methodology §1): a (b, h) sequence of n tokens is cut
+    into n/w windows of w consecutive tokens.  The local pass is softmax
+    attention of every token over its own window, values V.  The global
+    pass is softmax attention of every token over the tokens at the same
+    position of every window (t = s mod w), values the local output, stored
+    in bf16.  Both passes use the same Q and K and the attention of R1-R6:
+    the local pass quantises Q and K in the natural order, the global pass in
+    position-major order (token s of window k at index p*(n/w) + k), so that
+    each pass's groups are runs of whole 64-token blocks; w and n/w must be
+    multiples of the block.  The page sets w = sqrt(n).
 """
 from __future__ import annotations
 
@@ -80,6 +91,10 @@ __all__ = [
     "project_residual",
     "l1_change",
     "RefreshTrigger",
+    "window_kept_lists",
+    "to_position_major",
+    "from_position_major",
+    "squad_attention",
     "block_scores",
     "select_blocks",
     "attention",
@@ -426,3 +441,60 @@ class RefreshTrigger:
         if self.refresh_next:
             self.c = 0.0
         return self.refresh_next
+
+
+# ---------------------------------------------------------------------------
+# SQuad two-pass attention (R11)
+# ---------------------------------------------------------------------------
+
+def window_kept_lists(B: int, H: int, seq_len: int, window: int, block: int):
+    """Kept lists of block-diagonal attention over windows of ``window``
+    tokens: query block i keeps the blocks of its own window, ascending."""
+    if window % block or seq_len % window:
+        raise ValueError("window must be a multiple of the block and divide seq_len")
+    nb = seq_len // block
+    per = window // block
+    idx = np.empty((B, H, nb, per), dtype=np.int32)
+    for i in range(nb):
+        idx[:, :, i, :] = (i // per) * per + np.arange(per)
+    return idx, np.full((B, H, nb), per, dtype=np.int32)
+
+
+def to_position_major(x, window: int):
+    """[B, H, n, ...] in window-major order (token p of window k at k*w + p) to
+    position-major order (at p*(n/w) + k)."""
+    B, H, n = x.shape[:3]
+    m = n // window
+    return np.ascontiguousarray(
+        x.reshape((B, H, m, window) + x.shape[3:]).swapaxes(2, 3).reshape(x.shape))
+
+
+def from_position_major(x, window: int):
+    """Inverse of to_position_major."""
+    B, H, n = x.shape[:3]
+    m = n // window
+    return np.ascontiguousarray(
+        x.reshape((B, H, window, m) + x.shape[3:]).swapaxes(2, 3).reshape(x.shape))
+
+
+def squad_attention(q_bits, k_bits, v_bits, window: int, block: int, sm_scale=None):
+    """SQuad two-pass attention of bf16 q, k, v [B, H, n, D] (R11), fp64 output.
+
+    Local pass over windows of ``window`` tokens with values v; its output is
+    rounded to bf16; global pass over the n/window tokens at each window
+    position with those values.
+    """
+    B, H, n, D = q_bits.shape
+    if n % window or window % block or (n // window) % block:
+        raise ValueError("window and n/window must be multiples of the block")
+    sm = default_sm_scale(D) if sm_scale is None else np.float32(sm_scale)
+    qc, sq, _ = quantize(q_bits, block)
+    kc, sk, _ = quantize(k_bits, block)
+    idx, cnt = window_kept_lists(B, H, n, window, block)
+    o_local = f64_to_bf16(attention(qc, sq, kc, sk, v_bits, idx, cnt, block, sm))
+    m = n // window
+    qc, sq, _ = quantize(to_position_major(q_bits, window), block)
+    kc, sk, _ = quantize(to_position_major(k_bits, window), block)
+    idx, cnt = window_kept_lists(B, H, n, m, block)
+    o = attention(qc, sq, kc, sk, to_position_major(o_local, window), idx, cnt, block, sm)
+    return from_position_major(o, window)

@@ -15,6 +15,7 @@ from tests import test_oracle_residual as TR
 from tests import test_oracle_rotation as TH
 from tests import test_oracle_projection as TP
 from tests import test_oracle_trigger as TT
+from tests import test_oracle_squad as TQS
 from tests import test_oracle_select as TS
 
 
@@ -126,6 +127,28 @@ def _l1_over_current(prev_bits, cur_bits):
     return num, float(np.abs(Q.bf16_to_f64(cur_bits)).sum())
 
 
+def _squad_variant(values_v=False, group_w=False, unpermute=True):
+    def bad(q_bits, k_bits, v_bits, window, block, sm_scale=None):
+        B, H, n, D = q_bits.shape
+        sm = Q.default_sm_scale(D)
+        qc, sq, _ = Q.quantize(q_bits, block)
+        kc, sk, _ = Q.quantize(k_bits, block)
+        idx, cnt = Q.window_kept_lists(B, H, n, window, block)
+        o_local = Q.f64_to_bf16(Q.attention(qc, sq, kc, sk, v_bits, idx, cnt, block, sm))
+        m = n // window
+        qc, sq, _ = Q.quantize(Q.to_position_major(q_bits, window), block)
+        kc, sk, _ = Q.quantize(Q.to_position_major(k_bits, window), block)
+        idx, cnt = Q.window_kept_lists(B, H, n, window if group_w else m, block)
+        vals = v_bits if values_v else o_local
+        o = Q.attention(qc, sq, kc, sk, Q.to_position_major(vals, window), idx, cnt, block, sm)
+        return Q.from_position_major(o, window) if unpermute else o
+    return bad
+
+
+def _pm_identity(x, window):
+    return np.ascontiguousarray(x)
+
+
 class _TriggerNoReset(Q.RefreshTrigger):
     def update(self, num=None, den=None):
         if num is None:
@@ -178,6 +201,13 @@ CASES = [
     ("l1_change", _l1_over_current, lambda: TT.test_l1_change_closed_forms()),
     ("RefreshTrigger", _TriggerNoReset, lambda: TT.test_trigger_hand_sequence()),
     ("RefreshTrigger", _TriggerAtOrAbove, lambda: TT.test_trigger_hand_sequence()),
+    ("squad_attention", _squad_variant(values_v=True),
+     lambda: TQS.test_squad_equals_masked_definition(4096, 64)),
+    ("squad_attention", _squad_variant(group_w=True),
+     lambda: TQS.test_squad_equals_masked_definition(8192, 64)),
+    ("squad_attention", _squad_variant(unpermute=False),
+     lambda: TQS.test_squad_equals_masked_definition(4096, 64)),
+    ("to_position_major", _pm_identity, lambda: TQS.test_position_major_index_formula()),
 ]
 
 
