@@ -53,6 +53,8 @@ def parse():
                    help="project the second-order residual to this rank at refresh steps")
     p.add_argument("--l1-change", action="store_true",
                    help="also run the adaptive-refresh L1 change after every step (timed apart)")
+    p.add_argument("--squad", action="store_true",
+                   help="also time SQuad two-pass attention on a 65,536-token, 24-head sequence")
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="before the run, copy a bf16 buffer of this many MiB once with a "
                         "plain elementwise kernel (reads and writes each byte once): the "
@@ -148,6 +150,45 @@ def cpu_baseline(w, budget_s: float, rotate: bool = False):
                    f"(extrapolated)"),
         "host_cpus": os.cpu_count(),
     }
+
+
+def squad_measure(Bn, steps, warmup):
+    """SQuad two-pass attention (window sqrt(n) = 256) on a 65,536-token
+    sequence of 24 heads x 128: time per call, the HBM roofline of the whole
+    operator and the MFMA work of its two attention passes."""
+    import torch
+
+    import qsa_gen
+    w = qsa_gen.get_workload("tiny").with_(batch=1, heads=24, grid=(1, 256, 256), block=64,
+                                           head_dim=128)
+    x = qsa_gen.make_qkv_torch(w, torch.device("cuda:0"))[0]
+    B, H, L, D, window = 1, 24, 65536, 128, 256
+    out = torch.empty_like(x["q"])
+    work = torch.empty(Bn.qsa_squad_work_bytes(B, H, L, D, 64, window), dtype=torch.uint8,
+                       device="cuda")
+    for _ in range(warmup):
+        Bn.qsa_squad_attention(x["q"], x["k"], x["v"], window, 64, out=out, work=work)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ts = []
+    for _ in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        Bn.qsa_squad_attention(x["q"], x["k"], x["v"], window, 64, out=out, work=work)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    t = sum(ts) / len(ts) * 1e-3
+    # the operator must read q, k, v and write out once: 4 bf16 tensors
+    alg_bytes = 4 * B * H * L * D * 2
+    # each pass: every token against its group of 256 (int8 QK^T and bf16 PV)
+    ops = 2 * B * H * L * window * D
+    tmin = 2 * (ops / PEAK_INT8_OPS + ops / PEAK_BF16_FLOPS)
+    return {"workload": "squad_65536x24x128_w256", "ms": round(t * 1e3, 4),
+            "roofline": {"bound": "hbm", "achieved": round(alg_bytes / t / 1e9, 1),
+                         "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                         "frac": round(alg_bytes / t / PEAK_HBM_BYTES, 4)},
+            "attention_passes_mfma_floor_ms": round(tmin * 1e3, 4)}
 
 
 def main():
@@ -354,6 +395,10 @@ def main():
                 "frac": round(q_bytes / t_q1 / PEAK_HBM_BYTES, 4) if t_q1 else None},
         },
     }
+    if args.squad:
+        del inputs, qc, kc, qp, kp, kept, out, r, dr
+        torch.cuda.empty_cache()
+        res["squad"] = squad_measure(Bn, max(3, args.steps), 1)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.rotate)
     print(json.dumps(res), flush=True)

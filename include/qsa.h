@@ -21,8 +21,9 @@
  *     the last block is shorter when block does not divide seq_len.
  *   - Every tensor pointer must be 16-byte aligned (QSA_ERR_ALIGN).
  *   - The caller owns all memory.  The library allocates nothing and keeps no
- *     state between calls; calls are re-entrant.  Only qsa_project_residual
- *     and qsa_l1_change need scratch memory, which their caller passes in.
+ *     state between calls; calls are re-entrant.  Only qsa_project_residual,
+ *     qsa_l1_change and qsa_squad_attention need scratch memory, which their
+ *     caller passes in.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and runs asynchronously.  Argument errors are detected on the host
  *     before anything is enqueued; device faults surface at the caller's next
@@ -300,6 +301,62 @@ uint64_t qsa_project_work_bytes(const qsa_dims* dims, int32_t rank);
  */
 int qsa_l1_change(const qsa_dims* dims, const uint16_t* prev, const uint16_t* cur, double* sums,
                   void* work, uint64_t work_bytes, void* stream);
+
+/*
+ * qsa_window_kept -- kept lists of block-diagonal attention over windows of
+ * `window` consecutive tokens (the passes of SQuad attention, SQuad
+ * gist.science/es/paper/2608.16585, technical summary, methodology §1):
+ * query block i keeps the blocks of its own window, ascending:
+ *   kept_idx[b,h,i,j] = (i / per) * per + j  for j < per = window / block,
+ *                       -1 for per <= j < kmax;  kept_cnt[b,h,i] = per
+ *
+ *   window       in: a multiple of dims->block that divides seq_len
+ *   kmax         in: row stride of kept_idx, >= window / block
+ *   kept_idx    out: int32 [B,H,nb,kmax];  kept_cnt out: int32 [B,H,nb]
+ * QSA_ERR_PARAM for a window or kmax out of range.
+ */
+int qsa_window_kept(const qsa_dims* dims, int32_t window, int32_t kmax, int32_t* kept_idx,
+                    int32_t* kept_cnt, void* stream);
+
+/*
+ * qsa_reorder_windows -- reorder the rows of every (b, h) sequence of n
+ * tokens between window-major order (token p of window k at k*w + p) and
+ * position-major order (at p*(n/w) + k), the order of SQuad's global pass:
+ *   inverse = 0:  y[p*(n/w) + k] = x[k*w + p]
+ *   inverse = 1:  y[k*w + p] = x[p*(n/w) + k]
+ *
+ *   window   in: w, divides seq_len
+ *   x, y     in / out: bf16 [B,H,L,D]; must not overlap
+ * QSA_ERR_PARAM for a window that does not divide seq_len.
+ */
+int qsa_reorder_windows(const qsa_dims* dims, int32_t window, int32_t inverse, const uint16_t* x,
+                        uint16_t* y, void* stream);
+
+/*
+ * qsa_squad_attention -- SQuad two-pass attention (technical summary,
+ * methodology §1) on this path's attention core:
+ *   1. local pass: qsa_quantize(Q), qsa_quantize(K) in the natural order,
+ *      then block-sparse attention (as qsa_sparse_attn) over the windows of
+ *      `window` tokens, values V; output O_local, bf16;
+ *   2. global pass: Q, K and O_local reordered to position-major order
+ *      (qsa_reorder_windows), Q and K quantised in that order, attention over
+ *      groups of seq_len / window tokens with values O_local;
+ *   3. out = the global output in the natural order.
+ * The page sets window = sqrt(seq_len).
+ *
+ *   q, k, v     in: bf16 [B,H,L,D]
+ *   window      in: window and seq_len / window both multiples of dims->block
+ *   sm_scale    in: > 0 and finite (normally 1/sqrt(D))
+ *   out        out: bf16 [B,H,L,D], must not overlap the inputs
+ *   work    in/out: device scratch of qsa_squad_work_bytes(dims, window) bytes
+ * QSA_ERR_PARAM for a window out of range, a bad sm_scale or too little work.
+ */
+int qsa_squad_attention(const qsa_dims* dims, const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, int32_t window, float sm_scale, uint16_t* out,
+                        void* work, uint64_t work_bytes, void* stream);
+
+/* Bytes of scratch qsa_squad_attention needs (0 for invalid dims or window). */
+uint64_t qsa_squad_work_bytes(const qsa_dims* dims, int32_t window);
 
 /* Static text of a status code. */
 const char* qsa_status_string(int status);

@@ -33,7 +33,8 @@ QSA_L1_WORK_BYTES = 16384
 EXPORTED = ("qsa_quantize", "qsa_select_blocks", "qsa_sparse_attn", "qsa_full_attn_residual",
             "qsa_apply_residual", "qsa_order_query_blocks", "qsa_sparse_attn_ordered",
             "qsa_quantize_rotated", "qsa_project_residual", "qsa_project_work_bytes",
-            "qsa_l1_change",
+            "qsa_l1_change", "qsa_window_kept", "qsa_reorder_windows", "qsa_squad_attention",
+            "qsa_squad_work_bytes",
             "qsa_status_string", "qsa_last_error_detail", "qsa_version")
 
 
@@ -77,11 +78,17 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                             vp, vp]
     lib.qsa_project_residual.argtypes = [pd, vp, i32, vp, vp, vp, ctypes.c_uint64, vp]
     lib.qsa_l1_change.argtypes = [pd, vp, vp, vp, vp, ctypes.c_uint64, vp]
+    lib.qsa_window_kept.argtypes = [pd, i32, i32, vp, vp, vp]
+    lib.qsa_reorder_windows.argtypes = [pd, i32, i32, vp, vp, vp]
+    lib.qsa_squad_attention.argtypes = [pd, vp, vp, vp, i32, f32, vp, vp, ctypes.c_uint64, vp]
+    lib.qsa_squad_work_bytes.argtypes = [pd, i32]
+    lib.qsa_squad_work_bytes.restype = ctypes.c_uint64
     lib.qsa_project_work_bytes.argtypes = [pd, i32]
     lib.qsa_project_work_bytes.restype = ctypes.c_uint64
     for f in ("qsa_quantize", "qsa_quantize_rotated", "qsa_select_blocks", "qsa_sparse_attn",
               "qsa_full_attn_residual", "qsa_apply_residual", "qsa_order_query_blocks",
-              "qsa_sparse_attn_ordered", "qsa_project_residual", "qsa_l1_change"):
+              "qsa_sparse_attn_ordered", "qsa_project_residual", "qsa_l1_change",
+              "qsa_window_kept", "qsa_reorder_windows", "qsa_squad_attention"):
         getattr(lib, f).restype = ctypes.c_int
     lib.qsa_status_string.argtypes = [ctypes.c_int]
     lib.qsa_status_string.restype = ctypes.c_char_p
@@ -350,3 +357,62 @@ def qsa_l1_change(prev: torch.Tensor, cur: torch.Tensor, sums=None, work=None, s
                                         _ptr(work), ctypes.c_uint64(work.numel()),
                                         _stream(stream)))
     return sums
+
+
+def qsa_window_kept(B: int, H: int, L: int, block: int, window: int, kmax=None, kept_idx=None,
+                    kept_cnt=None, device="cuda", stream=None):
+    """Kept lists of block-diagonal attention over windows of ``window`` tokens."""
+    nb = n_blocks(L, block)
+    kmax = window // block if kmax is None else kmax
+    kept_idx = (torch.empty((B, H, nb, kmax), dtype=torch.int32, device=device)
+                if kept_idx is None else kept_idx)
+    kept_cnt = (torch.empty((B, H, nb), dtype=torch.int32, device=device)
+                if kept_cnt is None else kept_cnt)
+    _need(kept_idx, "kept_idx", torch.int32, (B, H, nb, kmax))
+    _need(kept_cnt, "kept_cnt", torch.int32, (B, H, nb))
+    d = make_dims(B, H, L, 64, block)
+    _check(load_library().qsa_window_kept(ctypes.byref(d), int(window), int(kmax),
+                                          _ptr(kept_idx), _ptr(kept_cnt), _stream(stream)))
+    return kept_idx, kept_cnt
+
+
+def qsa_reorder_windows(x: torch.Tensor, window: int, inverse: bool = False, out=None,
+                        stream=None):
+    """Rows of bf16 x [B,H,L,D] from window-major to position-major order
+    (or back with ``inverse``)."""
+    _need(x, "x", torch.bfloat16)
+    B, H, L, D = x.shape
+    out = torch.empty_like(x) if out is None else out
+    _need(out, "out", torch.bfloat16, (B, H, L, D))
+    d = make_dims(B, H, L, D, 64)
+    _check(load_library().qsa_reorder_windows(ctypes.byref(d), int(window), int(bool(inverse)),
+                                              _ptr(x), _ptr(out), _stream(stream)))
+    return out
+
+
+def qsa_squad_work_bytes(B: int, H: int, L: int, D: int, block: int, window: int) -> int:
+    d = make_dims(B, H, L, D, block)
+    return int(load_library().qsa_squad_work_bytes(ctypes.byref(d), int(window)))
+
+
+def qsa_squad_attention(q, k, v, window: int, block: int = 64, sm_scale: float | None = None,
+                        out=None, work=None, stream=None):
+    """SQuad two-pass attention of bf16 q, k, v [B,H,L,D]: local windows of
+    ``window`` tokens, then same-position groups with the local output as
+    values."""
+    for t, name in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, name, torch.bfloat16, tuple(q.shape))
+    B, H, L, D = q.shape
+    out = torch.empty_like(q) if out is None else out
+    _need(out, "out", torch.bfloat16, (B, H, L, D))
+    need = qsa_squad_work_bytes(B, H, L, D, block, window)
+    if work is None:
+        work = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    _need(work, "work", torch.uint8)
+    sm = default_sm_scale(D) if sm_scale is None else float(sm_scale)
+    d = make_dims(B, H, L, D, block)
+    _check(load_library().qsa_squad_attention(ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v),
+                                              int(window), ctypes.c_float(sm), _ptr(out),
+                                              _ptr(work), ctypes.c_uint64(work.numel()),
+                                              _stream(stream)))
+    return out

@@ -388,4 +388,82 @@ int qsa_l1_change(const qsa_dims* dims, const uint16_t* prev, const uint16_t* cu
                                             static_cast<hipStream_t>(stream)));
 }
 
+int qsa_window_kept(const qsa_dims* dims, int32_t window, int32_t kmax, int32_t* kept_idx,
+                    int32_t* kept_cnt, void* stream) {
+  const char* fn = "qsa_window_kept";
+  int st = check_dims(fn, dims);
+  if (st) return st;
+  REQUIRE_PTR(kept_idx);
+  REQUIRE_PTR(kept_cnt);
+  if (window < dims->block || window % dims->block || dims->seq_len % window)
+    return fail(QSA_ERR_PARAM, "%s: window=%d must be a multiple of block=%d dividing seq_len=%d",
+                fn, window, dims->block, dims->seq_len);
+  if (kmax < window / dims->block)
+    return fail(QSA_ERR_PARAM, "%s: kmax=%d < window/block=%d", fn, kmax, window / dims->block);
+  if ((st = check_device(fn))) return st;
+  (void)hipGetLastError();
+  return launched(fn, qsa::launch_window_kept(*dims, window, kmax, kept_idx, kept_cnt,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int qsa_reorder_windows(const qsa_dims* dims, int32_t window, int32_t inverse, const uint16_t* x,
+                        uint16_t* y, void* stream) {
+  const char* fn = "qsa_reorder_windows";
+  int st = check_dims(fn, dims);
+  if (st) return st;
+  REQUIRE_PTR(x);
+  REQUIRE_PTR(y);
+  if (window < 1 || dims->seq_len % window)
+    return fail(QSA_ERR_PARAM, "%s: window=%d must divide seq_len=%d", fn, window,
+                dims->seq_len);
+  if (inverse != 0 && inverse != 1)
+    return fail(QSA_ERR_PARAM, "%s: inverse=%d must be 0 or 1", fn, inverse);
+  if ((st = check_device(fn))) return st;
+  (void)hipGetLastError();
+  return launched(fn, qsa::launch_reorder(*dims, window, inverse, x, y,
+                                          static_cast<hipStream_t>(stream)));
+}
+
+static bool squad_window_ok(const qsa_dims* d, int32_t window) {
+  return window >= d->block && window % d->block == 0 && d->seq_len % window == 0 &&
+         (d->seq_len / window) % d->block == 0;
+}
+
+uint64_t qsa_squad_work_bytes(const qsa_dims* dims, int32_t window) {
+  if (check_dims("qsa_squad_work_bytes", dims) != QSA_OK) return 0;
+  if (!squad_window_ok(dims, window)) return 0;
+  return qsa::squad_plan(*dims, window).bytes;
+}
+
+int qsa_squad_attention(const qsa_dims* dims, const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, int32_t window, float sm_scale, uint16_t* out,
+                        void* work, uint64_t work_bytes, void* stream) {
+  const char* fn = "qsa_squad_attention";
+  int st = check_dims(fn, dims);
+  if (st) return st;
+  REQUIRE_PTR(q);
+  REQUIRE_PTR(k);
+  REQUIRE_PTR(v);
+  REQUIRE_PTR(out);
+  REQUIRE_PTR(work);
+  if (!squad_window_ok(dims, window))
+    return fail(QSA_ERR_PARAM,
+                "%s: window=%d and seq_len/window must both be multiples of block=%d", fn,
+                window, dims->block);
+  if (!(sm_scale > 0.0f) || !isfinite(sm_scale))
+    return fail(QSA_ERR_PARAM, "%s: sm_scale=%g must be positive and finite", fn, sm_scale);
+  const int64_t nb = dims->seq_len / dims->block;
+  if (nb > QSA_MAX_BLOCKS)
+    return fail(QSA_ERR_SHAPE, "%s: %lld blocks exceed %d", fn, (long long)nb, QSA_MAX_BLOCKS);
+  const uint64_t need = qsa::squad_plan(*dims, window).bytes;
+  if (work_bytes < need)
+    return fail(QSA_ERR_PARAM, "%s: work_bytes=%llu is less than the %llu needed", fn,
+                (unsigned long long)work_bytes, (unsigned long long)need);
+  if ((st = check_device(fn))) return st;
+  (void)hipGetLastError();
+  return launched(fn, qsa::launch_squad(*dims, q, k, v, window, sm_scale, out,
+                                        static_cast<char*>(work),
+                                        static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

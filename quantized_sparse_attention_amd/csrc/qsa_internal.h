@@ -111,6 +111,22 @@ int l1_change_blocks(uint64_t n_elements);
 hipError_t launch_l1_change(uint64_t n_elements, const uint16_t* prev, const uint16_t* cur,
                             double* sums, double* work, hipStream_t s);
 
+// SQuad two-pass attention: scratch layout (byte offsets, 256-aligned).
+struct SquadPlan {
+  int kmax;
+  uint64_t bytes;
+  uint64_t q_codes, k_codes, q_scales, k_scales, q_pooled, k_pooled, kept_idx, kept_cnt;
+  uint64_t o_local, q_perm, k_perm, v_perm;
+};
+SquadPlan squad_plan(const qsa_dims& d, int window);
+hipError_t launch_window_kept(const qsa_dims& d, int window, int kmax, int32_t* kept_idx,
+                              int32_t* kept_cnt, hipStream_t s);
+hipError_t launch_reorder(const qsa_dims& d, int window, int inverse, const uint16_t* x,
+                          uint16_t* y, hipStream_t s);
+hipError_t launch_squad(const qsa_dims& d, const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, int window, float sm_scale, uint16_t* out, char* work,
+                        hipStream_t s);
+
 hipError_t launch_apply_residual(const qsa_dims& d, const uint16_t* sparse_out,
                                  const uint16_t* r, const uint16_t* dr, uint16_t* out,
                                  hipStream_t s);

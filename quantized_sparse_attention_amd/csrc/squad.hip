@@ -1,0 +1,161 @@
+// SQuad two-pass attention on this path's attention core.
+//
+// SQuad (gist.science/es/paper/2608.16585, technical summary, methodology
+// §1): a sequence of n tokens is cut into windows of w consecutive tokens;
+// a local softmax pass mixes each window, then a global softmax pass mixes
+// the tokens at the same position of every window, with the local output as
+// its values.  Both passes here are the block-sparse int8/bf16 attention of
+// attn.hip with block-diagonal kept lists: the local pass over windows of w
+// tokens in the natural order, the global pass over groups of n/w tokens in
+// position-major order (token p of window k at p*(n/w) + k), so every group
+// is a run of whole blocks and both passes run as dense tiles.
+//
+// Kernels of their own: the kept lists of block-diagonal attention, and the
+// reorder between window-major and position-major order (a row gather of
+// 16-byte chunks, HBM-bound).
+#include "qsa_internal.h"
+
+namespace qsa {
+namespace {
+
+__global__ __launch_bounds__(256) void window_kept_kernel(int32_t* __restrict__ kept_idx,
+                                                          int32_t* __restrict__ kept_cnt,
+                                                          uint64_t rows, int nb, int per,
+                                                          int kmax) {
+  const uint64_t row = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= rows) return;
+  const int i = (int)(row % (uint64_t)nb);
+  const int first = (i / per) * per;
+  int32_t* kl = kept_idx + row * (uint64_t)kmax;
+  for (int j = 0; j < kmax; ++j) kl[j] = j < per ? first + j : -1;
+  kept_cnt[row] = per;
+}
+
+// y row r takes x row src(r): forward (window-major -> position-major)
+// src(p*m + k) = k*w + p; inverse src(k*w + p) = p*m + k.
+template <int D>
+__global__ __launch_bounds__(256) void reorder_kernel(const uint16_t* __restrict__ x,
+                                                      uint16_t* __restrict__ y, int n, int w,
+                                                      int inverse, uint64_t chunks) {
+  constexpr int CPR = D / 8;  // 16-byte chunks per row
+  const uint64_t c = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= chunks) return;
+  const uint64_t grow = c / CPR;  // global row over (b, h, r)
+  const int part = (int)(c % CPR);
+  const uint64_t bh = grow / (uint64_t)n;
+  const int r = (int)(grow % (uint64_t)n);
+  const int m = n / w;
+  const int src = inverse ? (r % w) * m + r / w : (r % m) * w + r / m;
+  const uint4 v =
+      *reinterpret_cast<const uint4*>(x + ((bh * (uint64_t)n + src) * D) + part * 8);
+  *reinterpret_cast<uint4*>(y + grow * D + part * 8) = v;
+}
+
+}  // namespace
+
+hipError_t launch_window_kept(const qsa_dims& d, int window, int kmax, int32_t* kept_idx,
+                              int32_t* kept_cnt, hipStream_t s) {
+  const int nb = d.seq_len / d.block;
+  const uint64_t rows = (uint64_t)d.batch * d.heads * nb;
+  hipLaunchKernelGGL(window_kept_kernel, dim3((uint32_t)((rows + 255) / 256)), dim3(256), 0, s,
+                     kept_idx, kept_cnt, rows, nb, window / d.block, kmax);
+  return hipGetLastError();
+}
+
+hipError_t launch_reorder(const qsa_dims& d, int window, int inverse, const uint16_t* x,
+                          uint16_t* y, hipStream_t s) {
+  const uint64_t chunks = (uint64_t)d.batch * d.heads * d.seq_len * (d.head_dim / 8);
+  const dim3 grid((uint32_t)((chunks + 255) / 256));
+  if (d.head_dim == 128)
+    hipLaunchKernelGGL((reorder_kernel<128>), grid, dim3(256), 0, s, x, y, d.seq_len, window,
+                       inverse, chunks);
+  else
+    hipLaunchKernelGGL((reorder_kernel<64>), grid, dim3(256), 0, s, x, y, d.seq_len, window,
+                       inverse, chunks);
+  return hipGetLastError();
+}
+
+SquadPlan squad_plan(const qsa_dims& d, int window) {
+  SquadPlan p;
+  const uint64_t bh = (uint64_t)d.batch * d.heads;
+  const uint64_t n = (uint64_t)d.seq_len, D = (uint64_t)d.head_dim;
+  const uint64_t nb = n / (uint64_t)d.block;
+  const int m = d.seq_len / window;
+  p.kmax = (window > m ? window : m) / d.block;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t off = p.bytes;
+    p.bytes += (bytes + 255) / 256 * 256;
+    return off;
+  };
+  p.bytes = 0;
+  p.q_codes = take(bh * n * D);
+  p.k_codes = take(bh * n * D);
+  p.q_scales = take(bh * nb * 4);
+  p.k_scales = take(bh * nb * 4);
+  p.q_pooled = take(bh * nb * D * 4);
+  p.k_pooled = take(bh * nb * D * 4);
+  p.kept_idx = take(bh * nb * (uint64_t)p.kmax * 4);
+  p.kept_cnt = take(bh * nb * 4);
+  p.o_local = take(bh * n * D * 2);
+  p.q_perm = take(bh * n * D * 2);
+  p.k_perm = take(bh * n * D * 2);
+  p.v_perm = take(bh * n * D * 2);
+  return p;
+}
+
+hipError_t launch_squad(const qsa_dims& d, const uint16_t* q, const uint16_t* k,
+                        const uint16_t* v, int window, float sm_scale, uint16_t* out, char* work,
+                        hipStream_t s) {
+  const SquadPlan p = squad_plan(d, window);
+  int8_t* qc = reinterpret_cast<int8_t*>(work + p.q_codes);
+  int8_t* kc = reinterpret_cast<int8_t*>(work + p.k_codes);
+  float* qs = reinterpret_cast<float*>(work + p.q_scales);
+  float* ks = reinterpret_cast<float*>(work + p.k_scales);
+  int32_t* qp = reinterpret_cast<int32_t*>(work + p.q_pooled);
+  int32_t* kp = reinterpret_cast<int32_t*>(work + p.k_pooled);
+  int32_t* idx = reinterpret_cast<int32_t*>(work + p.kept_idx);
+  int32_t* cnt = reinterpret_cast<int32_t*>(work + p.kept_cnt);
+  uint16_t* o_local = reinterpret_cast<uint16_t*>(work + p.o_local);
+  uint16_t* q_perm = reinterpret_cast<uint16_t*>(work + p.q_perm);
+  uint16_t* k_perm = reinterpret_cast<uint16_t*>(work + p.k_perm);
+  uint16_t* v_perm = reinterpret_cast<uint16_t*>(work + p.v_perm);
+  const int m = d.seq_len / window;
+
+  AttnArgs a{};
+  a.q_codes = qc;
+  a.q_scales = qs;
+  a.k_codes = kc;
+  a.k_scales = ks;
+  a.kept_idx = idx;
+  a.kept_cnt = cnt;
+  a.order = nullptr;
+  a.kmax = p.kmax;
+  a.sm_scale = sm_scale;
+
+  hipError_t e;
+#define QSA_TRY(x) \
+  if ((e = (x)) != hipSuccess) return e
+  // local pass: windows of w tokens, natural order, values V
+  QSA_TRY(launch_quantize(d, q, qc, qs, qp, s));
+  QSA_TRY(launch_quantize(d, k, kc, ks, kp, s));
+  QSA_TRY(launch_window_kept(d, window, p.kmax, idx, cnt, s));
+  a.v = v;
+  a.out = o_local;
+  QSA_TRY(launch_sparse_attn(d, a, s));
+  // global pass: groups of n/w tokens in position-major order, values the
+  // local output
+  QSA_TRY(launch_reorder(d, window, 0, q, q_perm, s));
+  QSA_TRY(launch_reorder(d, window, 0, k, k_perm, s));
+  QSA_TRY(launch_reorder(d, window, 0, o_local, v_perm, s));
+  QSA_TRY(launch_quantize(d, q_perm, qc, qs, qp, s));
+  QSA_TRY(launch_quantize(d, k_perm, kc, ks, kp, s));
+  QSA_TRY(launch_window_kept(d, m, p.kmax, idx, cnt, s));
+  a.v = v_perm;
+  a.out = q_perm;  // free once its codes are taken
+  QSA_TRY(launch_sparse_attn(d, a, s));
+  QSA_TRY(launch_reorder(d, window, 1, q_perm, out, s));
+#undef QSA_TRY
+  return hipSuccess;
+}
+
+}  // namespace qsa

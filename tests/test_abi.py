@@ -214,3 +214,33 @@ def test_l1_change_validation(lib):
     assert l1(dims=_d(D=32)) == B.QSA_ERR_SHAPE
     if NO_GPU:
         assert l1() == B.QSA_ERR_DEVICE
+
+
+def test_squad_validation(lib):
+    u64, f = ctypes.c_uint64, ctypes.c_float
+    d = _d(L=4096, D=64)
+    need = lib.qsa_squad_work_bytes(d, 64)
+    assert need > 0
+    assert lib.qsa_squad_work_bytes(d, 96) == 0       # not a multiple of the block
+    assert lib.qsa_squad_work_bytes(d, 2048) == 0     # n / w = 2 is not
+    assert lib.qsa_squad_work_bytes(_d(L=4100, D=64), 64) == 0
+
+    def sq(window=64, sm=0.125, wb=None, ptrs=None):
+        p = ptrs or P[:5]
+        return lib.qsa_squad_attention(d, p[0], p[1], p[2], window, f(sm), p[3], p[4],
+                                       u64(need if wb is None else wb), None)
+
+    assert sq(window=96) == B.QSA_ERR_PARAM
+    assert sq(sm=0.0) == B.QSA_ERR_PARAM
+    assert sq(sm=float("inf")) == B.QSA_ERR_PARAM
+    assert sq(wb=need - 1) == B.QSA_ERR_PARAM
+    assert sq(ptrs=[None] + P[1:5]) == B.QSA_ERR_NULL
+    assert sq(ptrs=P[:4] + [ctypes.c_void_p(0x1002)]) == B.QSA_ERR_ALIGN
+    assert lib.qsa_window_kept(d, 96, 4, P[0], P[1], None) == B.QSA_ERR_PARAM
+    assert lib.qsa_window_kept(d, 128, 1, P[0], P[1], None) == B.QSA_ERR_PARAM
+    assert lib.qsa_reorder_windows(d, 100, 0, P[0], P[1], None) == B.QSA_ERR_PARAM
+    assert lib.qsa_reorder_windows(d, 64, 2, P[0], P[1], None) == B.QSA_ERR_PARAM
+    if NO_GPU:
+        assert sq() == B.QSA_ERR_DEVICE
+        assert lib.qsa_window_kept(d, 128, 2, P[0], P[1], None) == B.QSA_ERR_DEVICE
+        assert lib.qsa_reorder_windows(d, 64, 1, P[0], P[1], None) == B.QSA_ERR_DEVICE

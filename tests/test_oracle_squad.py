@@ -18,9 +18,10 @@ import qsa_gen
 
 
 def _inputs(B, H, n, D, seed):
-    w = qsa_gen.get_workload("tiny").with_(batch=B, heads=H, grid=(1, n // 64, 64), block=64,
-                                           head_dim=D)
-    return qsa_gen.make_qkv(w, seed)
+    """Seeded inputs (the seed selects the generator stream; step 0)."""
+    w = qsa_gen.get_workload("tiny").with_(cfg_id=100 + seed, batch=B, heads=H,
+                                           grid=(1, n // 64, 64), block=64, head_dim=D)
+    return qsa_gen.make_qkv(w, 0)
 
 
 def test_position_major_index_formula():
