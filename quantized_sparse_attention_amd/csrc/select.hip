@@ -5,7 +5,8 @@
 // top-k salient local guidance): every query block keeps the key blocks whose
 // mean-pooled dequantised codes score highest, plus a fixed band of offsets.
 //
-// One workgroup (4 waves) per (batch*head, tile of TR query blocks).
+// One workgroup (4 waves) per (batch*head, tile of TR = 8 query blocks; two
+// workgroups share a CU, which hides the latency of the select passes).
 //  1. Exact integer scores S_ij = sum_d Pq[i,d] Pk[j,d] on the int8 MFMA:
 //     each pooled sum P (|P| <= 127*128) is split into int8 digits
 //     P = 128*hi + lo with lo in [0,127], hi in [-127,127], and
@@ -14,17 +15,24 @@
 //     fp64 (all values are integers below 2^53).
 //  2. score = fl64(fl64(S * sq*sk) / (n_i*n_j)) in IEEE fp64, mapped to an
 //     order-preserving uint64 key (-0 canonicalised to +0), kept in LDS.
-//  3. Per row (one wave), an 8-pass radix select over the keys finds the
-//     k-th largest key T and how many keys equal to T are taken.
+//  3. Per row (one wave), a radix select over the keys, one byte per pass,
+//     finds the k-th largest key T and how many keys equal to T are taken.
+//     The passes start after the bytes shared by the row's smallest and
+//     largest key (shared by every key) and stop once the bin holding the
+//     k-th key is taken whole; T is then known on its decided bytes only.
 //  4. Ascending compaction with wave ballots: j is kept if key > T, or
-//     key == T and fewer than `take` lower-indexed ties precede it, or
-//     j - i is a band offset.
+//     key == T and fewer than `take` lower-indexed ties precede it (both
+//     compared on T's decided bytes), or j - i is a band offset.
 #include "qsa_internal.h"
 
 #pragma clang fp contract(off)
 
 namespace qsa {
 namespace {
+
+#ifndef QSA_SEL_TR
+#define QSA_SEL_TR 8
+#endif
 
 constexpr int kSelThreads = 256;
 constexpr int kHist = 256;
@@ -137,7 +145,30 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     uint64_t prefix = 0, pmask = 0;
     int need = k_eff;  // how many still to take among keys matching prefix
     const bool do_select = active && k_eff > 0 && k_eff < nb;
-    for (int pass = 0; pass < 8; ++pass) {
+    // Every key lies between the row's smallest and largest, so the bytes
+    // those two share are shared by all keys: the passes start after them.
+    int first_pass = 8;
+    if (do_select) {
+      uint64_t kmin = ~0ull, kmax_ = 0ull;
+      for (int j = lane; j < nb; j += 64) {
+        const uint64_t key = keys[j];
+        kmin = key < kmin ? key : kmin;
+        kmax_ = key > kmax_ ? key : kmax_;
+      }
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) {
+        const uint64_t a = __shfl_xor(kmin, o, 64), b = __shfl_xor(kmax_, o, 64);
+        kmin = a < kmin ? a : kmin;
+        kmax_ = b > kmax_ ? b : kmax_;
+      }
+      const uint64_t diff = kmin ^ kmax_;
+      first_pass = diff ? __clzll((long long)diff) / 8 : 8;
+      if (first_pass > 0) {
+        pmask = first_pass == 8 ? ~0ull : ~0ull << (64 - 8 * first_pass);
+        prefix = kmax_ & pmask;
+      }
+    }
+    for (int pass = do_select ? first_pass : 8; pass < 8; ++pass) {
       const int shift = 56 - 8 * pass;
       // The histogram is this wave's own: LDS operations of one wave are
       // performed in order, so waiting for them (lgkmcnt) orders the zeroing,
@@ -183,9 +214,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         const int src = __ffsll((unsigned long long)who) - 1;
         digit = __shfl(digit, src, 64);
         cnt_above = __shfl(cnt_above, src, 64);
+        const uint32_t in_bin = s_hist[wave][digit];
         need -= (int)cnt_above;
         prefix |= (uint64_t)digit << shift;
         pmask |= 0xffull << shift;
+        // every key of the chosen bin is taken: no finer digit can matter
+        if ((uint32_t)need == in_bin) break;
       }
     }
 
@@ -204,10 +238,13 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         } else if (k_eff == nb) {
           sel = true;
         } else {
-          const bool eq = key == prefix;
+          // compared on the decided digits only (all of them unless the
+          // select stopped at a bin taken whole)
+          const uint64_t mk = key & pmask;
+          const bool eq = mk == prefix;
           const uint64_t eqb = __ballot(valid && eq);
           const int rank = ties_seen + __popcll(eqb & lanemask_lt(lane));
-          sel = key > prefix || (eq && rank < need);
+          sel = mk > prefix || (eq && rank < need);
           ties_seen += __popcll(eqb);
         }
         sel = valid && (sel || in_band);
@@ -230,7 +267,7 @@ hipError_t launch_select(const qsa_dims& d, const int32_t* pooled_q, const float
                          hipStream_t s) {
   const int nb = (d.seq_len + d.block - 1) / d.block;
   const size_t lds_cap = 160 * 1024 - sizeof(uint32_t) * 4 * kHist - 256;
-  int TR = 16;
+  int TR = QSA_SEL_TR;
   while (TR > 1 && (size_t)TR * nb * sizeof(uint64_t) > lds_cap) TR >>= 1;
   const size_t lds = (size_t)TR * nb * sizeof(uint64_t);
   if (lds > lds_cap) return hipErrorInvalidValue;

@@ -295,6 +295,36 @@ def test_select_edges():
     assert np.all(g["ks"].cpu().numpy()[0, 0, 2] == 0)
 
 
+@pytest.mark.parametrize("case", ["all_equal", "two_values", "few_values", "wide_range"])
+def test_select_ties_and_ranges(case):
+    """Score rows with every key equal (no radix pass at all), two or a few
+    distinct values (ties straddling the k-th place) and a wide exponent
+    range (every pass): kept lists bit-exact."""
+    w = TINY.with_(grid=(2, 20, 64), head_dim=128)  # 2560 tokens, 40 blocks
+    x = qsa_gen.make_qkv(w)
+    rng = np.random.default_rng(3)
+    kv = oracle.bf16_to_f64(x["k"])
+    if case == "all_equal":
+        x["q"][:] = 0  # every score 0
+    elif case == "two_values":
+        blk = np.arange(w.seq_len) // 64
+        kv[:] = np.where((blk % 2 == 0)[None, None, :, None], 1.0, 2.0)
+        x["k"] = oracle.f64_to_bf16(kv)
+    elif case == "few_values":
+        blk = np.arange(w.seq_len) // 64
+        kv[:] = ((blk % 3) + 1.0)[None, None, :, None]
+        x["k"] = oracle.f64_to_bf16(kv)
+    else:
+        scale = 2.0 ** rng.integers(-12, 12, size=w.seq_len // 64)
+        kv *= np.repeat(scale, 64)[None, None, :, None]
+        x["k"] = oracle.f64_to_bf16(kv)
+    for topk, band in [(1, (0,)), (7, ()), (13, (0, 3)), (39, (0,))]:
+        o = oracle_front(x, w, topk=topk, band=band)
+        g = _gpu_front(x, w, topk, band, o["kmax"])
+        assert np.array_equal(g["cnt"].cpu().numpy(), o["cnt"]), (case, topk, band)
+        assert np.array_equal(g["idx"].cpu().numpy(), o["idx"]), (case, topk, band)
+
+
 def test_attention_edges():
     w, x, o, g = _setup("tail64_d128")
     v = dev_bf16(x["v"])
