@@ -684,6 +684,12 @@ __attribute__((amdgpu_waves_per_eu(2, 8))) void attn_kernel(AttnArgs a, int L, i
 
   if (!REFRESH) {
     if (!qvalid) return;
+    size_t orow_off = row_off;
+    if (a.out_map) {
+      const int w = a.out_w, m = L / a.out_w;
+      const int orow = a.out_map == 1 ? (qrow % w) * m + qrow / w : (qrow % m) * w + qrow / m;
+      orow_off = head_off + (size_t)orow * D;
+    }
 #pragma unroll
     for (int dt = 0; dt < C::DT; ++dt) {
 #pragma unroll
@@ -693,14 +699,14 @@ __attribute__((amdgpu_waves_per_eu(2, 8))) void attn_kernel(AttnArgs a, int L, i
 #pragma unroll
         for (int e = 0; e < 4; ++e) os[e] = acc.o[dt][4 * r4 + e] * inv_k;
         if (a.r_in) {
-          const float4 rv = load_bf16x4(a.r_in + row_off + d0);
+          const float4 rv = load_bf16x4(a.r_in + orow_off + d0);
           os[0] += rv.x; os[1] += rv.y; os[2] += rv.z; os[3] += rv.w;
         }
         if (a.dr_in) {
-          const float4 dv = load_bf16x4(a.dr_in + row_off + d0);
+          const float4 dv = load_bf16x4(a.dr_in + orow_off + d0);
           os[0] += dv.x; os[1] += dv.y; os[2] += dv.z; os[3] += dv.w;
         }
-        store_bf16x4(a.out + row_off + d0, os[0], os[1], os[2], os[3]);
+        store_bf16x4(a.out + orow_off + d0, os[0], os[1], os[2], os[3]);
       }
     }
     return;

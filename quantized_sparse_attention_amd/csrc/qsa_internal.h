@@ -57,6 +57,12 @@ hipError_t launch_quantize(const qsa_dims& d, const uint16_t* x, int8_t* codes, 
 hipError_t launch_quantize_rotated(const qsa_dims& d, const uint16_t* x, int8_t* codes,
                                    float* scales, int32_t* pooled, hipStream_t s);
 
+// qsa_quantize of the rows in position-major order of windows of `window`
+// tokens (row p*(L/window) + k is row k*window + p of x), gathered from x.
+hipError_t launch_quantize_position_major(const qsa_dims& d, const uint16_t* x, int window,
+                                          int8_t* codes, float* scales, int32_t* pooled,
+                                          hipStream_t s);
+
 hipError_t launch_select(const qsa_dims& d, const int32_t* pooled_q, const float* scale_q,
                          const int32_t* pooled_k, const float* scale_k, int32_t topk,
                          const Band& band, int32_t kmax, int32_t* kept_idx, int32_t* kept_cnt,
@@ -82,6 +88,12 @@ struct AttnArgs {
   uint16_t* dr_out;
   int32_t has_prev;
   uint16_t* out;
+  // sparse step only: where query row r's output (and r, dr) rows live.
+  // 0: row r; 1: row (r % out_w) * (L / out_w) + r / out_w (window-major to
+  // position-major); 2: row (r % m) * out_w + r / m with m = L / out_w (the
+  // inverse).  out_w must divide L.
+  int32_t out_map;
+  int32_t out_w;
 };
 
 hipError_t launch_sparse_attn(const qsa_dims& d, const AttnArgs& a, hipStream_t s);
@@ -116,7 +128,7 @@ struct SquadPlan {
   int kmax;
   uint64_t bytes;
   uint64_t q_codes, k_codes, q_scales, k_scales, q_pooled, k_pooled, kept_idx, kept_cnt;
-  uint64_t o_local, q_perm, k_perm, v_perm;
+  uint64_t o_local;
 };
 SquadPlan squad_plan(const qsa_dims& d, int window);
 hipError_t launch_window_kept(const qsa_dims& d, int window, int kmax, int32_t* kept_idx,

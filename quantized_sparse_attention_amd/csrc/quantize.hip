@@ -69,12 +69,15 @@ __device__ __forceinline__ void fwht_row(float (&v)[8], int lane) {
   }
 }
 
-template <int BS, int D, bool ROT>
+// MAP: the rows are quantised in position-major order of windows of w tokens
+// (row p*(L/w) + k of the quantised sequence is row k*w + p of x), read
+// straight from x.
+template <int BS, int D, bool ROT, bool MAP>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x,
                                                        int8_t* __restrict__ codes,
                                                        float* __restrict__ scales,
                                                        int32_t* __restrict__ pooled, int L,
-                                                       int nb) {
+                                                       int nb, int w) {
   constexpr int CPR = D / 8;        // 16-byte chunks per token row
   constexpr int RPP = 256 / CPR;    // rows covered per pass
   constexpr int PASSES = BS / RPP;  // passes over the block
@@ -92,7 +95,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   const int cc = tid % CPR;
   const int r0 = tid / CPR;
 
-  const uint16_t* xb = x + (bh * (uint64_t)L + (uint64_t)t0) * D + cc * 8;
+  const uint16_t* xh = x + bh * (uint64_t)L * D + cc * 8;
+  const int m = MAP ? L / w : 1;
   int8_t* cb = codes + (bh * (uint64_t)L + (uint64_t)t0) * D + cc * 8;
 
   float y[PASSES][8];
@@ -101,7 +105,11 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   for (int p = 0; p < PASSES; ++p) {
     const int row = r0 + p * RPP;
     uint4 raw = make_uint4(0, 0, 0, 0);
-    if (row < n) raw = *reinterpret_cast<const uint4*>(xb + (size_t)row * D);
+    if (row < n) {
+      const int r = t0 + row;
+      const int src = MAP ? (r % m) * w + r / m : r;
+      raw = *reinterpret_cast<const uint4*>(xh + (size_t)src * D);
+    }
     const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -159,38 +167,44 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   if (tid == 0) scales[blk] = s;
 }
 
-template <int BS, int D, bool ROT>
+template <int BS, int D, bool ROT, bool MAP>
 hipError_t launch_t(const qsa_dims& d, const uint16_t* x, int8_t* codes, float* scales,
-                    int32_t* pooled, hipStream_t s) {
+                    int32_t* pooled, int w, hipStream_t s) {
   const int nb = (d.seq_len + BS - 1) / BS;
   const uint64_t n_wg = (uint64_t)d.batch * d.heads * nb;
-  hipLaunchKernelGGL((quantize_kernel<BS, D, ROT>), dim3((uint32_t)n_wg), dim3(256), 0, s, x,
-                     codes, scales, pooled, d.seq_len, nb);
+  hipLaunchKernelGGL((quantize_kernel<BS, D, ROT, MAP>), dim3((uint32_t)n_wg), dim3(256), 0, s,
+                     x, codes, scales, pooled, d.seq_len, nb, w);
   return hipGetLastError();
 }
 
-template <bool ROT>
+template <bool ROT, bool MAP>
 hipError_t dispatch(const qsa_dims& d, const uint16_t* x, int8_t* codes, float* scales,
-                    int32_t* pooled, hipStream_t s) {
+                    int32_t* pooled, int w, hipStream_t s) {
   if (d.block == 64 && d.head_dim == 128)
-    return launch_t<64, 128, ROT>(d, x, codes, scales, pooled, s);
+    return launch_t<64, 128, ROT, MAP>(d, x, codes, scales, pooled, w, s);
   if (d.block == 64 && d.head_dim == 64)
-    return launch_t<64, 64, ROT>(d, x, codes, scales, pooled, s);
+    return launch_t<64, 64, ROT, MAP>(d, x, codes, scales, pooled, w, s);
   if (d.block == 128 && d.head_dim == 128)
-    return launch_t<128, 128, ROT>(d, x, codes, scales, pooled, s);
-  return launch_t<128, 64, ROT>(d, x, codes, scales, pooled, s);
+    return launch_t<128, 128, ROT, MAP>(d, x, codes, scales, pooled, w, s);
+  return launch_t<128, 64, ROT, MAP>(d, x, codes, scales, pooled, w, s);
 }
 
 }  // namespace
 
 hipError_t launch_quantize(const qsa_dims& d, const uint16_t* x, int8_t* codes, float* scales,
                            int32_t* pooled, hipStream_t s) {
-  return dispatch<false>(d, x, codes, scales, pooled, s);
+  return dispatch<false, false>(d, x, codes, scales, pooled, 1, s);
 }
 
 hipError_t launch_quantize_rotated(const qsa_dims& d, const uint16_t* x, int8_t* codes,
                                    float* scales, int32_t* pooled, hipStream_t s) {
-  return dispatch<true>(d, x, codes, scales, pooled, s);
+  return dispatch<true, false>(d, x, codes, scales, pooled, 1, s);
+}
+
+hipError_t launch_quantize_position_major(const qsa_dims& d, const uint16_t* x, int window,
+                                          int8_t* codes, float* scales, int32_t* pooled,
+                                          hipStream_t s) {
+  return dispatch<false, true>(d, x, codes, scales, pooled, window, s);
 }
 
 }  // namespace qsa

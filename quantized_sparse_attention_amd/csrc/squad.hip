@@ -12,7 +12,11 @@
 //
 // Kernels of their own: the kept lists of block-diagonal attention, and the
 // reorder between window-major and position-major order (a row gather of
-// 16-byte chunks, HBM-bound).
+// 16-byte chunks, HBM-bound; exported for callers that need it).  The
+// operator itself reorders nothing: the global pass quantises Q and K from
+// rows gathered in position-major order, the local pass writes its output
+// rows in position-major order and the global pass writes its rows back in
+// the natural order (row maps of the attention epilogue).
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -97,9 +101,6 @@ SquadPlan squad_plan(const qsa_dims& d, int window) {
   p.kept_idx = take(bh * nb * (uint64_t)p.kmax * 4);
   p.kept_cnt = take(bh * nb * 4);
   p.o_local = take(bh * n * D * 2);
-  p.q_perm = take(bh * n * D * 2);
-  p.k_perm = take(bh * n * D * 2);
-  p.v_perm = take(bh * n * D * 2);
   return p;
 }
 
@@ -116,9 +117,6 @@ hipError_t launch_squad(const qsa_dims& d, const uint16_t* q, const uint16_t* k,
   int32_t* idx = reinterpret_cast<int32_t*>(work + p.kept_idx);
   int32_t* cnt = reinterpret_cast<int32_t*>(work + p.kept_cnt);
   uint16_t* o_local = reinterpret_cast<uint16_t*>(work + p.o_local);
-  uint16_t* q_perm = reinterpret_cast<uint16_t*>(work + p.q_perm);
-  uint16_t* k_perm = reinterpret_cast<uint16_t*>(work + p.k_perm);
-  uint16_t* v_perm = reinterpret_cast<uint16_t*>(work + p.v_perm);
   const int m = d.seq_len / window;
 
   AttnArgs a{};
@@ -135,25 +133,26 @@ hipError_t launch_squad(const qsa_dims& d, const uint16_t* q, const uint16_t* k,
   hipError_t e;
 #define QSA_TRY(x) \
   if ((e = (x)) != hipSuccess) return e
-  // local pass: windows of w tokens, natural order, values V
+  // local pass: windows of w tokens, natural order, values V; its output
+  // rows are written in position-major order, ready as the global values
   QSA_TRY(launch_quantize(d, q, qc, qs, qp, s));
   QSA_TRY(launch_quantize(d, k, kc, ks, kp, s));
   QSA_TRY(launch_window_kept(d, window, p.kmax, idx, cnt, s));
   a.v = v;
   a.out = o_local;
+  a.out_map = 1;
+  a.out_w = window;
   QSA_TRY(launch_sparse_attn(d, a, s));
-  // global pass: groups of n/w tokens in position-major order, values the
-  // local output
-  QSA_TRY(launch_reorder(d, window, 0, q, q_perm, s));
-  QSA_TRY(launch_reorder(d, window, 0, k, k_perm, s));
-  QSA_TRY(launch_reorder(d, window, 0, o_local, v_perm, s));
-  QSA_TRY(launch_quantize(d, q_perm, qc, qs, qp, s));
-  QSA_TRY(launch_quantize(d, k_perm, kc, ks, kp, s));
+  // global pass: groups of n/w tokens in position-major order (Q and K
+  // quantised from rows gathered in that order), values the local output;
+  // its output rows are written back in the natural order
+  QSA_TRY(launch_quantize_position_major(d, q, window, qc, qs, qp, s));
+  QSA_TRY(launch_quantize_position_major(d, k, window, kc, ks, kp, s));
   QSA_TRY(launch_window_kept(d, m, p.kmax, idx, cnt, s));
-  a.v = v_perm;
-  a.out = q_perm;  // free once its codes are taken
+  a.v = o_local;
+  a.out = out;
+  a.out_map = 2;
   QSA_TRY(launch_sparse_attn(d, a, s));
-  QSA_TRY(launch_reorder(d, window, 1, q_perm, out, s));
 #undef QSA_TRY
   return hipSuccess;
 }
