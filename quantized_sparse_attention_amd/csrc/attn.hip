@@ -19,9 +19,11 @@
 //    Per tile the K codes [64 x D] int8 and V [64 x D] bf16 go HBM/L2 -> LDS
 //    with 16-byte direct-to-LDS loads (no register staging), rows
 //    XOR-swizzled at 16-byte granularity so the operand reads are free of
-//    bank conflicts.  Each wave copies its MFMA operands of the tile into
-//    registers right away, so the single LDS tile is refilled with the next
-//    tile while this one is computed;
+//    bank conflicts.  Either each wave copies its MFMA operands of the tile
+//    into registers right away, so the single LDS tile is refilled with the
+//    next tile while this one is computed, or (64-token blocks, D = 128) the
+//    tile has two LDS buffers and the operands are read where they are used,
+//    which frees the registers for a third wave per SIMD;
 //  * S^T = K_j . Q^T on v_mfma_i32_32x32x32_i8 (exact int32 dots);
 //  * logits z = (sm_scale * sq_i * sk_j * log2 e) * S and softmax in fp32
 //    with exp2.  The running max is computed on the first tile only; later
@@ -44,6 +46,15 @@
 
 #ifndef QSA_ATTN_QB
 #define QSA_ATTN_QB 2
+#endif
+// the sparse kernel of 64-token blocks and D = 128 walks with two LDS tile
+// buffers at three waves per SIMD (0: one buffer, operands copied to
+// registers, two waves per SIMD)
+#ifndef QSA_ATTN_JIT
+#define QSA_ATTN_JIT 1
+#endif
+#ifndef QSA_ATTN_JIT_WAVES
+#define QSA_ATTN_JIT_WAVES 3
 #endif
 
 namespace qsa {
@@ -548,6 +559,70 @@ __device__ __forceinline__ void walk(const Ctx<BS, D>& x, const v4i (&qb)[Cfg<BS
   }
 }
 
+#if QSA_ATTN_JIT
+// The walk with two LDS tile buffers and the MFMA operands read from LDS
+// right where they are used (no register copy of the tile): the registers
+// freed let three waves share a SIMD, which hides more of the gather and
+// dependency latency.  Tile n is computed from buffer n % 2 while tile n+1
+// loads into the other; one barrier per tile.
+template <int BS, int D, int NWV, typename Next>
+__device__ __forceinline__ void walk_jit(const Ctx<BS, D>& x, const v4i (&qb)[Cfg<BS, D>::KS],
+                                         const LaneOffs<BS, D>& lo, Acc<BS, D>& acc,
+                                         Next&& next) {
+  using C = Cfg<BS, D>;
+  auto dma = [&](int t, int buf) {
+    dma_tile<BS, D, NWV>(x.kc_h + (size_t)t * KT * D, x.v_h + (size_t)t * KT * D,
+                         x.s_k + buf * C::K_BYTES, x.s_v + buf * (C::V_BYTES / 2), x.wave,
+                         x.lane, KT);
+  };
+  bool keep = false;
+  int cur = next(keep);
+  if (cur < 0) return;
+  __syncthreads();  // both buffers are free
+  dma(cur, 0);
+  __builtin_amdgcn_s_waitcnt(0x0f70);
+  __syncthreads();
+  int buf = 0;
+  while (cur >= 0) {
+    cur = __builtin_amdgcn_readfirstlane(cur);
+    bool knext = false;
+    const int nxt = next(knext);
+    if (nxt >= 0) dma(nxt, buf ^ 1);  // every wave is done with that buffer
+    if (keep) {
+      const float cs = x.c0 * load_uniform(x.sk_h, cur / C::SUB);
+      const int8_t* lk = x.s_k + buf * C::K_BYTES;
+      const uint16_t* lv = x.s_v + buf * (C::V_BYTES / 2);
+      v16i s[C::NT];
+#pragma unroll
+      for (int t = 0; t < C::NT; ++t) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[t][r] = 0;
+#pragma unroll
+        for (int c = 0; c < C::KS; ++c)
+          s[t] = __builtin_amdgcn_mfma_i32_32x32x32_i8(
+              *reinterpret_cast<const v4i*>(lk + 32 * t * D + lo.k[c]), qb[c], s[t], 0, 0, 0);
+      }
+      uint32_t pk[C::NT][8];
+      softmax_update<BS, D, false>(acc, s, pk, qb, x.kc_h + (size_t)cur * KT * D, x.lane, cs,
+                                   KT);
+#pragma unroll
+      for (int st = 0; st < C::PS; ++st) {
+        const v8bf b = pk_operand<BS, D>(pk, st);
+#pragma unroll
+        for (int dt = 0; dt < C::DT; ++dt)
+          acc.o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_operand<BS, D>(lo, lv, st, dt),
+                                                              b, acc.o[dt], 0, 0, 0);
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // the next tile landed
+    __syncthreads();
+    cur = nxt;
+    keep = knext;
+    buf ^= 1;
+  }
+}
+#endif
+
 // The short last tile of the sequence (keys >= nvalid masked); every wave
 // loads its share, the waves whose query block keeps it compute it.
 template <int BS, int D, int NWV>
@@ -573,18 +648,26 @@ __device__ __forceinline__ void tail_tile(const Ctx<BS, D>& x, const v4i (&qb)[C
 // One workgroup per (batch*head, group of QB consecutive query blocks), with
 // BS/32 waves per query block.  The group walks the union of its blocks' kept
 // sets once, so a key tile kept by several of them is loaded once.
-// Register budget: the sparse kernel is held to two waves per SIMD (256 VGPRs,
-// all accumulators in architectural VGPRs, no AGPR round trips); the refresh
-// kernel carries two output accumulators and runs one wave per SIMD.
+// Register budget: two waves per SIMD (256 VGPRs, all accumulators in
+// architectural VGPRs, no AGPR round trips), except the sparse kernel of
+// 64-token blocks and D = 128, which takes the walk with two tile buffers and
+// three waves per SIMD (168 VGPRs) when QSA_ATTN_JIT is set: the kernel waits
+// on latency more than on any unit, and the third wave covers more of it.
+template <int BS, int D, bool REFRESH>
+struct JitWalk {
+  static constexpr bool on = QSA_ATTN_JIT && !REFRESH && BS == 64 && D == 128;
+};
+
 template <int BS, int D, int QB, bool REFRESH>
 __global__ __launch_bounds__((QB * BS / 32 * 64))
-__attribute__((amdgpu_waves_per_eu(2, 8))) void attn_kernel(AttnArgs a, int L, int nb,
-                                                                        uint32_t n_work) {
+__attribute__((amdgpu_waves_per_eu(JitWalk<BS, D, REFRESH>::on ? QSA_ATTN_JIT_WAVES : 2, 8))) void attn_kernel(
+    AttnArgs a, int L, int nb, uint32_t n_work) {
   using C = Cfg<BS, D>;
   constexpr int NWV = QB * C::WPB;  // waves in the workgroup
   constexpr int THREADS = 64 * NWV;
-  __shared__ __attribute__((aligned(1024))) int8_t s_k[C::K_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint16_t s_v[C::V_BYTES / 2];
+  constexpr int NBUF = JitWalk<BS, D, REFRESH>::on ? 2 : 1;
+  __shared__ __attribute__((aligned(1024))) int8_t s_k[NBUF * C::K_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint16_t s_v[NBUF * C::V_BYTES / 2];
   __shared__ uint32_t s_bits[QB][kMaxWords];
 
   const uint32_t ng = (uint32_t)((nb + QB - 1) / QB);
@@ -655,7 +738,12 @@ __attribute__((amdgpu_waves_per_eu(2, 8))) void attn_kernel(AttnArgs a, int L, i
   for (int phase = 0; phase < (REFRESH ? 2 : 1); ++phase) {
     BitWalk<QB, C::SUB> w;
     w.init(s_bits, nb, nq, myb, n_tiles, tail_t, phase == 1);
-    walk<BS, D, NWV>(x, qb, lo, acc, [&](bool& keep) { return w.next(keep); });
+#if QSA_ATTN_JIT
+    if constexpr (JitWalk<BS, D, REFRESH>::on)
+      walk_jit<BS, D, NWV>(x, qb, lo, acc, [&](bool& keep) { return w.next(keep); });
+    else
+#endif
+      walk<BS, D, NWV>(x, qb, lo, acc, [&](bool& keep) { return w.next(keep); });
     if (w.tail_hit) tail_tile<BS, D, NWV>(x, qb, lo, acc, tail_t, w.tail_keep);
     if (phase == 0) {
       const float lk = acc.l + __shfl_xor(acc.l, 32, 64);
