@@ -47,9 +47,9 @@
 #ifndef QSA_ATTN_QB
 #define QSA_ATTN_QB 2
 #endif
-// the sparse kernel of 64-token blocks and D = 128 walks with two LDS tile
-// buffers at three waves per SIMD (0: one buffer, operands copied to
-// registers, two waves per SIMD)
+// the kernels of 64-token blocks and D = 128 walk with two LDS tile buffers
+// at three waves per SIMD (0: one buffer, operands copied to registers, two
+// waves per SIMD)
 #ifndef QSA_ATTN_JIT
 #define QSA_ATTN_JIT 1
 #endif
@@ -649,13 +649,13 @@ __device__ __forceinline__ void tail_tile(const Ctx<BS, D>& x, const v4i (&qb)[C
 // BS/32 waves per query block.  The group walks the union of its blocks' kept
 // sets once, so a key tile kept by several of them is loaded once.
 // Register budget: two waves per SIMD (256 VGPRs, all accumulators in
-// architectural VGPRs, no AGPR round trips), except the sparse kernel of
-// 64-token blocks and D = 128, which takes the walk with two tile buffers and
-// three waves per SIMD (168 VGPRs) when QSA_ATTN_JIT is set: the kernel waits
-// on latency more than on any unit, and the third wave covers more of it.
+// architectural VGPRs, no AGPR round trips), except the kernels of 64-token
+// blocks and D = 128, which take the walk with two tile buffers and three
+// waves per SIMD (168 VGPRs) when QSA_ATTN_JIT is set: they wait on latency
+// more than on any unit, and the third wave covers more of it.
 template <int BS, int D, bool REFRESH>
 struct JitWalk {
-  static constexpr bool on = QSA_ATTN_JIT && !REFRESH && BS == 64 && D == 128;
+  static constexpr bool on = QSA_ATTN_JIT && BS == 64 && D == 128;
 };
 
 template <int BS, int D, int QB, bool REFRESH>
