@@ -424,6 +424,62 @@ __device__ __forceinline__ void build_kept_bits(uint32_t (*bits)[kMaxWords], con
   __syncthreads();
 }
 
+// The group's kept tiles as one ascending list in LDS, for groups of two
+// query blocks of 64 tokens: entry = tile | keep(block 0) << 14 | keep(block 1)
+// << 15 (tiles < 16384), without the short last tile, whose presence and keep
+// bits go to *tail (bit 0: in the union; bits 1, 2: kept by block 0, 1).  Built
+// once by wave 0 from the bitmaps; *count is the union size even when it
+// exceeds kSeqCap (then the list is incomplete and the bitmap walk is used).
+// Walking the list costs one LDS read and a few scalar instructions per tile,
+// where the bitmap walk scans and refills words with branches and waits.
+constexpr int kSeqCap = 480;
+
+__device__ __forceinline__ void build_seq(const uint32_t (*bits)[kMaxWords], int nb, int nq,
+                                          int tail_t, uint16_t* seq, int* count, int* tail,
+                                          int tid) {
+  if (tid >= 64) return;
+  const int lane = tid;
+  const int nw = (nb + 31) >> 5;
+  int base = 0, tl = 0;
+  for (int w0 = 0; w0 < nw; w0 += 64) {
+    const int w = w0 + lane;
+    uint32_t b0 = 0u, b1 = 0u;
+    if (w < nw) {
+      b0 = bits[0][w];
+      if (nq > 1) b1 = bits[1][w];
+    }
+    uint32_t u = b0 | b1;
+    if (tail_t >= 0 && (tail_t >> 5) == w) {
+      const int tb = tail_t & 31;
+      tl = (int)((u >> tb) & 1u) | (int)(((b0 >> tb) & 1u) << 1) | (int)(((b1 >> tb) & 1u) << 2);
+      u &= ~(1u << tb);
+    }
+    const int c = __popc(u);
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o, 64);
+      if (lane >= o) incl += v;
+    }
+    int pos = base + incl - c;
+    while (u) {
+      const int bit = __builtin_ctz(u);
+      u &= u - 1u;
+      if (pos < kSeqCap)
+        seq[pos] = (uint16_t)((w << 5) + bit) | (uint16_t)(((b0 >> bit) & 1u) << 14) |
+                   (uint16_t)(((b1 >> bit) & 1u) << 15);
+      ++pos;
+    }
+    base += __shfl(incl, 63, 64);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) tl |= __shfl_xor(tl, o, 64);
+  if (lane == 0) {
+    *count = base;
+    *tail = tl;
+  }
+}
+
 // Walk, in ascending order, over the 64-key tiles of the key blocks that at
 // least one query block of the group needs: the kept blocks (rest = false) or
 // the blocks outside the kept set (rest = true, the refresh step's other
@@ -669,6 +725,13 @@ __attribute__((amdgpu_waves_per_eu(JitWalk<BS, D, REFRESH>::on ? QSA_ATTN_JIT_WA
   __shared__ __attribute__((aligned(1024))) int8_t s_k[NBUF * C::K_BYTES];
   __shared__ __attribute__((aligned(1024))) uint16_t s_v[NBUF * C::V_BYTES / 2];
   __shared__ uint32_t s_bits[QB][kMaxWords];
+  // The sequence list and its size/tail word live in the bitmap words past
+  // the last used one (the bitmaps are sized for the largest block count), so
+  // the workgroup's LDS footprint, and with it the occupancy, is unchanged.
+  constexpr bool kSeq = JitWalk<BS, D, REFRESH>::on && QB == 2;
+  constexpr int kSeqWords = kSeqCap / 2;
+  uint16_t* s_seq = reinterpret_cast<uint16_t*>(&s_bits[QB - 1][kMaxWords - kSeqWords]);
+  int* s_seq_info = reinterpret_cast<int*>(&s_bits[0][kMaxWords - 2]);
 
   const uint32_t ng = (uint32_t)((nb + QB - 1) / QB);
   const uint32_t work = xcd_contiguous(blockIdx.x, n_work);
@@ -726,6 +789,14 @@ __attribute__((amdgpu_waves_per_eu(JitWalk<BS, D, REFRESH>::on ? QSA_ATTN_JIT_WA
   const int n_tiles = (L + KT - 1) / KT;
   const int tail_t = (L % KT) ? n_tiles - 1 : -1;
   const int myb = i < nb ? qsub : -1;
+  int seq_n = kSeqCap + 1;
+  if constexpr (kSeq) {
+    if (((nb + 31) >> 5) <= kMaxWords - kSeqWords) {
+      build_seq(s_bits, nb, nq, tail_t, s_seq, &s_seq_info[0], &s_seq_info[1], tid);
+      __syncthreads();
+      seq_n = __builtin_amdgcn_readfirstlane(s_seq_info[0]);
+    }
+  }
 
   // One online-softmax state.  It first runs over the kept blocks: that is
   // the sparse attention.  The refresh step parks the sparse output and then
@@ -739,12 +810,36 @@ __attribute__((amdgpu_waves_per_eu(JitWalk<BS, D, REFRESH>::on ? QSA_ATTN_JIT_WA
     BitWalk<QB, C::SUB> w;
     w.init(s_bits, nb, nq, myb, n_tiles, tail_t, phase == 1);
 #if QSA_ATTN_JIT
-    if constexpr (JitWalk<BS, D, REFRESH>::on)
-      walk_jit<BS, D, NWV>(x, qb, lo, acc, [&](bool& keep) { return w.next(keep); });
-    else
+    if constexpr (JitWalk<BS, D, REFRESH>::on) {
+      // kernels with the sequence list walk the kept tiles (phase 0) from it
+      // when they all fit; each entry is read one call ahead, so its LDS
+      // latency hides behind a whole tile
+      const bool use_seq = kSeq && phase == 0 && seq_n <= kSeqCap;
+      int n = 0;
+      uint32_t pre = use_seq && seq_n > 0 ? s_seq[0] : 0u;
+      const int kshift = 14 + (myb >= 0 ? myb : 0);
+      walk_jit<BS, D, NWV>(x, qb, lo, acc, [&](bool& keep) {
+        if (!use_seq) return w.next(keep);
+        if (n >= seq_n) return -1;
+        const uint32_t e = __builtin_amdgcn_readfirstlane(pre);
+        ++n;
+        pre = s_seq[n < seq_n ? n : 0];
+        keep = myb >= 0 && ((e >> kshift) & 1u);
+        return (int)(e & 0x3fffu);
+      });
+      bool th = w.tail_hit, tk = w.tail_keep;
+      if (use_seq) {
+        const int tb = __builtin_amdgcn_readfirstlane(s_seq_info[1]);
+        th = tb & 1;
+        tk = myb >= 0 && ((tb >> (1 + myb)) & 1);
+      }
+      if (th) tail_tile<BS, D, NWV>(x, qb, lo, acc, tail_t, tk);
+    } else
 #endif
+    {
       walk<BS, D, NWV>(x, qb, lo, acc, [&](bool& keep) { return w.next(keep); });
-    if (w.tail_hit) tail_tile<BS, D, NWV>(x, qb, lo, acc, tail_t, w.tail_keep);
+      if (w.tail_hit) tail_tile<BS, D, NWV>(x, qb, lo, acc, tail_t, w.tail_keep);
+    }
     if (phase == 0) {
       const float lk = acc.l + __shfl_xor(acc.l, 32, 64);
       inv_k = lk > 0.0f ? 1.0f / lk : 0.0f;
