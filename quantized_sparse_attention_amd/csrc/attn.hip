@@ -143,6 +143,48 @@ __device__ __forceinline__ void dma_tile(const int8_t* __restrict__ kt,
   }
 }
 
+// The same loads for whole tiles through buffer descriptors of the head's K
+// codes and V: each lane's byte offset inside a tile does not depend on the
+// tile, so it is computed once, and the tile enters as a scalar offset; the
+// tile loop then spends no vector instructions on addresses.
+template <int BS, int D, int NWV>
+struct BufDma {
+  using C = Cfg<BS, D>;
+  using M = Dma<D, NWV>;
+  __amdgpu_buffer_rsrc_t rk, rv;
+  uint32_t ok[M::K], ov[M::V];
+  __device__ __forceinline__ void init(const int8_t* kc_h, const uint16_t* v_h, int L, int wave,
+                                       int lane) {
+    // raw buffers (stride 0) of L rows; a descriptor word 3 of 0x00020000
+    // selects 32-bit untyped access on this architecture
+    rk = __builtin_amdgcn_make_buffer_rsrc((void*)kc_h, 0, L * D, 0x00020000);
+    rv = __builtin_amdgcn_make_buffer_rsrc((void*)v_h, 0, L * D * 2, 0x00020000);
+#pragma unroll
+    for (int n = 0; n < M::K; ++n) {
+      const int kb = wave * M::K + n;
+      const int row = kb * C::K_ROWS_PER_KB + lane / C::K_CPR;
+      ok[n] = (uint32_t)(row * D + (((lane % C::K_CPR) ^ kswz<D>(row)) << 4));
+    }
+#pragma unroll
+    for (int n = 0; n < M::V; ++n) {
+      const int kb = wave * M::V + n;
+      const int row = kb * C::V_ROWS_PER_KB + lane / C::V_CPR;
+      ov[n] = (uint32_t)(2 * (row * D + (((lane % C::V_CPR) ^ vswz<D>(row)) << 3)));
+    }
+  }
+  // all KT rows of tile t (t * KT + KT <= L)
+  __device__ __forceinline__ void tile(int t, int8_t* lk, uint16_t* lv, int wave) const {
+#pragma unroll
+    for (int n = 0; n < M::K; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(lk + (wave * M::K + n) * 1024),
+                                               16, ok[n], t * (KT * D), 0, 0);
+#pragma unroll
+    for (int n = 0; n < M::V; ++n)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(lv + (wave * M::V + n) * 512),
+                                               16, ov[n], t * (KT * D * 2), 0, 0);
+  }
+};
+
 // Per-lane LDS byte offsets of the MFMA operands (the swizzle of a lane's rows
 // does not depend on the tile, so these are computed once).
 template <int BS, int D>
@@ -626,10 +668,10 @@ __device__ __forceinline__ void walk_jit(const Ctx<BS, D>& x, const v4i (&qb)[Cf
                                          const LaneOffs<BS, D>& lo, Acc<BS, D>& acc,
                                          Next&& next) {
   using C = Cfg<BS, D>;
+  BufDma<BS, D, NWV> bd;
+  bd.init(x.kc_h, x.v_h, x.L, x.wave, x.lane);
   auto dma = [&](int t, int buf) {
-    dma_tile<BS, D, NWV>(x.kc_h + (size_t)t * KT * D, x.v_h + (size_t)t * KT * D,
-                         x.s_k + buf * C::K_BYTES, x.s_v + buf * (C::V_BYTES / 2), x.wave,
-                         x.lane, KT);
+    bd.tile(t, x.s_k + buf * C::K_BYTES, x.s_v + buf * (C::V_BYTES / 2), x.wave);
   };
   bool keep = false;
   int cur = next(keep);
