@@ -442,15 +442,17 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* p, float a, float b, floa
 
 // Kept sets of the query blocks of a workgroup as bitmaps over the key blocks,
 // in LDS: bit j of row b is set when key block j is in kept(i) of the group's
-// b-th query block i.  The tile walks below read them a 32-bit word at a time.
+// b-th query block i.  Row b holds words [b*nw, (b+1)*nw) of one array sized
+// for the largest block count (nw = words per row).  The tile walks below read
+// them a 32-bit word at a time.
 constexpr int kMaxWords = QSA_MAX_BLOCKS / 32;
 
 template <int QB, int THREADS, typename BlockAt>
-__device__ __forceinline__ void build_kept_bits(uint32_t (*bits)[kMaxWords], const AttnArgs& a,
+__device__ __forceinline__ void build_kept_bits(uint32_t* bits, const AttnArgs& a,
                                                 uint64_t row0, BlockAt&& block_at, int nq,
                                                 int nb, int tid) {
   const int nw = (nb + 31) >> 5;
-  for (int k = tid; k < QB * nw; k += THREADS) bits[k / nw][k % nw] = 0u;
+  for (int k = tid; k < QB * nw; k += THREADS) bits[k] = 0u;
   __syncthreads();
   for (int b = 0; b < nq; ++b) {
     const int blk = block_at(b);
@@ -460,35 +462,41 @@ __device__ __forceinline__ void build_kept_bits(uint32_t (*bits)[kMaxWords], con
     const int cnt = min(max(a.kept_cnt[row], 0), a.kmax);
     for (int p = tid; p < cnt; p += THREADS) {
       const int j = kl[p];
-      if (j >= 0 && j < nb) atomicOr(&bits[b][j >> 5], 1u << (j & 31));
+      if (j >= 0 && j < nb) atomicOr(&bits[b * nw + (j >> 5)], 1u << (j & 31));
     }
   }
   __syncthreads();
 }
 
-// The group's kept tiles as one ascending list in LDS, for groups of two
-// query blocks of 64 tokens: entry = tile | keep(block 0) << 14 | keep(block 1)
-// << 15 (tiles < 16384), without the short last tile, whose presence and keep
-// bits go to *tail (bit 0: in the union; bits 1, 2: kept by block 0, 1).  Built
-// once by wave 0 from the bitmaps; *count is the union size even when it
-// exceeds kSeqCap (then the list is incomplete and the bitmap walk is used).
+// The group's tiles of one phase as one ascending list in LDS, for groups of
+// two query blocks of 64 tokens: the kept tiles (rest = false) or the tiles
+// outside the kept sets (rest = true), each present when at least one block
+// needs it; entry = tile | needed(block 0) << 14 | needed(block 1) << 15
+// (tiles < 16384).  The short last tile is left out; its presence and need
+// bits go to info[1] (bit 0: present; bits 1, 2: needed by block 0, 1).
+// info[0] = the list length, also when it exceeds cap (then the list is
+// incomplete and the bitmap walk is used).  Built by wave 0 from the bitmaps.
 // Walking the list costs one LDS read and a few scalar instructions per tile,
 // where the bitmap walk scans and refills words with branches and waits.
-constexpr int kSeqCap = 480;
-
-__device__ __forceinline__ void build_seq(const uint32_t (*bits)[kMaxWords], int nb, int nq,
-                                          int tail_t, uint16_t* seq, int* count, int* tail,
+__device__ __forceinline__ void build_seq(const uint32_t* bits, int nb, int nq, int tail_t,
+                                          bool rest, uint16_t* seq, int cap, int* info,
                                           int tid) {
   if (tid >= 64) return;
   const int lane = tid;
   const int nw = (nb + 31) >> 5;
+  const int last_bits = nb - 32 * (nw - 1);
   int base = 0, tl = 0;
   for (int w0 = 0; w0 < nw; w0 += 64) {
     const int w = w0 + lane;
     uint32_t b0 = 0u, b1 = 0u;
     if (w < nw) {
-      b0 = bits[0][w];
-      if (nq > 1) b1 = bits[1][w];
+      b0 = bits[w];
+      if (nq > 1) b1 = bits[nw + w];
+      if (rest) {
+        const uint32_t valid = w == nw - 1 && last_bits < 32 ? (1u << last_bits) - 1u : ~0u;
+        b0 = ~b0 & valid;
+        b1 = nq > 1 ? ~b1 & valid : 0u;
+      }
     }
     uint32_t u = b0 | b1;
     if (tail_t >= 0 && (tail_t >> 5) == w) {
@@ -507,7 +515,7 @@ __device__ __forceinline__ void build_seq(const uint32_t (*bits)[kMaxWords], int
     while (u) {
       const int bit = __builtin_ctz(u);
       u &= u - 1u;
-      if (pos < kSeqCap)
+      if (pos < cap)
         seq[pos] = (uint16_t)((w << 5) + bit) | (uint16_t)(((b0 >> bit) & 1u) << 14) |
                    (uint16_t)(((b1 >> bit) & 1u) << 15);
       ++pos;
@@ -517,8 +525,8 @@ __device__ __forceinline__ void build_seq(const uint32_t (*bits)[kMaxWords], int
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) tl |= __shfl_xor(tl, o, 64);
   if (lane == 0) {
-    *count = base;
-    *tail = tl;
+    info[0] = base;
+    info[1] = tl;
   }
 }
 
@@ -530,13 +538,13 @@ __device__ __forceinline__ void build_seq(const uint32_t (*bits)[kMaxWords], int
 // tile of the sequence is not returned: tail_hit / tail_keep record it.
 template <int QB, int SUB>
 struct BitWalk {
-  const uint32_t (*bits)[kMaxWords];
+  const uint32_t* bits;
   int nw, nq, myb, n_tiles, tail_t, last_bits;
   int wi, base, j, sub;
   uint32_t u, mine;
   bool rest, kj, tail_hit, tail_keep;
 
-  __device__ __forceinline__ void init(const uint32_t (*b)[kMaxWords], int nb, int nq_, int myb_,
+  __device__ __forceinline__ void init(const uint32_t* b, int nb, int nq_, int myb_,
                                        int n_tiles_, int tail_t_, bool rest_) {
     bits = b;
     rest = rest_;
@@ -557,7 +565,7 @@ struct BitWalk {
     tail_keep = false;
   }
   __device__ __forceinline__ uint32_t row_word(int b, int w) const {
-    uint32_t v = bits[b][w];
+    uint32_t v = bits[b * nw + w];
     if (rest) {
       const uint32_t valid = w == nw - 1 && last_bits < 32 ? (1u << last_bits) - 1u : ~0u;
       v = ~v & valid;
@@ -766,14 +774,16 @@ __attribute__((amdgpu_waves_per_eu(JitWalk<BS, D, REFRESH>::on ? QSA_ATTN_JIT_WA
   constexpr int NBUF = JitWalk<BS, D, REFRESH>::on ? 2 : 1;
   __shared__ __attribute__((aligned(1024))) int8_t s_k[NBUF * C::K_BYTES];
   __shared__ __attribute__((aligned(1024))) uint16_t s_v[NBUF * C::V_BYTES / 2];
-  __shared__ uint32_t s_bits[QB][kMaxWords];
-  // The sequence list and its size/tail word live in the bitmap words past
-  // the last used one (the bitmaps are sized for the largest block count), so
-  // the workgroup's LDS footprint, and with it the occupancy, is unchanged.
+  __shared__ uint32_t s_bits[QB * kMaxWords];
+  // The tile list of the two-buffer walk and its length/tail words live in
+  // the bitmap array past the words the bitmaps use (it is sized for the
+  // largest block count), so the workgroup's LDS footprint, and with it the
+  // occupancy, is the same with or without the list.
   constexpr bool kSeq = JitWalk<BS, D, REFRESH>::on && QB == 2;
-  constexpr int kSeqWords = kSeqCap / 2;
-  uint16_t* s_seq = reinterpret_cast<uint16_t*>(&s_bits[QB - 1][kMaxWords - kSeqWords]);
-  int* s_seq_info = reinterpret_cast<int*>(&s_bits[0][kMaxWords - 2]);
+  const int nw_used = QB * ((nb + 31) >> 5);
+  int* s_seq_info = reinterpret_cast<int*>(&s_bits[nw_used]);
+  uint16_t* s_seq = reinterpret_cast<uint16_t*>(&s_bits[nw_used + 2]);
+  const int seq_cap = 2 * (QB * kMaxWords - nw_used - 2);
 
   const uint32_t ng = (uint32_t)((nb + QB - 1) / QB);
   const uint32_t work = xcd_contiguous(blockIdx.x, n_work);
@@ -831,14 +841,6 @@ __attribute__((amdgpu_waves_per_eu(JitWalk<BS, D, REFRESH>::on ? QSA_ATTN_JIT_WA
   const int n_tiles = (L + KT - 1) / KT;
   const int tail_t = (L % KT) ? n_tiles - 1 : -1;
   const int myb = i < nb ? qsub : -1;
-  int seq_n = kSeqCap + 1;
-  if constexpr (kSeq) {
-    if (((nb + 31) >> 5) <= kMaxWords - kSeqWords) {
-      build_seq(s_bits, nb, nq, tail_t, s_seq, &s_seq_info[0], &s_seq_info[1], tid);
-      __syncthreads();
-      seq_n = __builtin_amdgcn_readfirstlane(s_seq_info[0]);
-    }
-  }
 
   // One online-softmax state.  It first runs over the kept blocks: that is
   // the sparse attention.  The refresh step parks the sparse output and then
@@ -853,10 +855,17 @@ __attribute__((amdgpu_waves_per_eu(JitWalk<BS, D, REFRESH>::on ? QSA_ATTN_JIT_WA
     w.init(s_bits, nb, nq, myb, n_tiles, tail_t, phase == 1);
 #if QSA_ATTN_JIT
     if constexpr (JitWalk<BS, D, REFRESH>::on) {
-      // kernels with the sequence list walk the kept tiles (phase 0) from it
-      // when they all fit; each entry is read one call ahead, so its LDS
-      // latency hides behind a whole tile
-      const bool use_seq = kSeq && phase == 0 && seq_n <= kSeqCap;
+      // the phase's tiles from the list when they all fit (else the bitmap
+      // walk); each entry is read one call ahead, so its LDS latency hides
+      // behind a whole tile
+      int seq_n = seq_cap + 1;
+      if (kSeq && seq_cap > 0) {
+        if (phase > 0) __syncthreads();  // every wave is done with the last list
+        build_seq(s_bits, nb, nq, tail_t, phase == 1, s_seq, seq_cap, s_seq_info, tid);
+        __syncthreads();
+        seq_n = __builtin_amdgcn_readfirstlane(s_seq_info[0]);
+      }
+      const bool use_seq = seq_n <= seq_cap;
       int n = 0;
       uint32_t pre = use_seq && seq_n > 0 ? s_seq[0] : 0u;
       const int kshift = 14 + (myb >= 0 ? myb : 0);
