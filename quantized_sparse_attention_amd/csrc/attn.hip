@@ -23,7 +23,10 @@
 //    into registers right away, so the single LDS tile is refilled with the
 //    next tile while this one is computed, or (64-token blocks, D = 128) the
 //    tile has two LDS buffers and the operands are read where they are used,
-//    which frees the registers for a third wave per SIMD;
+//    which frees the registers for a third wave per SIMD.  That walk takes
+//    its tiles from a list built once per phase from the bitmaps (one LDS
+//    read per tile) and loads them through buffer descriptors of the head's
+//    K and V (the tile is a scalar offset; no vector address arithmetic);
 //  * S^T = K_j . Q^T on v_mfma_i32_32x32x32_i8 (exact int32 dots);
 //  * logits z = (sm_scale * sq_i * sk_j * log2 e) * S and softmax in fp32
 //    with exp2.  The running max is computed on the first tile only; later
@@ -39,9 +42,10 @@
 //    the V^T operand read from the row-major V tile with ds_read_b64_tr_b16;
 //  * the epilogue normalises, adds the cached residuals (sparse step) or
 //    forms the residuals (refresh step), and stores bf16.
-// The refresh step keeps two online-softmax states, one over the kept blocks
-// and one over the others, so full and sparse attention share every
-// exponential and MFMA; it merges them at the end like split-K attention.
+// The refresh step runs one online-softmax state over the kept blocks (the
+// sparse attention), parks that normalised output in its own output rows,
+// then continues the same state over every other block (the full
+// attention): the two share every exponential and MFMA of the kept tiles.
 #include "qsa_internal.h"
 
 #ifndef QSA_ATTN_QB
