@@ -21,8 +21,12 @@
 //     Jacobi method (Golub and Van Loan, Matrix Computations, §8.5:
 //     symmetric Schur rotations; parallel round-robin ordering, D/2 disjoint
 //     rotations per round, D-1 rounds per sweep) in fp32 with G and the
-//     eigenvector matrix in LDS.  Each thread issues all LDS reads of its
-//     items before any write, so LDS latency overlaps across items.
+//     eigenvector matrix in LDS.  A round computes its D/2 rotations, then
+//     updates A one 2x2 block (rows of one pair x columns of another) at a
+//     time -- the row and the column rotation of a block in one step, since
+//     the block's new values depend on its own old ones only -- and V by
+//     columns: two barriers per round.  Each thread issues all LDS reads of
+//     its items before any write, so LDS latency overlaps across items.
 //     Eigenvalues are ranked descending (ties: lower index).
 //  3. project_kernel: one lane per token row: c = x V_r, then x V_r V_r^T in
 //     fp32, rounded to bf16 in place.
@@ -163,7 +167,8 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(
   constexpr int NP = D / 2;        // disjoint rotations per round
   constexpr int IT = NP * D / T;   // (pair, row-or-column) items per thread
   constexpr int KS = T / D;        // pair stride between a thread's items
-  static_assert(IT * T == NP * D && KS * D == T, "item split");
+  constexpr int BI = NP * NP / T;  // 2x2 blocks of A per thread
+  static_assert(IT * T == NP * D && KS * D == T && BI * T == NP * NP, "item split");
   __shared__ float a[D * LD];
   __shared__ float v[D * LD];
   __shared__ Rot rot[NP];
@@ -227,46 +232,59 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(
         rot[tid] = Rot{c, sn, p, q};
       }
       __syncthreads();
-      Rot r[IT];
-#pragma unroll
-      for (int n = 0; n < IT; ++n) r[n] = rot[k0 + KS * n];
-      // rows: A <- J^T A (all reads of a pair's rows before its writes)
+      // A <- J^T A J one 2x2 block at a time: block (P, Q) holds rows p, q of
+      // pair P and columns r, s of pair Q, and its new values depend on its
+      // four old ones only (the round's pairs are disjoint), so the row and
+      // the column rotation of a block are one step with no barrier between.
+      // The rotated pair's off-diagonal entries are set to 0.
       {
-        float ap[IT], aq[IT];
+        float b4[BI][4];
+        Rot rp[BI], rq[BI];
 #pragma unroll
-        for (int n = 0; n < IT; ++n) {
-          ap[n] = a[r[n].p * LD + idx];
-          aq[n] = a[r[n].q * LD + idx];
+        for (int n = 0; n < BI; ++n) {
+          const int blk = tid + T * n;
+          rp[n] = rot[blk / NP];
+          rq[n] = rot[blk % NP];
+          b4[n][0] = a[rp[n].p * LD + rq[n].p];
+          b4[n][1] = a[rp[n].p * LD + rq[n].q];
+          b4[n][2] = a[rp[n].q * LD + rq[n].p];
+          b4[n][3] = a[rp[n].q * LD + rq[n].q];
         }
 #pragma unroll
-        for (int n = 0; n < IT; ++n) {
-          if (r[n].s == 0.0f) continue;
-          a[r[n].p * LD + idx] = r[n].c * ap[n] - r[n].s * aq[n];
-          a[r[n].q * LD + idx] = r[n].s * ap[n] + r[n].c * aq[n];
+        for (int n = 0; n < BI; ++n) {
+          if (rp[n].s == 0.0f && rq[n].s == 0.0f) continue;
+          const float cp = rp[n].c, sp = rp[n].s, cq = rq[n].c, sq = rq[n].s;
+          // rows: J_P^T
+          const float xpr = cp * b4[n][0] - sp * b4[n][2], xps = cp * b4[n][1] - sp * b4[n][3];
+          const float xqr = sp * b4[n][0] + cp * b4[n][2], xqs = sp * b4[n][1] + cp * b4[n][3];
+          // columns: J_Q
+          float ypr = cq * xpr - sq * xps, yps = sq * xpr + cq * xps;
+          float yqr = cq * xqr - sq * xqs, yqs = sq * xqr + cq * xqs;
+          if (rp[n].p == rq[n].p) {  // diagonal block: a_pq = a_qp = 0
+            yps = 0.0f;
+            yqr = 0.0f;
+          }
+          a[rp[n].p * LD + rq[n].p] = ypr;
+          a[rp[n].p * LD + rq[n].q] = yps;
+          a[rp[n].q * LD + rq[n].p] = yqr;
+          a[rp[n].q * LD + rq[n].q] = yqs;
         }
       }
-      __syncthreads();
-      // columns: A <- A J, V <- V J; the rotated pair's off-diagonal is 0
+      // V <- V J
       {
-        float ap[IT], aq[IT], vp[IT], vq[IT];
+        Rot r[IT];
+        float vp[IT], vq[IT];
 #pragma unroll
         for (int n = 0; n < IT; ++n) {
-          ap[n] = a[idx * LD + r[n].p];
-          aq[n] = a[idx * LD + r[n].q];
+          r[n] = rot[k0 + KS * n];
           vp[n] = v[idx * LD + r[n].p];
           vq[n] = v[idx * LD + r[n].q];
         }
 #pragma unroll
         for (int n = 0; n < IT; ++n) {
           if (r[n].s == 0.0f) continue;
-          const float c = r[n].c, sn = r[n].s;
-          float np_ = c * ap[n] - sn * aq[n], nq = sn * ap[n] + c * aq[n];
-          if (idx == r[n].p) nq = 0.0f;
-          if (idx == r[n].q) np_ = 0.0f;
-          a[idx * LD + r[n].p] = np_;
-          a[idx * LD + r[n].q] = nq;
-          v[idx * LD + r[n].p] = c * vp[n] - sn * vq[n];
-          v[idx * LD + r[n].q] = sn * vp[n] + c * vq[n];
+          v[idx * LD + r[n].p] = r[n].c * vp[n] - r[n].s * vq[n];
+          v[idx * LD + r[n].q] = r[n].s * vp[n] + r[n].c * vq[n];
         }
       }
       __syncthreads();
