@@ -28,8 +28,9 @@
 //     columns: two barriers per round.  Each thread issues all LDS reads of
 //     its items before any write, so LDS latency overlaps across items.
 //     Eigenvalues are ranked descending (ties: lower index).
-//  3. project_kernel: one lane per token row: c = x V_r, then x V_r V_r^T in
-//     fp32, rounded to bf16 in place.
+//  3. project_kernel: 32 token rows per wave on the bf16 MFMA: C^T = V_r^T X^T,
+//     then X V_r V_r^T = V_r C^T, with three-term bf16 splits of the basis and
+//     of the coefficients (fp32-level error), rounded to bf16 in place.
 #include "qsa_internal.h"
 
 namespace qsa {
@@ -325,63 +326,141 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(
 // 3. projection of every row onto the kept directions, in place
 // ---------------------------------------------------------------------------
 
+// On the bf16 MFMA, 32 token rows per wave:
+//   C^T [ranks x rows] = V_r^T . X^T   (A: basis rows from LDS; B: the rows of
+//                                       X, one 16-byte load per k-step)
+//   Xhat^T [D x rows]  = V_r . C^T     (A: basis from LDS; B: the C^T
+//                                       accumulator, in registers)
+// with fp32 accumulation.  The basis and the coefficients are each split into
+// three bf16 terms (hi + mid + lo: the residual of each rounding is exact in
+// fp32, so together they carry the fp32 value to ~2^-24 relative) and the six
+// products of the second stage above that size are summed, so the result
+// carries fp32-level error before its bf16 rounding.  The C^T accumulator
+// holds, in lane l, row l % 32 and ranks 8(r/4) + 4(l/32) + r%4 of register
+// r: read 8 registers at a time it is the B operand of a 16-rank k-step
+// whose rank slots are {4g + e, 8 + 4g + e} (g = l/32, e < 4), and the basis
+// operand takes its rank slots in that same order.
+constexpr int kProjWaves = 4;
+
+__device__ __forceinline__ void split3(float v, uint16_t (&t)[3]) {
+#pragma unroll
+  for (int s3 = 0; s3 < 3; ++s3) {
+    const uint32_t h = pack_bf16x2(v, 0.0f);
+    t[s3] = (uint16_t)(h & 0xffffu);
+    v -= bf16_lo(h);
+  }
+}
+
 template <int D, int RP>
-__global__ __launch_bounds__(kThreads) void project_kernel(uint16_t* __restrict__ x,
-                                                           const float* __restrict__ wbasis,
-                                                           int L) {
-  __shared__ __attribute__((aligned(16))) float s_b[D * RP];
+__global__ __launch_bounds__(64 * kProjWaves) void project_kernel(uint16_t* __restrict__ x,
+                                                                  const float* __restrict__ wbasis,
+                                                                  int L) {
+  constexpr int RPAD = RP < 32 ? 32 : RP;     // ranks of the first stage's tiles
+  constexpr int RT = RPAD / 32;               // first-stage rank tiles
+  constexpr int KS1 = D / 16;                 // first-stage k-steps (channels)
+  constexpr int KS2 = RP < 16 ? 1 : RP / 16;  // second-stage k-steps (ranks)
+  constexpr int DT = D / 32;                  // second-stage channel tiles
+  constexpr int VT_LD = D + 8;                // V^T rows in LDS (bf16), padded
+  constexpr int V_LD = RPAD + 4;              // V rows in LDS (bf16), padded
+  __shared__ __attribute__((aligned(16))) uint16_t s_vt[3][RPAD * VT_LD];
+  __shared__ __attribute__((aligned(16))) uint16_t s_v[3][D * V_LD];
+
   const uint64_t bh = blockIdx.y;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, l32 = lane & 31;
   const float* wb = wbasis + bh * (uint64_t)(D * RP);
-  for (int e = tid * 4; e < D * RP; e += kThreads * 4)
-    *reinterpret_cast<float4*>(&s_b[e]) = *reinterpret_cast<const float4*>(&wb[e]);
-  __syncthreads();
-
-  const int row = blockIdx.x * kThreads + tid;
-  if (row >= L) return;
-  uint16_t* xr = x + (bh * (uint64_t)L + row) * D;
-
-  float c[RP];
+  for (int e = tid; e < D * RPAD; e += 64 * kProjWaves) {
+    const int d = e / RPAD, k = e % RPAD;
+    uint16_t t[3];
+    split3(k < RP ? wb[d * RP + k] : 0.0f, t);
 #pragma unroll
-  for (int k = 0; k < RP; ++k) c[k] = 0.0f;
-#pragma unroll 1
-  for (int d0 = 0; d0 < D; d0 += 8) {
-    const uint4 raw = *reinterpret_cast<const uint4*>(xr + d0);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float xe = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
-      const float4* brow = reinterpret_cast<const float4*>(&s_b[(d0 + e) * RP]);
-#pragma unroll
-      for (int k4 = 0; k4 < RP / 4; ++k4) {
-        const float4 b = brow[k4];
-        c[4 * k4 + 0] = __builtin_fmaf(xe, b.x, c[4 * k4 + 0]);
-        c[4 * k4 + 1] = __builtin_fmaf(xe, b.y, c[4 * k4 + 1]);
-        c[4 * k4 + 2] = __builtin_fmaf(xe, b.z, c[4 * k4 + 2]);
-        c[4 * k4 + 3] = __builtin_fmaf(xe, b.w, c[4 * k4 + 3]);
-      }
+    for (int s3 = 0; s3 < 3; ++s3) {
+      s_vt[s3][k * VT_LD + d] = t[s3];
+      s_v[s3][d * V_LD + k] = t[s3];
     }
   }
-#pragma unroll 1
-  for (int d0 = 0; d0 < D; d0 += 8) {
-    float o[8];
+  __syncthreads();
+
+  const int row0 = (blockIdx.x * kProjWaves + wave) * 32;
+  if (row0 >= L) return;  // past the only barrier
+  // rows past the end re-read the last row and are not stored; that row
+  // belongs to this wave, whose reads all precede its stores
+  const int row = min(row0 + l32, L - 1);
+  uint16_t* xb = x + bh * (uint64_t)L * D;
+
+  v4i xo[KS1];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float4* brow = reinterpret_cast<const float4*>(&s_b[(d0 + e) * RP]);
-      float acc = 0.0f;
+  for (int ks = 0; ks < KS1; ++ks)
+    xo[ks] = *reinterpret_cast<const v4i*>(xb + (size_t)row * D + 16 * ks + 8 * g);
+  v16f ct[RT];
 #pragma unroll
-      for (int k4 = 0; k4 < RP / 4; ++k4) {
-        const float4 b = brow[k4];
-        acc = __builtin_fmaf(c[4 * k4 + 0], b.x, acc);
-        acc = __builtin_fmaf(c[4 * k4 + 1], b.y, acc);
-        acc = __builtin_fmaf(c[4 * k4 + 2], b.z, acc);
-        acc = __builtin_fmaf(c[4 * k4 + 3], b.w, acc);
+  for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) ct[rt][r] = 0.0f;
+#pragma unroll
+  for (int ks = 0; ks < KS1; ++ks) {
+    const v8bf b = __builtin_bit_cast(v8bf, xo[ks]);
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int s3 = 0; s3 < 3; ++s3) {
+        const v8bf a = *reinterpret_cast<const v8bf*>(
+            &s_vt[s3][(32 * rt + l32) * VT_LD + 16 * ks + 8 * g]);
+        ct[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, ct[rt], 0, 0, 0);
       }
-      o[e] = acc;
+  }
+
+  // coefficient splits as second-stage B operands: k-step ks2 takes
+  // registers 8 (ks2 % 2) .. +7 of rank tile ks2 / 2
+  uint32_t cb[3][KS2][4];
+#pragma unroll
+  for (int ks2 = 0; ks2 < KS2; ++ks2)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 8 * (ks2 & 1) + 2 * j;
+      float c0 = ct[ks2 >> 1][r], c1 = ct[ks2 >> 1][r + 1];
+#pragma unroll
+      for (int s3 = 0; s3 < 3; ++s3) {
+        const uint32_t h = pack_bf16x2(c0, c1);
+        cb[s3][ks2][j] = h;
+        c0 -= bf16_lo(h);
+        c1 -= bf16_hi(h);
+      }
     }
-    *reinterpret_cast<uint4*>(xr + d0) =
-        make_uint4(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]), pack_bf16x2(o[4], o[5]),
-                   pack_bf16x2(o[6], o[7]));
+
+  const bool store = row0 + l32 < L;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    v16f o;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[r] = 0.0f;
+#pragma unroll
+    for (int ks2 = 0; ks2 < KS2; ++ks2) {
+      v8bf a[3], b[3];
+#pragma unroll
+      for (int s3 = 0; s3 < 3; ++s3) {
+        const uint16_t* base = &s_v[s3][(32 * dt + l32) * V_LD + 16 * ks2 + 4 * g];
+        const uint2 lo4 = *reinterpret_cast<const uint2*>(base);
+        const uint2 hi4 = *reinterpret_cast<const uint2*>(base + 8);
+        a[s3] = __builtin_bit_cast(v8bf, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
+        b[s3] = __builtin_bit_cast(v8bf, make_uint4(cb[s3][ks2][0], cb[s3][ks2][1],
+                                                    cb[s3][ks2][2], cb[s3][ks2][3]));
+      }
+      // smallest products first
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[1], o, 0, 0, 0);
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[0], o, 0, 0, 0);
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[2], o, 0, 0, 0);
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[0], o, 0, 0, 0);
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[1], o, 0, 0, 0);
+      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[0], o, 0, 0, 0);
+    }
+    if (store) {
+      uint16_t* xr = xb + (size_t)(row0 + l32) * D + 32 * dt + 4 * g;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<uint2*>(xr + 8 * q) =
+            make_uint2(pack_bf16x2(o[4 * q], o[4 * q + 1]), pack_bf16x2(o[4 * q + 2], o[4 * q + 3]));
+    }
   }
 }
 
@@ -397,22 +476,23 @@ hipError_t launch_d(const qsa_dims& d, uint16_t* dr, int rank, float* basis, flo
   hipLaunchKernelGGL((jacobi_kernel<D>), dim3(bh), dim3(kJacobiThreads), 0, st, partial, pl.chunks,
                      rank, pl.rank_pad, eigvals, basis, wbasis);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const dim3 grid((uint32_t)((d.seq_len + kThreads - 1) / kThreads), bh);
+  const dim3 grid((uint32_t)((d.seq_len + 32 * kProjWaves - 1) / (32 * kProjWaves)), bh);
+  const dim3 block(64 * kProjWaves);
   switch (pl.rank_pad) {
     case 8:
-      hipLaunchKernelGGL((project_kernel<D, 8>), grid, dim3(kThreads), 0, st, dr, wbasis,
+      hipLaunchKernelGGL((project_kernel<D, 8>), grid, block, 0, st, dr, wbasis,
                          d.seq_len);
       break;
     case 16:
-      hipLaunchKernelGGL((project_kernel<D, 16>), grid, dim3(kThreads), 0, st, dr, wbasis,
+      hipLaunchKernelGGL((project_kernel<D, 16>), grid, block, 0, st, dr, wbasis,
                          d.seq_len);
       break;
     case 32:
-      hipLaunchKernelGGL((project_kernel<D, 32>), grid, dim3(kThreads), 0, st, dr, wbasis,
+      hipLaunchKernelGGL((project_kernel<D, 32>), grid, block, 0, st, dr, wbasis,
                          d.seq_len);
       break;
     default:
-      hipLaunchKernelGGL((project_kernel<D, 64>), grid, dim3(kThreads), 0, st, dr, wbasis,
+      hipLaunchKernelGGL((project_kernel<D, 64>), grid, block, 0, st, dr, wbasis,
                          d.seq_len);
       break;
   }
