@@ -434,32 +434,85 @@ def test_ordered_attention_is_identical(name):
     assert np.array_equal(host_bits(a), host_bits(b))
 
 
+def _match(ov):
+    """Mutual-best pairing (ov = block overlaps, saturated at 255): rounds in
+    which every single block picks the single block of largest overlap (ties:
+    the lower index) and two blocks that pick each other pair up; leftovers
+    pair in block order.  Returns partner[b] (-1: the single block)."""
+    n = len(ov)
+    ov = np.minimum(ov, 255)
+    partner = -np.ones(n, np.int64)
+    for _ in range(48):
+        alive = partner < 0
+        best = -np.ones(n, np.int64)
+        for t in np.nonzero(alive)[0]:
+            cand = np.nonzero(alive)[0]
+            cand = cand[cand != t]
+            if len(cand):
+                best[t] = cand[int(np.argmax(ov[t, cand]))]  # first maximum: lower index
+        made = False
+        for t in range(n):
+            u = best[t]
+            if alive[t] and u > t and best[u] == t:
+                partner[t], partner[u] = u, t
+                made = True
+        if not made:
+            break
+    pending = -1
+    for b in range(n):
+        if partner[b] >= 0:
+            continue
+        if pending < 0:
+            pending = b
+        else:
+            partner[pending], partner[b] = b, pending
+            pending = -1
+    return partner
+
+
+def _chain(S):
+    """Greedy chain from item 0 to the unused item of largest overlap (rows of
+    S are signatures), ties to the lowest index."""
+    M = S.astype(np.int64) @ S.T.astype(np.int64)
+    n = len(S)
+    used = np.zeros(n, bool)
+    cur, seq = 0, [0]
+    used[0] = True
+    for _ in range(n - 1):
+        cur = int(np.argmax(np.where(used, -1, M[cur])))  # first maximum: lowest index
+        used[cur] = True
+        seq.append(cur)
+    return seq
+
+
 def _reference_order(idx, cnt, nb, chunk=256, bits=256):
     """The documented processing order, restated in numpy: per chunk of 256
-    blocks a greedy chain from the chunk's first block, always to the unused
-    block of the chunk whose 256-bit signature (bit j mod 256 for key block
-    j) shares the most bits with the current one, ties to the lowest index."""
+    blocks, the blocks paired by mutual best partners on the overlaps of
+    256-bit signatures (bit j mod 256 for key block j), the pairs (indexed by
+    their lower block) ordered by a greedy chain over the signatures of their
+    unions, an odd chunk's single block last; chunks of at most two blocks
+    keep their order."""
     Bn, H = cnt.shape[:2]
     out = np.zeros((Bn, H, nb), np.int64)
     for b in range(Bn):
         for h in range(H):
             sig = np.zeros((nb, bits), bool)
             for i in range(nb):
-                js = [j for j in idx[b, h, i, :cnt[b, h, i]] if 0 <= j < nb]
-                sig[i, np.array(js, dtype=np.int64) % bits] = True
+                js = np.array([j for j in idx[b, h, i, :cnt[b, h, i]] if 0 <= j < nb],
+                              dtype=np.int64)
+                sig[i, js % bits] = True
             for c0 in range(0, nb, chunk):
                 n = min(chunk, nb - c0)
+                if n <= 2:
+                    out[b, h, c0:c0 + n] = c0 + np.arange(n)
+                    continue
                 S = sig[c0:c0 + n].astype(np.int64)
-                M = S @ S.T
-                used = np.zeros(n, bool)
-                cur = 0
-                used[0] = True
-                seq = [0]
-                for _ in range(n - 1):
-                    sc = np.where(used, -1, M[cur])
-                    cur = int(np.argmax(sc))  # first maximum: lowest index
-                    used[cur] = True
-                    seq.append(cur)
+                partner = _match(S @ S.T)
+                pairs = [(t, int(partner[t])) for t in range(n) if partner[t] > t]
+                seq = []
+                for k in _chain(np.array([S[p] | S[q] for p, q in pairs])):
+                    seq += list(pairs[k])
+                seq += [t for t in range(n) if partner[t] < 0]
                 out[b, h, c0:c0 + n] = c0 + np.array(seq)
     return out
 
@@ -467,7 +520,7 @@ def _reference_order(idx, cnt, nb, chunk=256, bits=256):
 @pytest.mark.parametrize("nb", [3, 257, 3000])
 def test_order_chunks(nb):
     """The order permutes each chunk of 256 consecutive blocks within itself,
-    starts every chunk with its first block, and changes no output bit."""
+    is the documented re-paired chain, and changes no output bit."""
     D, blk, H = 64, 64, 2
     L = nb * blk - 17  # a ragged last block
     gen = torch.Generator(device="cuda").manual_seed(nb)
@@ -484,7 +537,6 @@ def test_order_chunks(nb):
     o = order.cpu().numpy()
     for c0 in range(0, nb, 256):
         seg = o[..., c0:c0 + 256]
-        assert np.all(seg[..., 0] == c0)
         assert np.all(np.sort(seg, axis=-1) == np.arange(c0, min(nb, c0 + 256)))
     ref = _reference_order(idx.cpu().numpy(), cnt.cpu().numpy(), nb)
     assert np.array_equal(o, ref), "order differs from the documented greedy chain"
