@@ -64,6 +64,8 @@ def parse():
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_sparse_attn_wan14b_720p.json")
 ATTN_SOURCE = os.path.join(ROOT, "quantized_sparse_attention_amd", "csrc", "attn.hip")
+# the processing order decides which tiles neighbouring workgroups share
+ORDER_SOURCE = os.path.join(ROOT, "quantized_sparse_attention_amd", "csrc", "order.hip")
 
 
 def source_digest(path):
@@ -74,15 +76,16 @@ def source_digest(path):
 
 def measured_traffic(workload):
     """HBM bytes per launch of the sparse attention kernel from the committed
-    PMC record, or None when there is none for this workload or the kernel
-    source changed since the counters were taken."""
+    PMC record, or None when there is none for this workload or the kernel or
+    ordering source changed since the counters were taken."""
     try:
         with open(TRAFFIC_RECORD) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("workload") != workload or rec.get("attn_source_sha256") != source_digest(
-            ATTN_SOURCE):
+    if (rec.get("workload") != workload
+            or rec.get("attn_source_sha256") != source_digest(ATTN_SOURCE)
+            or rec.get("order_source_sha256") != source_digest(ORDER_SOURCE)):
         return None
     return rec.get("traffic_bytes_per_launch")
 
