@@ -256,7 +256,7 @@ def main():
     def layer_step(s, kind, rec):
         x = inputs[s]
         idx, cnt = kept[s]
-        e = [ev() for _ in range(8)]
+        e = [ev() for _ in range(9)]
         projected = False
         e[0].record(stream)
         quant(x["q"], bs, qc, qs, qp)
@@ -265,8 +265,10 @@ def main():
         Bn.qsa_select_blocks(qp, qs, kp, ks, L, bs, w.topk, w.band, kmax, idx, cnt)
         e[2].record(stream)
         if kind == "F":
+            Bn.qsa_order_query_blocks(idx, cnt, L, bs, D, order)
+            e[8].record(stream)
             Bn.qsa_full_attn_residual(qc, qs, kc, ks, x["v"], idx, cnt, bs, r, dr,
-                                      state["has_prev"], sm, out_full=out)
+                                      state["has_prev"], sm, out_full=out, order=order)
             e[4].record(stream)
             projected = args.rank is not None and state["has_prev"]
             if projected:
@@ -316,7 +318,8 @@ def main():
             t_order.append(e[2].elapsed_time(e[4]))
             t_sparse.append(e[4].elapsed_time(e[3]))  # the attention launch alone
         else:
-            t_full.append(e[2].elapsed_time(e[4]))
+            t_order.append(e[2].elapsed_time(e[8]))
+            t_full.append(e[8].elapsed_time(e[4]))  # the refresh launch alone
             if projected:
                 t_proj.append(e[4].elapsed_time(e[5]))
         (step_sp if kind == "S" else step_f).append(e[0].elapsed_time(e[3]))

@@ -178,15 +178,23 @@ int qsa_sparse_attn(const qsa_dims* dims, const int8_t* q_codes, const float* q_
 
 /*
  * qsa_order_query_blocks -- a processing order of the query blocks of every
- * (b, h) for qsa_sparse_attn_ordered.  Sparse attention gathers the key tiles
- * of each query block's kept set (technical summary §1); blocks whose kept
- * sets overlap can share those loads (in one workgroup and in one XCD's L2).
- * The order puts such blocks next to each other.  The blocks of each (b, h)
- * are cut into chunks of 256 consecutive blocks; each chunk is ordered by a
- * greedy chain from its first block that always continues with the unused
- * block of the chunk whose kept set shares the most bits with the current one
- * in a 256-bit signature (bit j mod 256 for key block j), ties to the lowest
- * index.  Chunks keep their natural order.  Deterministic.
+ * (b, h) for qsa_sparse_attn_ordered and qsa_full_attn_residual_ordered.
+ * Sparse attention gathers the key tiles of each query block's kept set
+ * (technical summary §1); blocks whose kept sets overlap can share those
+ * loads: positions 2k and 2k+1 of the order go to one workgroup, which walks
+ * the union of the two kept sets, and neighbouring workgroups run together
+ * on one XCD.  The blocks of each (b, h) are cut into chunks of 256
+ * consecutive blocks.  Kept sets are compared through 256-bit signatures
+ * (bit j mod 256 for key block j).  In each chunk the blocks are paired by
+ * rounds of mutual best partners: every single block picks the single block
+ * of largest signature overlap (saturated at 255; ties to the lower index)
+ * and two blocks that pick each other pair up (blocks still single after 48
+ * rounds pair in block order).  The pairs, indexed by their lower block, are
+ * then ordered by a greedy chain from pair 0 that always continues with the
+ * unused pair whose union signature shares the most bits with the current
+ * one (ties to the lower pair index); an odd chunk's single block goes last.
+ * Chunks of at most two blocks keep their order; chunks keep their natural
+ * order.  Deterministic.
  *
  *   kept_idx, kept_cnt in: as for qsa_sparse_attn (row stride kmax)
  *   order             out: int32 [B,H,nb], a permutation of 0..nb-1 per (b, h)
@@ -234,6 +242,29 @@ int qsa_full_attn_residual(const qsa_dims* dims, const int8_t* q_codes, const fl
                            const int32_t* kept_idx, const int32_t* kept_cnt, int32_t kmax,
                            float sm_scale, int32_t has_prev, uint16_t* r, uint16_t* dr,
                            uint16_t* out_full, void* stream);
+
+/*
+ * qsa_full_attn_residual_ordered -- qsa_full_attn_residual with the query
+ * blocks of each (b, h) processed in the given order (a permutation,
+ * normally from qsa_order_query_blocks).  Every block's two passes (kept
+ * blocks, then the others) run over its own tiles in ascending order with the
+ * same arithmetic, so r, dr and out_full are bit-identical to
+ * qsa_full_attn_residual's; blocks whose kept sets overlap share more tile
+ * loads (the workgroup's walks are the unions of its blocks' kept sets and of
+ * their complements).
+ *
+ *   order in: int32 [B,H,nb], a permutation of 0..nb-1 per (b, h).  Entries
+ *             outside [0, nb) are skipped; the rows of a block that the order
+ *             does not list are left unwritten in r, dr and out_full.
+ *   other arguments as qsa_full_attn_residual.
+ */
+int qsa_full_attn_residual_ordered(const qsa_dims* dims, const int8_t* q_codes,
+                                   const float* q_scales, const int8_t* k_codes,
+                                   const float* k_scales, const uint16_t* v,
+                                   const int32_t* kept_idx, const int32_t* kept_cnt,
+                                   int32_t kmax, const int32_t* order, float sm_scale,
+                                   int32_t has_prev, uint16_t* r, uint16_t* dr,
+                                   uint16_t* out_full, void* stream);
 
 /*
  * qsa_apply_residual -- standalone sparse-step correction (technical summary

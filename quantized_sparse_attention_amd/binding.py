@@ -34,7 +34,7 @@ EXPORTED = ("qsa_quantize", "qsa_select_blocks", "qsa_sparse_attn", "qsa_full_at
             "qsa_apply_residual", "qsa_order_query_blocks", "qsa_sparse_attn_ordered",
             "qsa_quantize_rotated", "qsa_project_residual", "qsa_project_work_bytes",
             "qsa_l1_change", "qsa_window_kept", "qsa_reorder_windows", "qsa_squad_attention",
-            "qsa_squad_work_bytes",
+            "qsa_squad_work_bytes", "qsa_full_attn_residual_ordered",
             "qsa_status_string", "qsa_last_error_detail", "qsa_version")
 
 
@@ -72,6 +72,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.qsa_sparse_attn.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp]
     lib.qsa_full_attn_residual.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, i32, f32, i32, vp, vp,
                                            vp, vp]
+    lib.qsa_full_attn_residual_ordered.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, i32, vp, f32,
+                                                   i32, vp, vp, vp, vp]
     lib.qsa_apply_residual.argtypes = [pd, vp, vp, vp, vp, vp]
     lib.qsa_order_query_blocks.argtypes = [pd, vp, vp, i32, vp, vp]
     lib.qsa_sparse_attn_ordered.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, i32, vp, f32, vp, vp,
@@ -88,7 +90,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     for f in ("qsa_quantize", "qsa_quantize_rotated", "qsa_select_blocks", "qsa_sparse_attn",
               "qsa_full_attn_residual", "qsa_apply_residual", "qsa_order_query_blocks",
               "qsa_sparse_attn_ordered", "qsa_project_residual", "qsa_l1_change",
-              "qsa_window_kept", "qsa_reorder_windows", "qsa_squad_attention"):
+              "qsa_window_kept", "qsa_reorder_windows", "qsa_squad_attention",
+              "qsa_full_attn_residual_ordered"):
         getattr(lib, f).restype = ctypes.c_int
     lib.qsa_status_string.argtypes = [ctypes.c_int]
     lib.qsa_status_string.restype = ctypes.c_char_p
@@ -279,8 +282,10 @@ def qsa_sparse_attn_ordered(q_codes, q_scales, k_codes, k_scales, v, kept_idx, k
 
 def qsa_full_attn_residual(q_codes, q_scales, k_codes, k_scales, v, kept_idx, kept_cnt,
                            block: int, r, dr, has_prev: bool, sm_scale: float | None = None,
-                           out_full=None, stream=None):
-    """Refresh step: full attention output; r (in/out) and dr (out) updated in place."""
+                           out_full=None, stream=None, order=None):
+    """Refresh step: full attention output; r (in/out) and dr (out) updated in place.
+    With ``order`` (int32 [B,H,nb], e.g. from qsa_order_query_blocks) the query
+    blocks are processed in that order (qsa_full_attn_residual_ordered)."""
     B, H, L, D, kmax = _attn_checks(q_codes, q_scales, k_codes, k_scales, v, kept_idx, kept_cnt,
                                     block)
     _need(r, "r", torch.bfloat16, (B, H, L, D))
@@ -289,10 +294,18 @@ def qsa_full_attn_residual(q_codes, q_scales, k_codes, k_scales, v, kept_idx, ke
     _need(out_full, "out_full", torch.bfloat16, (B, H, L, D))
     sm = default_sm_scale(D) if sm_scale is None else float(sm_scale)
     d = make_dims(B, H, L, D, block)
-    _check(load_library().qsa_full_attn_residual(
-        ctypes.byref(d), _ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales), _ptr(v),
-        _ptr(kept_idx), _ptr(kept_cnt), int(kmax), ctypes.c_float(sm), int(bool(has_prev)),
-        _ptr(r), _ptr(dr), _ptr(out_full), _stream(stream)))
+    lib = load_library()
+    if order is None:
+        _check(lib.qsa_full_attn_residual(
+            ctypes.byref(d), _ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales),
+            _ptr(v), _ptr(kept_idx), _ptr(kept_cnt), int(kmax), ctypes.c_float(sm),
+            int(bool(has_prev)), _ptr(r), _ptr(dr), _ptr(out_full), _stream(stream)))
+    else:
+        _need(order, "order", torch.int32, (B, H, kept_cnt.shape[-1]))
+        _check(lib.qsa_full_attn_residual_ordered(
+            ctypes.byref(d), _ptr(q_codes), _ptr(q_scales), _ptr(k_codes), _ptr(k_scales),
+            _ptr(v), _ptr(kept_idx), _ptr(kept_cnt), int(kmax), _ptr(order), ctypes.c_float(sm),
+            int(bool(has_prev)), _ptr(r), _ptr(dr), _ptr(out_full), _stream(stream)))
     return out_full
 
 

@@ -288,12 +288,12 @@ int qsa_sparse_attn_ordered(const qsa_dims* dims, const int8_t* q_codes, const f
   return launched(fn, qsa::launch_sparse_attn(*dims, a, static_cast<hipStream_t>(stream)));
 }
 
-int qsa_full_attn_residual(const qsa_dims* dims, const int8_t* q_codes, const float* q_scales,
-                           const int8_t* k_codes, const float* k_scales, const uint16_t* v,
-                           const int32_t* kept_idx, const int32_t* kept_cnt, int32_t kmax,
-                           float sm_scale, int32_t has_prev, uint16_t* r, uint16_t* dr,
-                           uint16_t* out_full, void* stream) {
-  const char* fn = "qsa_full_attn_residual";
+namespace {
+int full_attn_residual(const char* fn, const qsa_dims* dims, const int8_t* q_codes,
+                       const float* q_scales, const int8_t* k_codes, const float* k_scales,
+                       const uint16_t* v, const int32_t* kept_idx, const int32_t* kept_cnt,
+                       int32_t kmax, const int32_t* order, float sm_scale, int32_t has_prev,
+                       uint16_t* r, uint16_t* dr, uint16_t* out_full, void* stream) {
   int st = check_attn_common(fn, dims, q_codes, q_scales, k_codes, k_scales, v, kept_idx,
                              kept_cnt, kmax, sm_scale);
   if (st) return st;
@@ -311,6 +311,7 @@ int qsa_full_attn_residual(const qsa_dims* dims, const int8_t* q_codes, const fl
   a.v = v;
   a.kept_idx = kept_idx;
   a.kept_cnt = kept_cnt;
+  a.order = order;
   a.kmax = kmax;
   a.sm_scale = sm_scale;
   a.r_out = r;
@@ -319,6 +320,30 @@ int qsa_full_attn_residual(const qsa_dims* dims, const int8_t* q_codes, const fl
   a.out = out_full;
   (void)hipGetLastError();
   return launched(fn, qsa::launch_full_attn_residual(*dims, a, static_cast<hipStream_t>(stream)));
+}
+}  // namespace
+
+int qsa_full_attn_residual(const qsa_dims* dims, const int8_t* q_codes, const float* q_scales,
+                           const int8_t* k_codes, const float* k_scales, const uint16_t* v,
+                           const int32_t* kept_idx, const int32_t* kept_cnt, int32_t kmax,
+                           float sm_scale, int32_t has_prev, uint16_t* r, uint16_t* dr,
+                           uint16_t* out_full, void* stream) {
+  return full_attn_residual("qsa_full_attn_residual", dims, q_codes, q_scales, k_codes,
+                            k_scales, v, kept_idx, kept_cnt, kmax, nullptr, sm_scale, has_prev,
+                            r, dr, out_full, stream);
+}
+
+int qsa_full_attn_residual_ordered(const qsa_dims* dims, const int8_t* q_codes,
+                                   const float* q_scales, const int8_t* k_codes,
+                                   const float* k_scales, const uint16_t* v,
+                                   const int32_t* kept_idx, const int32_t* kept_cnt,
+                                   int32_t kmax, const int32_t* order, float sm_scale,
+                                   int32_t has_prev, uint16_t* r, uint16_t* dr,
+                                   uint16_t* out_full, void* stream) {
+  const char* fn = "qsa_full_attn_residual_ordered";
+  REQUIRE_PTR(order);
+  return full_attn_residual(fn, dims, q_codes, q_scales, k_codes, k_scales, v, kept_idx,
+                            kept_cnt, kmax, order, sm_scale, has_prev, r, dr, out_full, stream);
 }
 
 int qsa_apply_residual(const qsa_dims* dims, const uint16_t* sparse_out, const uint16_t* r,

@@ -148,8 +148,10 @@ class QuantSparseAttention:
             if self.r is None:
                 self.r = torch.zeros_like(v)
                 self.dr = torch.zeros_like(v)
+            order = (B.qsa_order_query_blocks(idx, cnt, q.shape[2], c.block, q.shape[3])
+                     if c.reorder else None)
             out = B.qsa_full_attn_residual(qc, qs, kc, ks, v, idx, cnt, c.block, self.r, self.dr,
-                                           self.has_prev, sm)
+                                           self.has_prev, sm, order=order)
             if c.rank is not None and self.has_prev:
                 Bn, H, L, D = v.shape
                 need = B.qsa_project_work_bytes(Bn, H, L, D, c.rank)

@@ -104,6 +104,8 @@ def test_valid_arguments_reach_the_device_check(lib):
     assert lib.qsa_order_query_blocks(_d(), P[0], P[1], 2, P[2], None) == B.QSA_ERR_DEVICE
     assert lib.qsa_sparse_attn_ordered(_d(), *P[:7], 2, P[8], ctypes.c_float(0.125), None, None,
                                        P[7], None) == B.QSA_ERR_DEVICE
+    assert lib.qsa_full_attn_residual_ordered(_d(), *P[:7], 2, P[10], ctypes.c_float(0.125), 1,
+                                              P[7], P[8], P[9], None) == B.QSA_ERR_DEVICE
 
 
 def _sel(lib, topk=1, band=(0,), n_band=None, kmax=2, dims=None, ptrs=None):
@@ -153,6 +155,14 @@ def test_attention_validation(lib):
                                        None) == B.QSA_ERR_NULL
     assert lib.qsa_sparse_attn_ordered(_d(), *P[:7], 2, P[8], f(0.0), None, None, P[7],
                                        None) == B.QSA_ERR_PARAM
+    assert lib.qsa_full_attn_residual_ordered(_d(), *P[:7], 2, None, f(0.1), 0, P[7], P[8],
+                                              P[9], None) == B.QSA_ERR_NULL
+    assert lib.qsa_full_attn_residual_ordered(_d(), *P[:7], 2, ctypes.c_void_p(0x3004), f(0.1),
+                                              0, P[7], P[8], P[9], None) == B.QSA_ERR_ALIGN
+    assert lib.qsa_full_attn_residual_ordered(_d(), *P[:7], 2, P[10], f(0.1), 2, P[7], P[8],
+                                              P[9], None) == B.QSA_ERR_PARAM
+    assert lib.qsa_full_attn_residual_ordered(_d(), *P[:7], 2, P[10], f(0.1), 0, None, P[8],
+                                              P[9], None) == B.QSA_ERR_NULL
     assert lib.qsa_order_query_blocks(_d(), P[0], P[1], 0, P[2], None) == B.QSA_ERR_PARAM
     assert lib.qsa_order_query_blocks(_d(), P[0], None, 2, P[2], None) == B.QSA_ERR_NULL
     assert lib.qsa_order_query_blocks(_d(), P[0], P[1], 2, ctypes.c_void_p(0x3004),

@@ -434,6 +434,31 @@ def test_ordered_attention_is_identical(name):
     assert np.array_equal(host_bits(a), host_bits(b))
 
 
+@pytest.mark.parametrize("name", list(CFGS))
+@pytest.mark.parametrize("has_prev", [0, 1])
+def test_ordered_refresh_is_identical(name, has_prev):
+    """A refresh step over the query blocks in the computed order (and in its
+    reverse) writes the same full output, r and dr, bit for bit."""
+    w, x, o, g = _setup(name)
+    v = dev_bf16(x["v"])
+    order = B.qsa_order_query_blocks(g["idx"], g["cnt"], w.seq_len, w.block, w.head_dim)
+    rev = torch.flip(order, dims=[-1]).contiguous()
+    rng = np.random.default_rng(5)
+    r_prev = dev_bf16(qsa_gen.f32_to_bf16_bits(
+        rng.standard_normal(x["v"].shape).astype(np.float32) * 0.02))
+    outs = []
+    for od in (None, order, rev):
+        r = r_prev.clone()
+        dr = torch.zeros_like(v)
+        full = B.qsa_full_attn_residual(g["qc"], g["qs"], g["kc"], g["ks"], v, g["idx"], g["cnt"],
+                                        w.block, r, dr, has_prev, order=od)
+        torch.cuda.synchronize()
+        outs.append([host_bits(t) for t in (full, r, dr)])
+    for got in outs[1:]:
+        for a, b, nm in zip(outs[0], got, ("full", "r", "dr")):
+            assert np.array_equal(a, b), f"{name} has_prev={has_prev}: {nm} differs"
+
+
 def _match(ov):
     """Mutual-best pairing (ov = block overlaps, saturated at 255): rounds in
     which every single block picks the single block of largest overlap (ties:
