@@ -43,33 +43,57 @@ __device__ __forceinline__ uint64_t order_key(double score) {
   return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
 }
 
-// Digits of 16 consecutive pooled sums, packed 4 per 32-bit word.
-__device__ __forceinline__ void split16(const int32_t* __restrict__ p, bool valid, v4i& hi,
-                                        v4i& lo) {
+// Digits of 16 consecutive pooled sums (four int4 loads; all zero for a
+// column past the last block), packed 4 per 32-bit word.
+__device__ __forceinline__ void split16(const int4 (&raw)[4], bool valid, v4i& hi, v4i& lo) {
 #pragma unroll
   for (int w = 0; w < 4; ++w) {
     uint32_t h = 0, l = 0;
-    if (valid) {
-      const int4 v = *reinterpret_cast<const int4*>(p + 4 * w);
-      const int vv[4] = {v.x, v.y, v.z, v.w};
+    const int vv[4] = {raw[w].x, raw[w].y, raw[w].z, raw[w].w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int hv = vv[e] >> 7;   // floor division by 128
-        const int lv = vv[e] & 127;  // remainder in [0, 127]
-        h |= (uint32_t)(hv & 0xff) << (8 * e);
-        l |= (uint32_t)lv << (8 * e);
-      }
+    for (int e = 0; e < 4; ++e) {
+      const int hv = vv[e] >> 7;   // floor division by 128
+      const int lv = vv[e] & 127;  // remainder in [0, 127]
+      h |= (uint32_t)(hv & 0xff) << (8 * e);
+      l |= (uint32_t)lv << (8 * e);
     }
-    hi[w] = (int)h;
-    lo[w] = (int)l;
+    hi[w] = valid ? (int)h : 0;
+    lo[w] = valid ? (int)l : 0;
   }
+}
+
+template <int KSTEPS>
+__device__ __forceinline__ void load16(const int32_t* __restrict__ p, int4 (&raw)[KSTEPS][4]) {
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) raw[ks][w] = *reinterpret_cast<const int4*>(p + ks * 64 + 4 * w);
 }
 
 __device__ __forceinline__ uint64_t lanemask_lt(int lane) {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-template <int D>
+// Calls f(j, valid, key) for the keys of one row in ascending chunks of 64
+// (lane l takes j = base + l; every lane of the wave takes part in every
+// chunk).  NPL > 0: the lane's keys are in registers kr[e] (j = 64e + lane,
+// nb <= 64 * NPL); NPL == 0: they are read from the row in LDS.
+template <int NPL, typename F>
+__device__ __forceinline__ void each_key(const uint64_t* keys, const uint64_t (&kr)[NPL > 0 ? NPL : 1],
+                                         int nb, int lane, F&& f) {
+  if constexpr (NPL > 0) {
+#pragma unroll
+    for (int e = 0; e < NPL; ++e)
+      if (64 * e < nb) f(64 * e + lane, 64 * e + lane < nb, kr[e]);
+  } else {
+    for (int base = 0; base < nb; base += 64) {
+      const int j = base + lane;
+      f(j, j < nb, j < nb ? keys[j] : 0ull);
+    }
+  }
+}
+
+template <int D, int NPL>
 __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const int32_t* __restrict__ pq, const float* __restrict__ sq, const int32_t* __restrict__ pk,
     const float* __restrict__ sk, int L, int bs, int nb, int TR, int topk, Band band, int kmax,
@@ -88,41 +112,63 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
   // ---- 1+2: scores of TR query blocks against every key block -------------
   const int g = lane >> 4;  // k-group of the 16x16x64 MFMA operands
-  const int arow = lane & 15;
   v4i a_hi[KSTEPS], a_lo[KSTEPS];
   {
+    const int arow = lane & 15;
     const int i = r0 + arow;
     const bool ok = arow < TR && i < nb;
+    int4 raw[KSTEPS][4];
+    load16<KSTEPS>(pqh + (uint64_t)(ok ? i : 0) * D + g * 16, raw);
 #pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks)
-      split16(pqh + (uint64_t)(ok ? i : 0) * D + ks * 64 + g * 16, ok, a_hi[ks], a_lo[ks]);
+    for (int ks = 0; ks < KSTEPS; ++ks) split16(raw[ks], ok, a_hi[ks], a_lo[ks]);
   }
+  // this lane's accumulator rows 4g + r: their query scale and token count
+  double a_sq[4];
+  int a_n[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = r0 + 4 * g + r;
+    const bool ok = 4 * g + r < TR && i < nb;
+    a_sq[r] = ok ? (double)sqh[i] : 0.0;
+    a_n[r] = ok ? min(bs, L - i * bs) : 0;
+  }
+  // Column tiles ct = wave, wave + 4, ...; the pooled sums and scale of the
+  // next tile are loaded while this one is scored.
   const int n_ctiles = (nb + 15) / 16;
+  int4 raw[KSTEPS][4];
+  float skv = 0.0f;
+  auto fetch = [&](int ct) {
+    const int j = min(ct * 16 + (lane & 15), nb - 1);
+    load16<KSTEPS>(pkh + (uint64_t)j * D + g * 16, raw);
+    skv = skh[j];
+  };
+  if (wave < n_ctiles) fetch(wave);
   for (int ct = wave; ct < n_ctiles; ct += 4) {
     const int j = ct * 16 + (lane & 15);
     const bool okj = j < nb;
+    v4i b_hi[KSTEPS], b_lo[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) split16(raw[ks], okj, b_hi[ks], b_lo[ks]);
+    const double skj = (double)skv;
+    if (ct + 4 < n_ctiles) fetch(ct + 4);
     v4i hh = {0, 0, 0, 0}, mid = {0, 0, 0, 0}, ll = {0, 0, 0, 0};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
-      v4i b_hi, b_lo;
-      split16(pkh + (uint64_t)(okj ? j : 0) * D + ks * 64 + g * 16, okj, b_hi, b_lo);
-      hh = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_hi[ks], b_hi, hh, 0, 0, 0);
-      mid = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_hi[ks], b_lo, mid, 0, 0, 0);
-      mid = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_lo[ks], b_hi, mid, 0, 0, 0);
-      ll = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_lo[ks], b_lo, ll, 0, 0, 0);
+      hh = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_hi[ks], b_hi[ks], hh, 0, 0, 0);
+      mid = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_hi[ks], b_lo[ks], mid, 0, 0, 0);
+      mid = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_lo[ks], b_hi[ks], mid, 0, 0, 0);
+      ll = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_lo[ks], b_lo[ks], ll, 0, 0, 0);
     }
     if (okj) {
-      const double skj = (double)skh[j];
       const int nj = min(bs, L - j * bs);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * g + r;  // accumulator row of this lane
-        const int i = r0 + row;
-        if (row < TR && i < nb) {
+        if (row < TR && r0 + row < nb) {
           const double S = (double)hh[r] * 16384.0 + (double)mid[r] * 128.0 + (double)ll[r];
-          const double a = (double)sqh[i] * skj;
+          const double a = a_sq[r] * skj;
           const double b = S * a;
-          const int ci = min(bs, L - i * bs) * nj;
+          const int ci = a_n[r] * nj;
           // a power of two (every pair of full blocks) divides exactly by a
           // multiplication with its inverse: the same IEEE result as b / c
           const double q = (ci & (ci - 1)) == 0 ? b * (1.0 / (double)ci) : b / (double)ci;
@@ -141,6 +187,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     const int i = r0 + row;
     const bool active = row < TR && i < nb;
     const uint64_t* keys = s_keys + (uint64_t)(active ? row : 0) * nb;
+    uint64_t kr[NPL > 0 ? NPL : 1];
+    if constexpr (NPL > 0) {
+#pragma unroll
+      for (int e = 0; e < NPL; ++e) {
+        const int j = 64 * e + lane;
+        kr[e] = j < nb ? keys[j] : 0ull;
+      }
+    }
 
     uint64_t prefix = 0, pmask = 0;
     int need = k_eff;  // how many still to take among keys matching prefix
@@ -150,11 +204,12 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     int first_pass = 8;
     if (do_select) {
       uint64_t kmin = ~0ull, kmax_ = 0ull;
-      for (int j = lane; j < nb; j += 64) {
-        const uint64_t key = keys[j];
-        kmin = key < kmin ? key : kmin;
-        kmax_ = key > kmax_ ? key : kmax_;
-      }
+      each_key<NPL>(keys, kr, nb, lane, [&](int, bool v, uint64_t key) {
+        if (v) {
+          kmin = key < kmin ? key : kmin;
+          kmax_ = key > kmax_ ? key : kmax_;
+        }
+      });
 #pragma unroll
       for (int o = 32; o >= 1; o >>= 1) {
         const uint64_t a = __shfl_xor(kmin, o, 64), b = __shfl_xor(kmax_, o, 64);
@@ -177,59 +232,51 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       for (int e = 0; e < 4; ++e) s_hist[wave][lane * 4 + e] = 0;
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
       __builtin_amdgcn_wave_barrier();
-      if (do_select) {
-        for (int j = lane; j < nb; j += 64) {
-          const uint64_t key = keys[j];
-          if ((key & pmask) == prefix) atomicAdd(&s_hist[wave][(key >> shift) & 0xff], 1u);
-        }
-      }
+      each_key<NPL>(keys, kr, nb, lane, [&](int, bool v, uint64_t key) {
+        if (v && (key & pmask) == prefix) atomicAdd(&s_hist[wave][(key >> shift) & 0xff], 1u);
+      });
       __builtin_amdgcn_s_waitcnt(0xc07f);
       __builtin_amdgcn_wave_barrier();
-      if (do_select) {
-        uint32_t c[4];
+      uint32_t c[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) c[e] = s_hist[wave][lane * 4 + e];
-        const uint32_t mine = c[0] + c[1] + c[2] + c[3];
-        // inclusive suffix sum over lanes (lanes >= this one)
-        uint32_t suf = mine;
+      for (int e = 0; e < 4; ++e) c[e] = s_hist[wave][lane * 4 + e];
+      const uint32_t mine = c[0] + c[1] + c[2] + c[3];
+      // inclusive suffix sum over lanes (lanes >= this one)
+      uint32_t suf = mine;
 #pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t v = __shfl_down(suf, o, 64);
-          if (lane + o < 64) suf += v;
-        }
-        const uint32_t above = suf - mine;  // keys in higher digit bins
-        const bool here = above < (uint32_t)need && (uint32_t)need <= suf;
-        int digit = 0;
-        uint32_t cnt_above = above;
-        if (here) {
-          for (int e = 3; e >= 0; --e) {
-            if (cnt_above + c[e] >= (uint32_t)need) {
-              digit = lane * 4 + e;
-              break;
-            }
-            cnt_above += c[e];
-          }
-        }
-        const uint64_t who = __ballot(here);
-        const int src = __ffsll((unsigned long long)who) - 1;
-        digit = __shfl(digit, src, 64);
-        cnt_above = __shfl(cnt_above, src, 64);
-        const uint32_t in_bin = s_hist[wave][digit];
-        need -= (int)cnt_above;
-        prefix |= (uint64_t)digit << shift;
-        pmask |= 0xffull << shift;
-        // every key of the chosen bin is taken: no finer digit can matter
-        if ((uint32_t)need == in_bin) break;
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t v = __shfl_down(suf, o, 64);
+        if (lane + o < 64) suf += v;
       }
+      const uint32_t above = suf - mine;  // keys in higher digit bins
+      const bool here = above < (uint32_t)need && (uint32_t)need <= suf;
+      int digit = 0;
+      uint32_t cnt_above = above;
+      if (here) {
+        for (int e = 3; e >= 0; --e) {
+          if (cnt_above + c[e] >= (uint32_t)need) {
+            digit = lane * 4 + e;
+            break;
+          }
+          cnt_above += c[e];
+        }
+      }
+      const uint64_t who = __ballot(here);
+      const int src = __ffsll((unsigned long long)who) - 1;
+      digit = __shfl(digit, src, 64);
+      cnt_above = __shfl(cnt_above, src, 64);
+      const uint32_t in_bin = s_hist[wave][digit];
+      need -= (int)cnt_above;
+      prefix |= (uint64_t)digit << shift;
+      pmask |= 0xffull << shift;
+      // every key of the chosen bin is taken: no finer digit can matter
+      if ((uint32_t)need == in_bin) break;
     }
 
     if (active) {
       int32_t* out = kept_idx + ((bh * (uint64_t)nb) + i) * (uint64_t)kmax;
       int pos = 0, ties_seen = 0;
-      for (int base = 0; base < nb; base += 64) {
-        const int j = base + lane;
-        const bool valid = j < nb;
-        const uint64_t key = valid ? keys[j] : 0;
+      each_key<NPL>(keys, kr, nb, lane, [&](int j, bool valid, uint64_t key) {
         bool in_band = false;
         for (int b = 0; b < band.n; ++b) in_band |= (j - i) == band.off[b];
         bool sel;
@@ -252,13 +299,52 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
         const int p = pos + __popcll(selb & lanemask_lt(lane));
         if (sel && p < kmax) out[p] = j;
         pos += __popcll(selb);
-      }
+      });
       for (int p = pos + lane; p < kmax; p += 64) out[p] = -1;
       if (lane == 0) kept_cnt[bh * (uint64_t)nb + i] = min(pos, kmax);
     }
   }
 }
 
+}  // namespace
+
+namespace {
+template <int D, int NPL>
+void launch_select_kernel(dim3 grid, size_t lds, size_t lds_cap, hipStream_t s,
+                          const int32_t* pooled_q, const float* scale_q, const int32_t* pooled_k,
+                          const float* scale_k, const qsa_dims& d, int nb, int TR, int topk,
+                          const Band& band, int kmax, int32_t* kept_idx, int32_t* kept_cnt) {
+  static bool attr = false;
+  if (!attr) {
+    (void)hipFuncSetAttribute((const void*)select_kernel<D, NPL>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_cap);
+    attr = true;
+  }
+  hipLaunchKernelGGL((select_kernel<D, NPL>), grid, dim3(kSelThreads), lds, s, pooled_q, scale_q,
+                     pooled_k, scale_k, d.seq_len, d.block, nb, TR, topk, band, kmax, kept_idx,
+                     kept_cnt);
+}
+
+// keys per lane held in registers during the select: the smallest of 16, 24,
+// 32 that covers the row; longer rows are read from LDS
+template <int D>
+void launch_select_d(dim3 grid, size_t lds, size_t lds_cap, hipStream_t s,
+                     const int32_t* pooled_q, const float* scale_q, const int32_t* pooled_k,
+                     const float* scale_k, const qsa_dims& d, int nb, int TR, int topk,
+                     const Band& band, int kmax, int32_t* kept_idx, int32_t* kept_cnt) {
+#define QSA_SEL_LAUNCH(NPL)                                                                   \
+  launch_select_kernel<D, NPL>(grid, lds, lds_cap, s, pooled_q, scale_q, pooled_k, scale_k, d, \
+                               nb, TR, topk, band, kmax, kept_idx, kept_cnt)
+  if (nb <= 64 * 16)
+    QSA_SEL_LAUNCH(16);
+  else if (nb <= 64 * 24)
+    QSA_SEL_LAUNCH(24);
+  else if (nb <= 64 * 32)
+    QSA_SEL_LAUNCH(32);
+  else
+    QSA_SEL_LAUNCH(0);
+#undef QSA_SEL_LAUNCH
+}
 }  // namespace
 
 hipError_t launch_select(const qsa_dims& d, const int32_t* pooled_q, const float* scale_q,
@@ -272,27 +358,12 @@ hipError_t launch_select(const qsa_dims& d, const int32_t* pooled_q, const float
   const size_t lds = (size_t)TR * nb * sizeof(uint64_t);
   if (lds > lds_cap) return hipErrorInvalidValue;
   const dim3 grid((nb + TR - 1) / TR, (uint32_t)(d.batch * d.heads));
-  if (d.head_dim == 128) {
-    static bool attr = false;
-    if (!attr) {
-      (void)hipFuncSetAttribute((const void*)select_kernel<128>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_cap);
-      attr = true;
-    }
-    hipLaunchKernelGGL(select_kernel<128>, grid, dim3(kSelThreads), lds, s, pooled_q, scale_q,
-                       pooled_k, scale_k, d.seq_len, d.block, nb, TR, topk, band, kmax,
-                       kept_idx, kept_cnt);
-  } else {
-    static bool attr = false;
-    if (!attr) {
-      (void)hipFuncSetAttribute((const void*)select_kernel<64>,
-                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_cap);
-      attr = true;
-    }
-    hipLaunchKernelGGL(select_kernel<64>, grid, dim3(kSelThreads), lds, s, pooled_q, scale_q,
-                       pooled_k, scale_k, d.seq_len, d.block, nb, TR, topk, band, kmax,
-                       kept_idx, kept_cnt);
-  }
+  if (d.head_dim == 128)
+    launch_select_d<128>(grid, lds, lds_cap, s, pooled_q, scale_q, pooled_k, scale_k, d, nb, TR,
+                         topk, band, kmax, kept_idx, kept_cnt);
+  else
+    launch_select_d<64>(grid, lds, lds_cap, s, pooled_q, scale_q, pooled_k, scale_k, d, nb, TR,
+                        topk, band, kmax, kept_idx, kept_cnt);
   return hipGetLastError();
 }
 
