@@ -5,8 +5,9 @@
 // top-k salient local guidance): every query block keeps the key blocks whose
 // mean-pooled dequantised codes score highest, plus a fixed band of offsets.
 //
-// One workgroup (4 waves) per (batch*head, tile of TR = 8 query blocks; two
-// workgroups share a CU, which hides the latency of the select passes).
+// One workgroup per (batch*head, tile of TR query blocks): TR = 16 with 8
+// waves when the tile's keys fit the LDS (up to 1,216 key blocks; one
+// workgroup per CU), else TR = 8 with 4 waves (two per CU) or fewer rows.
 //  1. Exact integer scores S_ij = sum_d Pq[i,d] Pk[j,d] on the int8 MFMA:
 //     each pooled sum P (|P| <= 127*128) is split into int8 digits
 //     P = 128*hi + lo with lo in [0,127], hi in [-127,127], and
@@ -30,11 +31,7 @@
 namespace qsa {
 namespace {
 
-#ifndef QSA_SEL_TR
-#define QSA_SEL_TR 8
-#endif
-
-constexpr int kSelThreads = 256;
+constexpr int kSelMaxThreads = 512;
 constexpr int kHist = 256;
 
 __device__ __forceinline__ uint64_t order_key(double score) {
@@ -94,15 +91,18 @@ __device__ __forceinline__ void each_key(const uint64_t* keys, const uint64_t (&
 }
 
 template <int D, int NPL>
-__global__ __launch_bounds__(kSelThreads) void select_kernel(
+__global__ __launch_bounds__(kSelMaxThreads) void select_kernel(
     const int32_t* __restrict__ pq, const float* __restrict__ sq, const int32_t* __restrict__ pk,
     const float* __restrict__ sk, int L, int bs, int nb, int TR, int topk, Band band, int kmax,
     int32_t* __restrict__ kept_idx, int32_t* __restrict__ kept_cnt) {
-  extern __shared__ uint64_t s_keys[];  // [TR][nb]
-  __shared__ uint32_t s_hist[4][kHist];
+  // [TR][nb] keys, then one kHist-bin histogram per wave
+  extern __shared__ uint64_t s_keys[];
+  const int nwaves = blockDim.x >> 6;
+  uint32_t* s_hist_all = reinterpret_cast<uint32_t*>(s_keys + (size_t)TR * nb);
 
   constexpr int KSTEPS = D / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  uint32_t* s_hist = s_hist_all + wave * kHist;
   const uint64_t bh = blockIdx.y;
   const int r0 = blockIdx.x * TR;
   const int32_t* pqh = pq + bh * (uint64_t)nb * D;
@@ -132,8 +132,8 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     a_sq[r] = ok ? (double)sqh[i] : 0.0;
     a_n[r] = ok ? min(bs, L - i * bs) : 0;
   }
-  // Column tiles ct = wave, wave + 4, ...; the pooled sums and scale of the
-  // next tile are loaded while this one is scored.
+  // Column tiles ct = wave, wave + nwaves, ...; the pooled sums and scale of
+  // the next tile are loaded while this one is scored.
   const int n_ctiles = (nb + 15) / 16;
   int4 raw[KSTEPS][4];
   float skv = 0.0f;
@@ -143,14 +143,14 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
     skv = skh[j];
   };
   if (wave < n_ctiles) fetch(wave);
-  for (int ct = wave; ct < n_ctiles; ct += 4) {
+  for (int ct = wave; ct < n_ctiles; ct += nwaves) {
     const int j = ct * 16 + (lane & 15);
     const bool okj = j < nb;
     v4i b_hi[KSTEPS], b_lo[KSTEPS];
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) split16(raw[ks], okj, b_hi[ks], b_lo[ks]);
     const double skj = (double)skv;
-    if (ct + 4 < n_ctiles) fetch(ct + 4);
+    if (ct + nwaves < n_ctiles) fetch(ct + nwaves);
     v4i hh = {0, 0, 0, 0}, mid = {0, 0, 0, 0}, ll = {0, 0, 0, 0};
 #pragma unroll
     for (int ks = 0; ks < KSTEPS; ++ks) {
@@ -181,9 +181,9 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
   // ---- 3+4: per-row radix select and ascending compaction -----------------
   const int k_eff = min(topk, nb);
-  const int rows_per_wave = (TR + 3) / 4;
+  const int rows_per_wave = (TR + nwaves - 1) / nwaves;
   for (int it = 0; it < rows_per_wave; ++it) {
-    const int row = it * 4 + wave;
+    const int row = it * nwaves + wave;
     const int i = r0 + row;
     const bool active = row < TR && i < nb;
     const uint64_t* keys = s_keys + (uint64_t)(active ? row : 0) * nb;
@@ -229,17 +229,17 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       // performed in order, so waiting for them (lgkmcnt) orders the zeroing,
       // the counting and the reads without a workgroup barrier.
 #pragma unroll
-      for (int e = 0; e < 4; ++e) s_hist[wave][lane * 4 + e] = 0;
+      for (int e = 0; e < 4; ++e) s_hist[lane * 4 + e] = 0;
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
       __builtin_amdgcn_wave_barrier();
       each_key<NPL>(keys, kr, nb, lane, [&](int, bool v, uint64_t key) {
-        if (v && (key & pmask) == prefix) atomicAdd(&s_hist[wave][(key >> shift) & 0xff], 1u);
+        if (v && (key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 0xff], 1u);
       });
       __builtin_amdgcn_s_waitcnt(0xc07f);
       __builtin_amdgcn_wave_barrier();
       uint32_t c[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) c[e] = s_hist[wave][lane * 4 + e];
+      for (int e = 0; e < 4; ++e) c[e] = s_hist[lane * 4 + e];
       const uint32_t mine = c[0] + c[1] + c[2] + c[3];
       // inclusive suffix sum over lanes (lanes >= this one)
       uint32_t suf = mine;
@@ -265,7 +265,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
       const int src = __ffsll((unsigned long long)who) - 1;
       digit = __shfl(digit, src, 64);
       cnt_above = __shfl(cnt_above, src, 64);
-      const uint32_t in_bin = s_hist[wave][digit];
+      const uint32_t in_bin = s_hist[digit];
       need -= (int)cnt_above;
       prefix |= (uint64_t)digit << shift;
       pmask |= 0xffull << shift;
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(kSelThreads) void select_kernel(
 
 namespace {
 template <int D, int NPL>
-void launch_select_kernel(dim3 grid, size_t lds, size_t lds_cap, hipStream_t s,
+void launch_select_kernel(dim3 grid, int threads, size_t lds, size_t lds_cap, hipStream_t s,
                           const int32_t* pooled_q, const float* scale_q, const int32_t* pooled_k,
                           const float* scale_k, const qsa_dims& d, int nb, int TR, int topk,
                           const Band& band, int kmax, int32_t* kept_idx, int32_t* kept_cnt) {
@@ -320,7 +320,7 @@ void launch_select_kernel(dim3 grid, size_t lds, size_t lds_cap, hipStream_t s,
                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_cap);
     attr = true;
   }
-  hipLaunchKernelGGL((select_kernel<D, NPL>), grid, dim3(kSelThreads), lds, s, pooled_q, scale_q,
+  hipLaunchKernelGGL((select_kernel<D, NPL>), grid, dim3(threads), lds, s, pooled_q, scale_q,
                      pooled_k, scale_k, d.seq_len, d.block, nb, TR, topk, band, kmax, kept_idx,
                      kept_cnt);
 }
@@ -328,12 +328,12 @@ void launch_select_kernel(dim3 grid, size_t lds, size_t lds_cap, hipStream_t s,
 // keys per lane held in registers during the select: the smallest of 16, 24,
 // 32 that covers the row; longer rows are read from LDS
 template <int D>
-void launch_select_d(dim3 grid, size_t lds, size_t lds_cap, hipStream_t s,
+void launch_select_d(dim3 grid, int threads, size_t lds, size_t lds_cap, hipStream_t s,
                      const int32_t* pooled_q, const float* scale_q, const int32_t* pooled_k,
                      const float* scale_k, const qsa_dims& d, int nb, int TR, int topk,
                      const Band& band, int kmax, int32_t* kept_idx, int32_t* kept_cnt) {
 #define QSA_SEL_LAUNCH(NPL)                                                                   \
-  launch_select_kernel<D, NPL>(grid, lds, lds_cap, s, pooled_q, scale_q, pooled_k, scale_k, d, \
+  launch_select_kernel<D, NPL>(grid, threads, lds, lds_cap, s, pooled_q, scale_q, pooled_k, scale_k, d, \
                                nb, TR, topk, band, kmax, kept_idx, kept_cnt)
   if (nb <= 64 * 16)
     QSA_SEL_LAUNCH(16);
@@ -352,17 +352,27 @@ hipError_t launch_select(const qsa_dims& d, const int32_t* pooled_q, const float
                          const Band& band, int32_t kmax, int32_t* kept_idx, int32_t* kept_cnt,
                          hipStream_t s) {
   const int nb = (d.seq_len + d.block - 1) / d.block;
-  const size_t lds_cap = 160 * 1024 - sizeof(uint32_t) * 4 * kHist - 256;
-  int TR = QSA_SEL_TR;
-  while (TR > 1 && (size_t)TR * nb * sizeof(uint64_t) > lds_cap) TR >>= 1;
-  const size_t lds = (size_t)TR * nb * sizeof(uint64_t);
+  // 16 query blocks and 8 waves per workgroup when their keys and histograms
+  // fit the LDS (one workgroup per CU; the pooled K sums are split once per 16
+  // rows), else 8 blocks and 4 waves (two per CU), fewer for long sequences
+  const size_t lds_cap = 160 * 1024;
+  auto lds_of = [&](int tr, int threads) {
+    return (size_t)tr * nb * sizeof(uint64_t) + (size_t)(threads / 64) * kHist * sizeof(uint32_t);
+  };
+  int TR = 16, threads = kSelMaxThreads;
+  if (lds_of(TR, threads) > lds_cap) {
+    TR = 8;
+    threads = 256;
+    while (TR > 1 && lds_of(TR, threads) > lds_cap) TR >>= 1;
+  }
+  const size_t lds = lds_of(TR, threads);
   if (lds > lds_cap) return hipErrorInvalidValue;
   const dim3 grid((nb + TR - 1) / TR, (uint32_t)(d.batch * d.heads));
   if (d.head_dim == 128)
-    launch_select_d<128>(grid, lds, lds_cap, s, pooled_q, scale_q, pooled_k, scale_k, d, nb, TR,
+    launch_select_d<128>(grid, threads, lds, lds_cap, s, pooled_q, scale_q, pooled_k, scale_k, d, nb, TR,
                          topk, band, kmax, kept_idx, kept_cnt);
   else
-    launch_select_d<64>(grid, lds, lds_cap, s, pooled_q, scale_q, pooled_k, scale_k, d, nb, TR,
+    launch_select_d<64>(grid, threads, lds, lds_cap, s, pooled_q, scale_q, pooled_k, scale_k, d, nb, TR,
                         topk, band, kmax, kept_idx, kept_cnt);
   return hipGetLastError();
 }
