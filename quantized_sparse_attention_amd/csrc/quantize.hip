@@ -9,9 +9,11 @@
 // coalesced loads (8 bf16 per lane) and 8-byte stores.
 //
 // Bit-exactness: the scale is an IEEE fp32 division amax / 127 and each code
-// the round-half-even of an IEEE fp32 division x / scale.  The library is
-// compiled with correctly rounded fp32 division, no fast-math and no FP
-// contraction in this file, and fp32 denormals preserved.
+// the round-half-even of an IEEE fp32 division x / scale, reached through a
+// multiplication by 1 / scale and an exact check of the remainder (the
+// division itself only for the rare quotients next to a half-integer).  The
+// library is compiled with correctly rounded fp32 division, no fast-math and
+// no FP contraction in this file, and fp32 denormals preserved.
 //
 // Rotated variant (Hadamard rotation of the activations before quantisation,
 // DVD-Quant gist.science/es/paper/2505.18663, technical summary §2B: it
@@ -36,12 +38,39 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-__device__ __forceinline__ int code_of(float x, float s) {
-  // s > 0; |x| <= amax so |x / s| <= 127 * (1 + 2^-23): the clamp only
-  // guards the contract.
-  float q = __builtin_rintf(x / s);
-  q = fminf(fmaxf(q, -127.0f), 127.0f);
-  return (int)q;
+// code = clamp(rint(fl32(x / s)), -127, 127) for a block scale s > 0 with
+// |x| <= 127 s (the clamp only guards the contract).
+//
+// Without a division per element: with inv = fl32(1 / s), p = fl32(x * inv)
+// is within 127 * 2^-23 < 2^-16 of the exact quotient q = x / s, and so is
+// fl32(q) (half an ulp below 128 is 2^-18).  Unless q lies within 2^-16 of a
+// half-integer, p, q and fl32(q) round to the same integer c = rint(p).  The
+// remainder d = fl32(x - c s) (one fused rounding) tells: | |d| - s/2 | >
+// 2^-14 s implies | |q - c| - 1/2 | > 2^-16 (the roundings of d and of the
+// test move it by less than 2^-23 s), so c is right; otherwise the element
+// takes the IEEE division.  Needs 1 / s finite and s 2^-14 normal: the caller
+// takes the division for every element when s < 2^-100.
+__device__ __forceinline__ void codes8(const float (&x)[8], float s, float inv, bool fast,
+                                       int (&c)[8]) {
+  float q[8];
+  bool any_div = !fast;
+  uint32_t div = fast ? 0u : 0xffu;  // elements that take the division
+  if (fast) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      q[e] = __builtin_rintf(x[e] * inv);
+      const float d = __builtin_fmaf(-q[e], s, x[e]);
+      if (!(fabsf(fabsf(d) - 0.5f * s) > s * 0x1p-14f)) div |= 1u << e;
+    }
+    any_div = div != 0u;
+  }
+  if (any_div) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      if ((div >> e) & 1u) q[e] = __builtin_rintf(x[e] / s);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) c[e] = (int)fminf(fmaxf(q[e], -127.0f), 127.0f);
 }
 
 // In-place fast Walsh-Hadamard transform of one token row held 8 channels
@@ -125,6 +154,8 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   __syncthreads();
   amax = fmaxf(fmaxf(s_amax[0], s_amax[1]), fmaxf(s_amax[2], s_amax[3]));
   const float s = amax / 127.0f;  // IEEE division; 0 for an all-zero block
+  const bool fast = s >= 0x1p-100f;
+  const float inv = fast ? 1.0f / s : 0.0f;
 
   int psum[8];
 #pragma unroll
@@ -135,8 +166,12 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     const int row = r0 + p * RPP;
     if (row < n) {
       int c[8];
+      if (s > 0.0f) {
+        codes8(y[p], s, inv, fast, c);
+      } else {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) c[e] = s > 0.0f ? code_of(y[p][e], s) : 0;
+        for (int e = 0; e < 8; ++e) c[e] = 0;
+      }
       uint32_t lo = 0, hi = 0;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {

@@ -12,7 +12,9 @@ checks what it can compute one by one:
   sampled query blocks of those heads (first, second, middle, the ragged last
   block, two random); the residual r against the unrounded full - sparse;
 * everywhere: every output is finite and every kept list is ascending, in
-  range, contains its band and has top-k + band entries at most.
+  range, contains its band and has top-k + band entries at most; the sparse
+  step and a second refresh step (on top of the cached residual) give the
+  same bits when the query blocks run in the computed processing order.
 
 The inputs come from the seeded generator on the GPU (qsa_gen.make_qkv_torch);
 the oracle reads the same bf16 values copied to the host.
@@ -56,8 +58,20 @@ def run(request):
     order = B.qsa_order_query_blocks(idx, cnt, w.seq_len, w.block, w.head_dim)
     step_o = B.qsa_sparse_attn_ordered(qc, qs, kc, ks, x["v"], idx, cnt, order, w.block, r=r,
                                        dr=dr)
+    # a second refresh on top of the residual just cached (has_prev = 1), in
+    # ascending order and in the computed order
+    outs = []
+    for od in (None, order):
+        rr = r.clone()
+        ddr = torch.empty_like(r)
+        ff = B.qsa_full_attn_residual(qc, qs, kc, ks, x["v"], idx, cnt, w.block, rr, ddr, 1,
+                                      order=od)
+        outs.append((ff, rr, ddr))
     rot = [*B.qsa_quantize_rotated(x["q"], w.block), *B.qsa_quantize_rotated(x["k"], w.block)]
     torch.cuda.synchronize()
+    refresh_same = all(torch.equal(a.view(torch.int16), b.view(torch.int16))
+                       for a, b in zip(*outs))
+    del outs, rr, ddr, ff
     srt, _ = torch.sort(order.long(), dim=-1)
     order_ok = bool((srt == torch.arange(w.n_blocks, device=dev)).all())
     ordered_same = torch.equal(step.view(torch.int16), step_o.view(torch.int16))
@@ -77,7 +91,7 @@ def run(request):
         "dr_bits": _bits(dr[:, heads]),
         "finite": all(bool(torch.isfinite(t.float()).all()) for t in (sparse, full, r, step)),
         "idx_all": idx, "cnt_all": cnt,
-        "order_ok": order_ok, "ordered_same": ordered_same,
+        "order_ok": order_ok, "ordered_same": ordered_same, "refresh_same": refresh_same,
         "rot": [t[:, heads].cpu().numpy() for t in rot],
     }
     del rot
@@ -160,6 +174,12 @@ def test_fullsize_ordered_step_identical(run):
     """The processing order is a permutation on every head and changes no output bit."""
     assert run[3]["order_ok"]
     assert run[3]["ordered_same"]
+
+
+def test_fullsize_ordered_refresh_identical(run):
+    """A refresh step with a previous residual (has_prev = 1) writes the same
+    full output, r and dr on every head in the computed processing order."""
+    assert run[3]["refresh_same"]
 
 
 def test_fullsize_sparse_sampled(run):

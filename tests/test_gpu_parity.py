@@ -250,6 +250,41 @@ def test_quantize_map_sweep():
     assert np.array_equal(p_g.cpu().numpy(), p_o)
 
 
+def test_quantize_half_integer_quotients():
+    # Quotients x / scale at and next to every half-integer k + 1/2 (k < 127):
+    # scales that are powers of two (amax = 127 * 2^e: the ties are exact) and
+    # others (amax = 127 * 2^e * (1 + j/128) rounded to bf16), for exponents on
+    # both sides of 2^-100 and up to 2^120.  Each block holds its amax first,
+    # then the bf16 values nearest to +-(k + 1/2) * scale and their bf16
+    # neighbours, padded with amax.  Codes, scales and sums bit-exact.
+    blocks = []
+    for e in [-122, -110, -104, -101, -100, -99, -98, -60, -20, -3, 0, 7, 60, 120]:
+        for j in (0, 1, 37, 101):
+            am_bits = qsa_gen.f32_to_bf16_bits(
+                np.array([127.0 * 2.0 ** e * (1 + j / 128)], np.float32))
+            am = np.float32(qsa_gen.bf16_bits_to_f32(am_bits)[0])
+            sc = am / np.float32(127.0)
+            t = ((np.arange(127) + 0.5) * np.float64(sc)).astype(np.float32)
+            tb = qsa_gen.f32_to_bf16_bits(t).astype(np.int32)
+            near = np.concatenate([tb - 1, tb, tb + 1]).astype(np.uint16)
+            v = qsa_gen.bf16_bits_to_f32(near)
+            v = v[np.isfinite(v) & (np.abs(v) <= am)]
+            blk = np.concatenate([[am], v, -v]).astype(np.float32)
+            assert blk.size <= 64 * 128
+            blk = np.concatenate([blk, np.full(64 * 128 - blk.size, am, np.float32)])
+            blocks.append(blk.reshape(64, 128))
+    data = np.stack(blocks).reshape(1, 1, -1, 128)
+    bits = qsa_gen.f32_to_bf16_bits(data)
+    c_o, s_o, p_o = oracle.quantize(bits, 64)
+    c_g, s_g, p_g = B.qsa_quantize(dev_bf16(bits), 64)
+    assert np.array_equal(s_g.cpu().numpy().view(np.uint32), s_o.view(np.uint32))
+    assert np.array_equal(c_g.cpu().numpy(), c_o)
+    assert np.array_equal(p_g.cpu().numpy(), p_o)
+    # the set really holds exact ties and codes rounded both ways
+    q = data.reshape(-1)[: 64 * 128].astype(np.float64) / np.float64(s_o.reshape(-1)[0])
+    assert np.any(np.abs(q - np.round(q - 0.5) - 0.5) == 0)
+
+
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_examples.json")
 
 
