@@ -314,12 +314,11 @@ void launch_select_kernel(dim3 grid, int threads, size_t lds, size_t lds_cap, hi
                           const int32_t* pooled_q, const float* scale_q, const int32_t* pooled_k,
                           const float* scale_k, const qsa_dims& d, int nb, int TR, int topk,
                           const Band& band, int kmax, int32_t* kept_idx, int32_t* kept_cnt) {
-  static bool attr = false;
-  if (!attr) {
-    (void)hipFuncSetAttribute((const void*)select_kernel<D, NPL>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_cap);
-    attr = true;
-  }
+  // set once per kernel (a function-local static is initialised exactly once,
+  // also when several host threads launch at the same time)
+  static const hipError_t attr = hipFuncSetAttribute(
+      (const void*)select_kernel<D, NPL>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_cap);
+  (void)attr;
   hipLaunchKernelGGL((select_kernel<D, NPL>), grid, dim3(threads), lds, s, pooled_q, scale_q,
                      pooled_k, scale_k, d.seq_len, d.block, nb, TR, topk, band, kmax, kept_idx,
                      kept_cnt);
