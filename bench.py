@@ -55,11 +55,52 @@ def parse():
                    help="also run the adaptive-refresh L1 change after every step (timed apart)")
     p.add_argument("--squad", action="store_true",
                    help="also time SQuad two-pass attention on a 65,536-token, 24-head sequence")
+    p.add_argument("--no-peaks", action="store_true",
+                   help="skip the MFMA-rate probe (libqsa_probe.so) reported as measured_peaks")
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="before the run, copy a bf16 buffer of this many MiB once with a "
                         "plain elementwise kernel (reads and writes each byte once): the "
                         "reference for scaling the FETCH_SIZE / WRITE_SIZE counters")
     return p.parse_args()
+
+
+PROBE_LIB = os.path.join(ROOT, "quantized_sparse_attention_amd", "libqsa_probe.so")
+
+
+def measured_peaks(stream, blocks=2048, iters=40000):
+    """Sustained MFMA rates of MFMA-only loops (libqsa_probe.so) on this chip:
+    int8 32x32x32, bf16 32x32x16 and their 1:1 op mix, each launch about
+    30-60 ms so that the clock settles where the power limit puts it."""
+    import ctypes
+
+    import torch
+
+    if not os.path.exists(PROBE_LIB):
+        return {"error": "libqsa_probe.so not built"}
+    lib = ctypes.CDLL(PROBE_LIB)
+    lib.qsa_probe_mfma.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                   ctypes.c_void_p, ctypes.c_void_p]
+    lib.qsa_probe_mfma.restype = ctypes.c_int
+    lib.qsa_probe_mfma_ops.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+    lib.qsa_probe_mfma_ops.restype = ctypes.c_double
+    buf = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    res = {}
+    for kind, name in ((0, "int8_tops"), (1, "bf16_tflops"), (2, "mixed_tops")):
+        ts = []
+        for _ in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            st = lib.qsa_probe_mfma(kind, iters, blocks, ctypes.c_void_p(buf.data_ptr()),
+                                    ctypes.c_void_p(stream.cuda_stream))
+            e1.record(stream)
+            if st != 0:
+                return {"error": f"qsa_probe_mfma({kind}) returned {st}"}
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        ops = lib.qsa_probe_mfma_ops(kind, iters, blocks)
+        res[name] = round(ops / min(ts[1:]) / 1e12, 1)
+    res["launch"] = f"{blocks} workgroups x 256 threads, {iters} iterations per wave"
+    return res
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_sparse_attn_wan14b_720p.json")
@@ -401,6 +442,11 @@ def main():
                 "frac": round(q_bytes / t_q1 / PEAK_HBM_BYTES, 4) if t_q1 else None},
         },
     }
+    if not args.no_peaks:
+        pk = measured_peaks(stream)
+        if "mixed_tops" in pk and t_attn > 0:
+            pk["attn_frac_of_measured_mixed"] = round(achieved / 1e12 / pk["mixed_tops"], 4)
+        res["measured_peaks"] = pk
     if args.squad:
         del inputs, qc, kc, qp, kp, kept, out, r, dr
         torch.cuda.empty_cache()

@@ -3,7 +3,9 @@
     python -m quantized_sparse_attention_amd.build
 
 Compiles every csrc/*.hip to an object (in parallel) and links them into
-quantized_sparse_attention_amd/libqsa.so.  Always recompiles.
+quantized_sparse_attention_amd/libqsa.so; the benchmark's MFMA-rate probe
+(probe/*.hip) goes into a library of its own, libqsa_probe.so.  Always
+recompiles.
 """
 from __future__ import annotations
 
@@ -18,6 +20,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libqsa.so")
+PROBE_DIR = os.path.join(PKG, "probe")
+PROBE_LIB = os.path.join(PKG, "libqsa_probe.so")
 OBJ_DIR = os.path.join(PKG, "_build")
 
 ARCH = "gfx950"
@@ -49,12 +53,13 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libqsa.so)")
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(folder: str = CSRC):
+    return sorted(os.path.join(folder, f) for f in os.listdir(folder) if f.endswith(".hip"))
 
 
 def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(OBJ_DIR, os.path.basename(src)[:-4] + ".o")
+    sub = "probe_" if os.path.dirname(src) == PROBE_DIR else ""
+    obj = os.path.join(OBJ_DIR, sub + os.path.basename(src)[:-4] + ".o")
     cmd = [hipcc(), *HIPCC_FLAGS, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -68,19 +73,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
-    os.makedirs(OBJ_DIR, exist_ok=True)
-    srcs = sources()
-    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False, jobs: int = 8) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    srcs, probe = sources(), sources(PROBE_DIR)
+    with cf.ThreadPoolExecutor(max_workers=min(jobs, len(srcs) + len(probe))) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs + probe))
+    _link(objs[:len(srcs)], LIB, verbose)
+    _link(objs[len(srcs):], PROBE_LIB, verbose)
     return LIB
 
 

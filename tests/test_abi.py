@@ -254,3 +254,29 @@ def test_squad_validation(lib):
         assert sq() == B.QSA_ERR_DEVICE
         assert lib.qsa_window_kept(d, 128, 2, P[0], P[1], None) == B.QSA_ERR_DEVICE
         assert lib.qsa_reorder_windows(d, 64, 1, P[0], P[1], None) == B.QSA_ERR_DEVICE
+
+
+PROBE_LIB = os.path.join(ROOT, "quantized_sparse_attention_amd", "libqsa_probe.so")
+
+
+def test_probe_library_is_separate_and_checks_its_arguments():
+    """The benchmark's MFMA-rate probe lives in libqsa_probe.so, not in the
+    attention library, and rejects bad arguments before any launch."""
+    if not os.path.exists(PROBE_LIB):
+        pytest.skip("libqsa_probe.so not built")
+    out = subprocess.run(["nm", "-D", "--defined-only", PROBE_LIB], capture_output=True,
+                         text=True, check=True).stdout
+    assert set(re.findall(r"\bT (qsa_\w+)", out)) == {"qsa_probe_mfma", "qsa_probe_mfma_ops"}
+    main = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True,
+                          text=True, check=True).stdout
+    assert "qsa_probe" not in main
+    p = ctypes.CDLL(PROBE_LIB)
+    p.qsa_probe_mfma.argtypes = [ctypes.c_int32] * 3 + [ctypes.c_void_p] * 2
+    p.qsa_probe_mfma_ops.argtypes = [ctypes.c_int32] * 3
+    p.qsa_probe_mfma_ops.restype = ctypes.c_double
+    for args in ((3, 10, 4, 16), (0, 0, 4, 16), (1, 10, 0, 16), (2, 10, 4, None)):
+        assert p.qsa_probe_mfma(*args, None) == -1, args
+    # ops per launch: waves x iterations x (ops of the MFMAs of one iteration)
+    assert p.qsa_probe_mfma_ops(0, 10, 2) == 8 * 10 * 4 * 65536
+    assert p.qsa_probe_mfma_ops(1, 10, 2) == 8 * 10 * 4 * 32768
+    assert p.qsa_probe_mfma_ops(2, 10, 2) == 8 * 10 * (2 * 65536 + 4 * 32768)
