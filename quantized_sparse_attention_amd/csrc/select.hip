@@ -16,14 +16,19 @@
 //     fp64 (all values are integers below 2^53).
 //  2. score = fl64(fl64(S * sq*sk) / (n_i*n_j)) in IEEE fp64, mapped to an
 //     order-preserving uint64 key (-0 canonicalised to +0), kept in LDS.
-//  3. Per row (one wave), a radix select over the keys, one byte per pass,
-//     finds the k-th largest key T and how many keys equal to T are taken.
-//     The passes start after the bytes shared by the row's smallest and
-//     largest key (shared by every key) and stop once the bin holding the
-//     k-th key is taken whole; T is then known on its decided bytes only.
-//  4. Ascending compaction with wave ballots: j is kept if key > T, or
-//     key == T and fewer than `take` lower-indexed ties precede it (both
-//     compared on T's decided bytes), or j - i is a band offset.
+//  3. Per row (one wave), a radix select finds the k-th largest key.  Its
+//     sign class comes first from ballot counts (keys of score >= 0 are
+//     >= 2^63): if fewer than k keys are in the upper class, all of them are
+//     taken and the rest is chosen in the lower one.  Inside the class,
+//     t = key - (smallest key of the class) keeps the order, and the digits
+//     (8 bits, the last one shorter) start at the top bit of the class's
+//     range, so no pass is spent on the sign and exponent bits most keys
+//     share.  The passes stop once the bin holding the k-th key is taken
+//     whole; the threshold is then known on its decided bits only.
+//  4. Ascending compaction with wave ballots: j is kept if its key is in the
+//     class above the candidates', or it is a candidate whose decided bits
+//     of t exceed the threshold's, or equal them with fewer than `need`
+//     lower-indexed equal candidates before it, or j - i is a band offset.
 #include "qsa_internal.h"
 
 #pragma clang fp contract(off)
@@ -196,16 +201,30 @@ __global__ __launch_bounds__(kSelMaxThreads) void select_kernel(
       }
     }
 
-    uint64_t prefix = 0, pmask = 0;
-    int need = k_eff;  // how many still to take among keys matching prefix
+    // The k-th largest key is found in its sign class first: with npos keys
+    // of score >= 0 (keys >= 2^63), it is among them if npos >= k, else all
+    // of them are taken and the rest is chosen among the negative keys.
+    // Inside the class, t = key - (smallest key of the class) preserves the
+    // order and the radix digits start at the top bit of the class's range,
+    // so the first histogram already spreads the keys (the top bits of a
+    // key are the sign and the exponent, shared by many keys).
+    constexpr uint64_t kSign = 0x8000000000000000ull;
+    int need = k_eff;  // how many still to take among the candidates
     const bool do_select = active && k_eff > 0 && k_eff < nb;
-    // Every key lies between the row's smallest and largest, so the bytes
-    // those two share are shared by all keys: the passes start after them.
-    int first_pass = 8;
+    bool pos_class = true;     // candidates: keys >= 2^63, else keys < 2^63
+    uint64_t lo = 0;           // smallest candidate key
+    uint64_t prefix = 0, pmask = 0;  // decided high bits of t and their value
+    int lowbit = 0;            // undecided low bits of t
     if (do_select) {
+      int npos = 0;
+      each_key<NPL>(keys, kr, nb, lane, [&](int, bool v, uint64_t key) {
+        npos += __popcll(__ballot(v && key >= kSign));
+      });
+      pos_class = npos >= need;
+      if (!pos_class) need -= npos;
       uint64_t kmin = ~0ull, kmax_ = 0ull;
       each_key<NPL>(keys, kr, nb, lane, [&](int, bool v, uint64_t key) {
-        if (v) {
+        if (v && (key >= kSign) == pos_class) {
           kmin = key < kmin ? key : kmin;
           kmax_ = key > kmax_ ? key : kmax_;
         }
@@ -216,15 +235,15 @@ __global__ __launch_bounds__(kSelMaxThreads) void select_kernel(
         kmin = a < kmin ? a : kmin;
         kmax_ = b > kmax_ ? b : kmax_;
       }
-      const uint64_t diff = kmin ^ kmax_;
-      first_pass = diff ? __clzll((long long)diff) / 8 : 8;
-      if (first_pass > 0) {
-        pmask = first_pass == 8 ? ~0ull : ~0ull << (64 - 8 * first_pass);
-        prefix = kmax_ & pmask;
-      }
+      lo = kmin;
+      const uint64_t range = kmax_ - kmin;
+      lowbit = range ? 64 - __clzll((long long)range) : 0;
+      pmask = lowbit == 64 ? 0ull : ~0ull << lowbit;  // bits >= lowbit are 0 for every t
     }
-    for (int pass = do_select ? first_pass : 8; pass < 8; ++pass) {
-      const int shift = 56 - 8 * pass;
+    while (lowbit > 0) {
+      const int width = min(8, lowbit);
+      const int shift = lowbit - width;
+      const uint64_t dmask = (1ull << width) - 1;
       // The histogram is this wave's own: LDS operations of one wave are
       // performed in order, so waiting for them (lgkmcnt) orders the zeroing,
       // the counting and the reads without a workgroup barrier.
@@ -233,7 +252,9 @@ __global__ __launch_bounds__(kSelMaxThreads) void select_kernel(
       __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
       __builtin_amdgcn_wave_barrier();
       each_key<NPL>(keys, kr, nb, lane, [&](int, bool v, uint64_t key) {
-        if (v && (key & pmask) == prefix) atomicAdd(&s_hist[(key >> shift) & 0xff], 1u);
+        const uint64_t t = key - lo;
+        if (v && (key >= kSign) == pos_class && (t & pmask) == prefix)
+          atomicAdd(&s_hist[(t >> shift) & dmask], 1u);
       });
       __builtin_amdgcn_s_waitcnt(0xc07f);
       __builtin_amdgcn_wave_barrier();
@@ -248,7 +269,7 @@ __global__ __launch_bounds__(kSelMaxThreads) void select_kernel(
         const uint32_t v = __shfl_down(suf, o, 64);
         if (lane + o < 64) suf += v;
       }
-      const uint32_t above = suf - mine;  // keys in higher digit bins
+      const uint32_t above = suf - mine;  // candidates in higher digit bins
       const bool here = above < (uint32_t)need && (uint32_t)need <= suf;
       int digit = 0;
       uint32_t cnt_above = above;
@@ -268,8 +289,9 @@ __global__ __launch_bounds__(kSelMaxThreads) void select_kernel(
       const uint32_t in_bin = s_hist[digit];
       need -= (int)cnt_above;
       prefix |= (uint64_t)digit << shift;
-      pmask |= 0xffull << shift;
-      // every key of the chosen bin is taken: no finer digit can matter
+      pmask |= dmask << shift;
+      lowbit = shift;
+      // every candidate of the chosen bin is taken: no finer digit can matter
       if ((uint32_t)need == in_bin) break;
     }
 
@@ -285,13 +307,15 @@ __global__ __launch_bounds__(kSelMaxThreads) void select_kernel(
         } else if (k_eff == nb) {
           sel = true;
         } else {
-          // compared on the decided digits only (all of them unless the
-          // select stopped at a bin taken whole)
-          const uint64_t mk = key & pmask;
-          const bool eq = mk == prefix;
+          // keys of the class above the candidates' are all taken; the
+          // candidates compare on the decided digits only (all of them unless
+          // the select stopped at a bin taken whole)
+          const bool in_cls = (key >= kSign) == pos_class;
+          const uint64_t mk = (key - lo) & pmask;
+          const bool eq = in_cls && mk == prefix;
           const uint64_t eqb = __ballot(valid && eq);
           const int rank = ties_seen + __popcll(eqb & lanemask_lt(lane));
-          sel = mk > prefix || (eq && rank < need);
+          sel = (!pos_class && key >= kSign) || (in_cls && mk > prefix) || (eq && rank < need);
           ties_seen += __popcll(eqb);
         }
         sel = valid && (sel || in_band);
