@@ -239,30 +239,36 @@ def block_scores(pooled_q, scale_q, pooled_k, scale_k, seq_len: int, block: int)
     return b / c
 
 
-def select_blocks(scores, topk: int, band, kmax: int):
+def select_blocks(scores, topk: int, band, kmax: int, rows=None):
     """kept_idx int32 [B, H, nb, kmax] (ascending, padded with -1), kept_cnt (R5).
 
     top-k orders all key blocks by score descending (IEEE comparison, so
     -0 equals +0) and then by block index ascending, and keeps the first
     min(topk, nb); band(i) = {i + o : 0 <= i + o < nb}.
+
+    ``rows``: optional query block indices of the rows of ``scores``
+    ([B, H, len(rows), nb], a subset of the rows of the full score matrix);
+    the results then cover those rows only, in that order.
     """
-    B, H, nb, _ = scores.shape
+    B, H, nr, nb = scores.shape
+    rows = list(range(nb)) if rows is None else [int(i) for i in rows]
+    assert len(rows) == nr
     k = min(int(topk), nb)
-    kept_idx = np.full((B, H, nb, kmax), -1, dtype=np.int32)
-    kept_cnt = np.zeros((B, H, nb), dtype=np.int32)
+    kept_idx = np.full((B, H, nr, kmax), -1, dtype=np.int32)
+    kept_cnt = np.zeros((B, H, nr), dtype=np.int32)
     j = np.arange(nb)
     for b in range(B):
         for h in range(H):
             # lexsort: last key is primary -> score descending, then j ascending
-            order = np.lexsort((np.broadcast_to(j, (nb, nb)), -scores[b, h]), axis=-1)
-            for i in range(nb):
-                chosen = set(order[i, :k].tolist())
+            order = np.lexsort((np.broadcast_to(j, (nr, nb)), -scores[b, h]), axis=-1)
+            for n, i in enumerate(rows):
+                chosen = set(order[n, :k].tolist())
                 chosen.update(i + o for o in band if 0 <= i + o < nb)
                 lst = sorted(chosen)
                 if len(lst) > kmax:
                     raise ValueError("kmax too small for top-k plus band")
-                kept_idx[b, h, i, : len(lst)] = lst
-                kept_cnt[b, h, i] = len(lst)
+                kept_idx[b, h, n, : len(lst)] = lst
+                kept_cnt[b, h, n] = len(lst)
     return kept_idx, kept_cnt
 
 

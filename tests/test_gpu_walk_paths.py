@@ -110,3 +110,55 @@ def test_refresh_complement_phase_on_bitmaps():
         assert np.linalg.norm(err) / np.linalg.norm(ref) <= REL_L2, f"r block {i}"
         assert float(np.abs(err).max()) <= 2 * MAX_ABS + 2.0 ** -8 * float(np.abs(rho).max())
     print("[walk paths] refresh ok", flush=True)
+
+
+def test_maximum_block_count():
+    """QSA_MAX_BLOCKS = 16,384 key blocks of 64 tokens with a ragged last
+    block (1,048,575 tokens, one head): the select runs one row per workgroup
+    with its keys in LDS, and the attention walks the bitmaps at their full
+    width (no words are left for a tile list).  Codes bit-exact on the whole
+    tensor; kept lists bit-exact on sampled rows (the oracle's top-k of those
+    rows plus the band); sparse outputs (plain and ordered) on sampled query
+    blocks and the refresh output on the first and the ragged last block."""
+    w = qsa_gen.get_workload("tiny").with_(cfg_id=33, heads=1, head_dim=128, grid=(25, 1271, 33),
+                                           block=64, topk_override=6, noise_std=0.3)
+    nb = w.n_blocks
+    assert nb == B.QSA_MAX_BLOCKS and w.seq_len % 64 == 63 and w.kmax == w.topk + 1
+    print(f"\n[walk paths] maximum L={w.seq_len} nb={nb} topk={w.topk}", flush=True)
+    dev = torch.device("cuda:0")
+    x = qsa_gen.make_qkv_torch(w, dev)[0]
+    qc, qs, qp = B.qsa_quantize(x["q"], w.block)
+    kc, ks, kp = B.qsa_quantize(x["k"], w.block)
+    idx, cnt = B.qsa_select_blocks(qp, qs, kp, ks, w.seq_len, w.block, w.topk, w.band, w.kmax)
+    out = B.qsa_sparse_attn(qc, qs, kc, ks, x["v"], idx, cnt, w.block)
+    order = B.qsa_order_query_blocks(idx, cnt, w.seq_len, w.block, w.head_dim)
+    out_o = B.qsa_sparse_attn_ordered(qc, qs, kc, ks, x["v"], idx, cnt, order, w.block)
+    r = torch.zeros_like(x["v"])
+    dr = torch.zeros_like(r)
+    full = B.qsa_full_attn_residual(qc, qs, kc, ks, x["v"], idx, cnt, w.block, r, dr, 0)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), out_o.view(torch.int16))
+    print("[walk paths] maximum: GPU done", flush=True)
+    host = {t: host_bits(x[t]) for t in "qkv"}
+    oqc, osq, opq = oracle.quantize(host["q"], w.block)
+    okc, osk, opk = oracle.quantize(host["k"], w.block)
+    assert np.array_equal(qc.cpu().numpy(), oqc) and np.array_equal(kc.cpu().numpy(), okc)
+    assert np.array_equal(qs.cpu().numpy().view(np.uint32), osq.view(np.uint32))
+    assert np.array_equal(kp.cpu().numpy(), opk)
+    print("[walk paths] maximum: codes ok", flush=True)
+    rows = _samples(nb)
+    sc = oracle.block_scores(opq, osq, opk, osk, w.seq_len, w.block)[:, :, rows].copy()
+    oidx, ocnt = oracle.select_blocks(sc, w.topk, w.band, w.kmax, rows=rows)
+    del sc
+    gidx, gcnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    assert np.array_equal(gidx[:, :, rows], oidx) and np.array_equal(gcnt[:, :, rows], ocnt)
+    print("[walk paths] maximum: kept lists ok", flush=True)
+    sm = oracle.default_sm_scale(w.head_dim)
+    want = oracle.attention(oqc, osq, okc, osk, host["v"], gidx, gcnt, w.block, sm,
+                            which=[(0, 0, i) for i in rows])
+    _check(host_f64(out), want, w, "sparse")
+    fi, fc = oracle.full_kept_lists(1, 1, nb)
+    want_full = oracle.attention(oqc, osq, okc, osk, host["v"], fi, fc, w.block, sm,
+                                 which=[(0, 0, 0), (0, 0, nb - 1)])
+    _check(host_f64(full), want_full, w, "refresh output")
+    print("[walk paths] maximum ok", flush=True)

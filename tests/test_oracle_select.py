@@ -94,6 +94,22 @@ def test_selection_against_brute_force_sort(nb, k, band):
             assert np.all(idx[0, h, i, len(want):] == -1)
 
 
+def test_selection_of_a_row_subset_against_brute_force_sort():
+    # rows= selects given query blocks out of a wider score matrix; the band
+    # follows the real row index
+    nb, k, band = 40, 4, (-2, 0, 5)
+    rng = np.random.default_rng(77)
+    sc = rng.integers(-3, 4, (1, 1, nb, nb)).astype(np.float64)
+    rows = [0, 1, 17, 36, 39]
+    kmax = k + len(band)
+    idx, cnt = oracle.select_blocks(sc[:, :, rows], k, band, kmax, rows=rows)
+    assert idx.shape == (1, 1, len(rows), kmax)
+    for n, i in enumerate(rows):
+        want = _brute_kept(sc[0, 0, i], i, k, band, nb)
+        assert cnt[0, 0, n] == len(want)
+        assert idx[0, 0, n, : len(want)].tolist() == want
+
+
 def test_selection_invariants():
     rng = np.random.default_rng(11)
     nb, k, band = 40, 6, (-1, 0, 1)
