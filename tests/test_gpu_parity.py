@@ -380,6 +380,45 @@ def test_attention_edges():
     assert_close(out, want, what="edges")
 
 
+@pytest.mark.parametrize("L,bs,D", [(1, 64, 128), (37, 64, 64), (64, 64, 128), (100, 128, 128),
+                                    (129, 128, 64)])
+def test_short_sequences(L, bs, D):
+    """Sequences of one block or less (a single token included), and one full
+    block plus one token, through the whole path: front end bit-exact; sparse
+    and refresh outputs against the oracle; the ordered entry points give the
+    same bits."""
+    w = TINY.with_(grid=(1, 1, L), block=bs, head_dim=D)
+    x = qsa_gen.make_qkv(w)
+    o = oracle_front(x, w, topk=1, band=(0,))
+    g = _gpu_front(x, w, o["topk"], o["band"], o["kmax"])
+    for gk, ok in (("qc", "qc"), ("kc", "kc"), ("qp", "pq"), ("kp", "pk"), ("idx", "idx"),
+                   ("cnt", "cnt")):
+        assert np.array_equal(g[gk].cpu().numpy(), o[ok]), gk
+    assert np.array_equal(g["qs"].cpu().numpy().view(np.uint32), o["sq"].view(np.uint32))
+    v = dev_bf16(x["v"])
+    out = B.qsa_sparse_attn(g["qc"], g["qs"], g["kc"], g["ks"], v, g["idx"], g["cnt"], w.block)
+    assert_close(host_f64(out), _oracle_attn(o, x, w), what=f"L={L} sparse")
+    order = B.qsa_order_query_blocks(g["idx"], g["cnt"], w.seq_len, w.block, w.head_dim)
+    out_o = B.qsa_sparse_attn_ordered(g["qc"], g["qs"], g["kc"], g["ks"], v, g["idx"], g["cnt"],
+                                      order, w.block)
+    assert np.array_equal(host_bits(out), host_bits(out_o))
+    o_full = _oracle_attn(o, x, w, oracle.full_kept_lists(w.batch, w.heads, w.n_blocks))
+    rng = np.random.default_rng(L)
+    r_prev = dev_bf16(qsa_gen.f32_to_bf16_bits(
+        rng.standard_normal(x["v"].shape).astype(np.float32) * 0.02))
+    for has_prev in (0, 1):
+        res = []
+        for od in (None, order):
+            r = r_prev.clone()
+            dr = torch.zeros_like(v)
+            full = B.qsa_full_attn_residual(g["qc"], g["qs"], g["kc"], g["ks"], v, g["idx"],
+                                            g["cnt"], w.block, r, dr, has_prev, order=od)
+            res.append([host_bits(t) for t in (full, r, dr)])
+        assert_close(oracle.bf16_to_f64(res[0][0]), o_full, what=f"L={L} full")
+        for a_, b_ in zip(*res):
+            assert np.array_equal(a_, b_)
+
+
 def _messy_lists(w, seed):
     """Kept lists with repeats, entries outside [0, nb) and shuffled order."""
     nb = w.n_blocks
