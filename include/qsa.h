@@ -58,7 +58,7 @@ enum qsa_status {
 /* Problem shape shared by all calls. */
 typedef struct qsa_dims {
   int32_t batch;    /* B >= 1 */
-  int32_t heads;    /* H >= 1 */
+  int32_t heads;    /* H >= 1; batch * heads * nb <= QSA_MAX_WORK_BLOCKS */
   int32_t seq_len;  /* L >= 1 */
   int32_t head_dim; /* D: 64 or 128 */
   int32_t block;    /* token block used for quantisation and sparsity: 64 or 128 */
@@ -66,6 +66,9 @@ typedef struct qsa_dims {
 
 /* Largest number of key blocks qsa_select_blocks supports (nb). */
 #define QSA_MAX_BLOCKS 16384
+/* Largest batch * heads * nb of any call (QSA_ERR_SHAPE above it): every
+   launch's grid, in work-items, then fits the 32-bit dispatch size. */
+#define QSA_MAX_WORK_BLOCKS 16777216
 /* Largest number of band offsets. */
 #define QSA_MAX_BAND 8
 /* Largest rank of qsa_project_residual. */

@@ -27,6 +27,7 @@ QSA_ERR_DEVICE = -5
 QSA_ERR_LAUNCH = -6
 QSA_MAX_BAND = 8
 QSA_MAX_BLOCKS = 16384
+QSA_MAX_WORK_BLOCKS = 1 << 24
 QSA_MAX_RANK = 64
 QSA_L1_WORK_BYTES = 16384
 

@@ -54,8 +54,9 @@ int check_dims(const char* fn, const qsa_dims* d) {
     return fail(QSA_ERR_SHAPE, "%s: block=%d must be 64 or 128", fn, d->block);
   const int64_t nb = (d->seq_len + (int64_t)d->block - 1) / d->block;
   const int64_t work = (int64_t)d->batch * d->heads * nb;
-  if (work >= (int64_t)1 << 31)
-    return fail(QSA_ERR_SHAPE, "%s: batch*heads*blocks=%lld is too large", fn, (long long)work);
+  if (work > QSA_MAX_WORK_BLOCKS)
+    return fail(QSA_ERR_SHAPE, "%s: batch*heads*blocks=%lld exceeds QSA_MAX_WORK_BLOCKS=%d", fn,
+                (long long)work, QSA_MAX_WORK_BLOCKS);
   return QSA_OK;
 }
 

@@ -89,11 +89,21 @@ def test_quantize_validation(lib):
     assert _q(lib, _d(), P[:3] + [None]) == B.QSA_ERR_NULL
     assert _q(lib, _d(), [ctypes.c_void_p(0x1008)] + P[1:4]) == B.QSA_ERR_ALIGN
     assert _q(lib, _d(B_=1 << 20, H=1 << 10, L=1 << 12, bs=64)) == B.QSA_ERR_SHAPE
+    # batch * heads * blocks above QSA_MAX_WORK_BLOCKS (grids beyond 32-bit work-item counts)
+    assert _q(lib, _d(B_=256, H=1 << 10, L=64 * 64 + 1)) == B.QSA_ERR_SHAPE
+    assert b"QSA_MAX_WORK_BLOCKS" in lib.qsa_last_error_detail()
+
+
+def test_work_limit_matches_the_header():
+    txt = open(HEADER).read()
+    assert re.search(r"#define QSA_MAX_WORK_BLOCKS (\d+)", txt).group(1) == str(B.QSA_MAX_WORK_BLOCKS)
+    assert B.QSA_MAX_WORK_BLOCKS == 1 << 24
 
 
 @needs_no_gpu
 def test_valid_arguments_reach_the_device_check(lib):
     assert _q(lib, _d()) == B.QSA_ERR_DEVICE
+    assert _q(lib, _d(B_=256, H=1 << 10, L=64 * 64)) == B.QSA_ERR_DEVICE  # at QSA_MAX_WORK_BLOCKS
     band = (ctypes.c_int32 * 1)(0)
     assert lib.qsa_select_blocks(_d(), *P[:4], 1, band, 1, 2, P[4], P[5], None) == B.QSA_ERR_DEVICE
     assert lib.qsa_sparse_attn(_d(), *P[:7], 2, ctypes.c_float(0.125), None, None, P[7],
