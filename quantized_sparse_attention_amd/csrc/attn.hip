@@ -953,33 +953,38 @@ __attribute__((amdgpu_waves_per_eu(JitWalk<BS, D, REFRESH>::on ? QSA_ATTN_JIT_WA
   const float lf = acc.l + __shfl_xor(acc.l, 32, 64);
   const float inv_f = lf > 0.0f ? 1.0f / lf : 0.0f;
   if (!qvalid) return;
+  {
+    // r = full - sparse from the two rounded fp32 outputs: no fused
+    // multiply-subtract, so equal outputs (every block kept) give r = 0 exactly
+#pragma clang fp contract(off)
 #pragma unroll
-  for (int dt = 0; dt < C::DT; ++dt) {
+    for (int dt = 0; dt < C::DT; ++dt) {
 #pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int d0 = 32 * dt + 8 * r4 + 4 * g;
-      const uint2 hi = *reinterpret_cast<const uint2*>(a.dr_out + row_off + d0);
-      const uint2 lw = *reinterpret_cast<const uint2*>(a.out + row_off + d0);
-      float os[4];
-      os[0] = __uint_as_float((hi.x << 16) | (lw.x & 0xffffu));
-      os[1] = __uint_as_float((hi.x & 0xffff0000u) | (lw.x >> 16));
-      os[2] = __uint_as_float((hi.y << 16) | (lw.y & 0xffffu));
-      os[3] = __uint_as_float((hi.y & 0xffff0000u) | (lw.y >> 16));
-      float of[4], rho[4], drv[4];
+      for (int r4 = 0; r4 < 4; ++r4) {
+        const int d0 = 32 * dt + 8 * r4 + 4 * g;
+        const uint2 hi = *reinterpret_cast<const uint2*>(a.dr_out + row_off + d0);
+        const uint2 lw = *reinterpret_cast<const uint2*>(a.out + row_off + d0);
+        float os[4];
+        os[0] = __uint_as_float((hi.x << 16) | (lw.x & 0xffffu));
+        os[1] = __uint_as_float((hi.x & 0xffff0000u) | (lw.x >> 16));
+        os[2] = __uint_as_float((hi.y << 16) | (lw.y & 0xffffu));
+        os[3] = __uint_as_float((hi.y & 0xffff0000u) | (lw.y >> 16));
+        float of[4], rho[4], drv[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        of[e] = acc.o[dt][4 * r4 + e] * inv_f;
-        rho[e] = of[e] - os[e];
-        drv[e] = 0.0f;
+        for (int e = 0; e < 4; ++e) {
+          of[e] = acc.o[dt][4 * r4 + e] * inv_f;
+          rho[e] = of[e] - os[e];
+          drv[e] = 0.0f;
+        }
+        if (a.has_prev) {
+          const float4 rp = load_bf16x4(a.r_out + row_off + d0);
+          drv[0] = rho[0] - rp.x; drv[1] = rho[1] - rp.y;
+          drv[2] = rho[2] - rp.z; drv[3] = rho[3] - rp.w;
+        }
+        store_bf16x4(a.dr_out + row_off + d0, drv[0], drv[1], drv[2], drv[3]);
+        store_bf16x4(a.r_out + row_off + d0, rho[0], rho[1], rho[2], rho[3]);
+        store_bf16x4(a.out + row_off + d0, of[0], of[1], of[2], of[3]);
       }
-      if (a.has_prev) {
-        const float4 rp = load_bf16x4(a.r_out + row_off + d0);
-        drv[0] = rho[0] - rp.x; drv[1] = rho[1] - rp.y;
-        drv[2] = rho[2] - rp.z; drv[3] = rho[3] - rp.w;
-      }
-      store_bf16x4(a.dr_out + row_off + d0, drv[0], drv[1], drv[2], drv[3]);
-      store_bf16x4(a.r_out + row_off + d0, rho[0], rho[1], rho[2], rho[3]);
-      store_bf16x4(a.out + row_off + d0, of[0], of[1], of[2], of[3]);
     }
   }
 }

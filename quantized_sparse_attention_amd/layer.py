@@ -81,13 +81,20 @@ class QuantSparseAttention:
         self.refresh_next = True
 
     def state_dict(self):
-        return {"r": self.r, "dr": self.dr, "has_prev": self.has_prev,
-                "prev_out": self.prev_out, "change": self.change,
+        """A snapshot of the residual cache and trigger state.  Tensors are
+        copies: later steps write r, dr and the previous output in place, and
+        must not change a snapshot already taken."""
+        cp = lambda t: None if t is None else t.clone()  # noqa: E731
+        return {"r": cp(self.r), "dr": cp(self.dr), "has_prev": self.has_prev,
+                "prev_out": cp(self.prev_out), "change": self.change,
                 "refresh_next": self.refresh_next}
 
     def load_state_dict(self, sd):
-        self.r, self.dr, self.has_prev = sd["r"], sd["dr"], bool(sd["has_prev"])
-        self.prev_out = sd.get("prev_out")
+        """Restore a snapshot; the layer keeps copies of its tensors, so the
+        snapshot stays valid after later steps."""
+        cp = lambda t: None if t is None else t.clone()  # noqa: E731
+        self.r, self.dr, self.has_prev = cp(sd["r"]), cp(sd["dr"]), bool(sd["has_prev"])
+        self.prev_out = cp(sd.get("prev_out"))
         self.change = float(sd.get("change", 0.0))
         self.refresh_next = bool(sd.get("refresh_next", self.r is None))
 
