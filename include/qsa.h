@@ -337,6 +337,27 @@ int qsa_l1_change(const qsa_dims* dims, const uint16_t* prev, const uint16_t* cu
                   void* work, uint64_t work_bytes, void* stream);
 
 /*
+ * qsa_l1_change_noalloc -- qsa_l1_change for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, hosts that
+ * forbid allocation): the same sums, with the scratch taken from a fixed
+ * QSA_L1_WORK_BYTES array inside the library instead of a `work` argument.
+ * That array exists once per GPU the library runs on and lives until the
+ * process ends; its device address is looked up on the first call on each
+ * device.  The scratch size does not depend on the input size (the partial
+ * sums are bounded by QSA_L1_WORK_BYTES / 16 blocks), so every size
+ * qsa_l1_change accepts is accepted.  No allocation of any kind.
+ *
+ *   prev, cur in: bf16 [B,H,L,D]
+ *   sums     out: DEVICE fp64 [2]
+ * Calls on one GPU share its scratch: calls that may overlap in time (on
+ * different streams) race and must be serialised by the caller.  Errors as
+ * qsa_l1_change; QSA_ERR_DEVICE if the scratch's address cannot be found on
+ * the current device.
+ */
+int qsa_l1_change_noalloc(const qsa_dims* dims, const uint16_t* prev, const uint16_t* cur,
+                          double* sums, void* stream);
+
+/*
  * qsa_window_kept -- kept lists of block-diagonal attention over windows of
  * `window` consecutive tokens (the passes of SQuad attention, SQuad
  * gist.science/es/paper/2608.16585, technical summary, methodology §1):

@@ -34,7 +34,8 @@ QSA_L1_WORK_BYTES = 16384
 EXPORTED = ("qsa_quantize", "qsa_select_blocks", "qsa_sparse_attn", "qsa_full_attn_residual",
             "qsa_apply_residual", "qsa_order_query_blocks", "qsa_sparse_attn_ordered",
             "qsa_quantize_rotated", "qsa_project_residual", "qsa_project_work_bytes",
-            "qsa_l1_change", "qsa_window_kept", "qsa_reorder_windows", "qsa_squad_attention",
+            "qsa_l1_change", "qsa_l1_change_noalloc", "qsa_window_kept", "qsa_reorder_windows",
+            "qsa_squad_attention",
             "qsa_squad_work_bytes", "qsa_full_attn_residual_ordered",
             "qsa_status_string", "qsa_last_error_detail", "qsa_version")
 
@@ -81,6 +82,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
                                             vp, vp]
     lib.qsa_project_residual.argtypes = [pd, vp, i32, vp, vp, vp, ctypes.c_uint64, vp]
     lib.qsa_l1_change.argtypes = [pd, vp, vp, vp, vp, ctypes.c_uint64, vp]
+    lib.qsa_l1_change_noalloc.argtypes = [pd, vp, vp, vp, vp]
     lib.qsa_window_kept.argtypes = [pd, i32, i32, vp, vp, vp]
     lib.qsa_reorder_windows.argtypes = [pd, i32, i32, vp, vp, vp]
     lib.qsa_squad_attention.argtypes = [pd, vp, vp, vp, i32, f32, vp, vp, ctypes.c_uint64, vp]
@@ -91,6 +93,7 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     for f in ("qsa_quantize", "qsa_quantize_rotated", "qsa_select_blocks", "qsa_sparse_attn",
               "qsa_full_attn_residual", "qsa_apply_residual", "qsa_order_query_blocks",
               "qsa_sparse_attn_ordered", "qsa_project_residual", "qsa_l1_change",
+              "qsa_l1_change_noalloc",
               "qsa_window_kept", "qsa_reorder_windows", "qsa_squad_attention",
               "qsa_full_attn_residual_ordered"):
         getattr(lib, f).restype = ctypes.c_int
@@ -370,6 +373,20 @@ def qsa_l1_change(prev: torch.Tensor, cur: torch.Tensor, sums=None, work=None, s
     _check(load_library().qsa_l1_change(ctypes.byref(d), _ptr(prev), _ptr(cur), _ptr(sums),
                                         _ptr(work), ctypes.c_uint64(work.numel()),
                                         _stream(stream)))
+    return sums
+
+
+def qsa_l1_change_noalloc(prev: torch.Tensor, cur: torch.Tensor, sums: torch.Tensor,
+                          stream=None):
+    """qsa_l1_change with the library's own fixed scratch: the call allocates
+    nothing (``sums``, device fp64 [2], is the caller's)."""
+    _need(prev, "prev", torch.bfloat16)
+    _need(cur, "cur", torch.bfloat16, tuple(prev.shape))
+    _need(sums, "sums", torch.float64, (2,))
+    Bn, H, L, D = prev.shape
+    d = make_dims(Bn, H, L, D, 64)
+    _check(load_library().qsa_l1_change_noalloc(ctypes.byref(d), _ptr(prev), _ptr(cur),
+                                                _ptr(sums), _stream(stream)))
     return sums
 
 

@@ -9,12 +9,21 @@
 // operands whose exponents differ by at most 45) and summed in fp64: per
 // thread in a grid-stride order, then by a fixed tree, then the per-block
 // partials by one wave in a fixed order -- deterministic for a given size.
+#include <mutex>
+
 #include "qsa_internal.h"
+
+// The partial sums of qsa_l1_change_noalloc: a fixed QSA_L1_WORK_BYTES per
+// GPU, held until the process ends.  Host code reaches it only through the
+// per-device address from hipGetSymbolAddress (l1_static_scratch); the name
+// itself is a host-side stand-in, not a device address.
+static __device__ __align__(256) double scratch[QSA_L1_WORK_BYTES / sizeof(double)];
 
 namespace qsa {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kMaxScratchDevices = 64;
 
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
@@ -79,6 +88,24 @@ int l1_change_blocks(uint64_t n_elements) {
   const uint64_t n8 = n_elements / 8;
   uint64_t b = (n8 + kThreads - 1) / kThreads;
   return (int)(b < 1 ? 1 : (b > kL1MaxBlocks ? kL1MaxBlocks : b));
+}
+
+hipError_t l1_static_scratch(double** work) {
+  static std::mutex mu;
+  static double* addr[kMaxScratchDevices] = {};
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    addr[dev] = static_cast<double*>(p);
+  }
+  *work = addr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_l1_change(uint64_t n_elements, const uint16_t* prev, const uint16_t* cur,

@@ -414,6 +414,26 @@ int qsa_l1_change(const qsa_dims* dims, const uint16_t* prev, const uint16_t* cu
                                             static_cast<hipStream_t>(stream)));
 }
 
+int qsa_l1_change_noalloc(const qsa_dims* dims, const uint16_t* prev, const uint16_t* cur,
+                          double* sums, void* stream) {
+  const char* fn = "qsa_l1_change_noalloc";
+  int st = check_dims(fn, dims);
+  if (st) return st;
+  REQUIRE_PTR(prev);
+  REQUIRE_PTR(cur);
+  REQUIRE_PTR(sums);
+  if ((st = check_device(fn))) return st;
+  double* work = nullptr;
+  hipError_t e = qsa::l1_static_scratch(&work);
+  if (e != hipSuccess)
+    return fail(QSA_ERR_DEVICE, "%s: the library's scratch is not available on this device (%s)",
+                fn, hipGetErrorString(e));
+  const uint64_t n = (uint64_t)dims->batch * dims->heads * dims->seq_len * dims->head_dim;
+  (void)hipGetLastError();
+  return launched(fn, qsa::launch_l1_change(n, prev, cur, sums, work,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 int qsa_window_kept(const qsa_dims* dims, int32_t window, int32_t kmax, int32_t* kept_idx,
                     int32_t* kept_cnt, void* stream) {
   const char* fn = "qsa_window_kept";

@@ -122,6 +122,9 @@ constexpr int kL1MaxBlocks = QSA_L1_WORK_BYTES / 16;
 int l1_change_blocks(uint64_t n_elements);
 hipError_t launch_l1_change(uint64_t n_elements, const uint16_t* prev, const uint16_t* cur,
                             double* sums, double* work, hipStream_t s);
+// The current device's address of the library's own QSA_L1_WORK_BYTES scratch
+// (looked up once per device, on that device's first call).
+hipError_t l1_static_scratch(double** work);
 
 // SQuad two-pass attention: scratch layout (byte offsets, 256-aligned).
 struct SquadPlan {

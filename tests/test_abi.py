@@ -236,6 +236,19 @@ def test_l1_change_validation(lib):
         assert l1() == B.QSA_ERR_DEVICE
 
 
+def test_l1_change_noalloc_validation(lib):
+    def l1(dims=None, ptrs=None):
+        p = ptrs or P[:3]
+        return lib.qsa_l1_change_noalloc(dims or _d(), p[0], p[1], p[2], None)
+
+    assert l1(ptrs=[None] + P[1:3]) == B.QSA_ERR_NULL
+    assert l1(ptrs=P[:2] + [None]) == B.QSA_ERR_NULL
+    assert l1(ptrs=P[:2] + [ctypes.c_void_p(0x3008)]) == B.QSA_ERR_ALIGN
+    assert l1(dims=_d(D=32)) == B.QSA_ERR_SHAPE
+    if NO_GPU:
+        assert l1() == B.QSA_ERR_DEVICE
+
+
 def test_squad_validation(lib):
     u64, f = ctypes.c_uint64, ctypes.c_float
     d = _d(L=4096, D=64)
