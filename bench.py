@@ -55,6 +55,11 @@ def parse():
                    help="also run the adaptive-refresh L1 change after every step (timed apart)")
     p.add_argument("--squad", action="store_true",
                    help="also time SQuad two-pass attention on a 65,536-token, 24-head sequence")
+    p.add_argument("--ssar", action="store_true",
+                   help="also measure the residual corrections' error against full attention "
+                        "over a ten-step drifting schedule (F SSSS F SSSS)")
+    p.add_argument("--ssar-workload", default=None,
+                   help="workload of --ssar (default: the bench workload)")
     p.add_argument("--no-peaks", action="store_true",
                    help="skip the MFMA-rate probe (libqsa_probe.so) reported as measured_peaks")
     p.add_argument("--calib-copy-mb", type=int, default=0,
@@ -233,6 +238,113 @@ def squad_measure(Bn, steps, warmup):
                          "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                          "frac": round(alg_bytes / t / PEAK_HBM_BYTES, 4)},
             "attention_passes_mfma_floor_ms": round(tmin * 1e3, 4)}
+
+
+def ssar_measure(w, drift="walk", rank=32, check_blocks=3):
+    """Error of the sparse-step output against full attention on the same
+    quantised Q/K (the refresh kernel's output on the step's inputs), for the
+    corrections of the residual cache over F S S S S F S S S S:
+
+    * sparse: the block-sparse attention alone;
+    * first_order: sparse + r (r cached at the last refresh);
+    * second_order: sparse + r + dr (dr = change of r between the last two
+      refreshes), the method's correction;
+    * second_order_rank<r>: the same with dr projected to its top-r principal
+      components at each refresh;
+    * diagnostic_dr_scaled_by_steps_over_period: sparse + r + (k / 5) dr at the
+      k-th step after a refresh -- not the method (which adds dr unscaled), a
+      measure of how much of the second-order error is dr's extrapolation span.
+
+    ``drift``: "walk" adds fresh N(0, drift_std) to the fp32 state at every step
+    (the workload's recipe); "coherent" adds the same N(0, drift_std) field at
+    every step (a straight trajectory, under which the residual changes
+    linearly).  The full-attention reference is checked against the oracle on
+    a few sampled query blocks of head 0 at every step."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import qsa_gen
+    from quantized_sparse_attention_amd import QSAConfig, QuantSparseAttention
+    from quantized_sparse_attention_amd import binding as Bn
+
+    dev = torch.device("cuda:0")
+    sched = "FSSSSFSSSS"
+    if drift == "walk":
+        xs = qsa_gen.make_qkv_torch(w, dev, step_seeds=list(range(len(sched))))
+    else:
+        x0, x1 = qsa_gen.make_qkv_torch(w, dev, step_seeds=[0, 1])
+        xs = []
+        for s in range(len(sched)):
+            xs.append({t: (x0[t].float() + s * (x1[t].float() - x0[t].float())).to(torch.bfloat16)
+                       for t in "qkv"})
+        del x0, x1
+    cfg = dict(block=w.block, topk=w.topk, band=w.band)
+    variants = {"first_order": QuantSparseAttention(QSAConfig(order=1, **cfg)),
+                "second_order": QuantSparseAttention(QSAConfig(order=2, **cfg)),
+                f"second_order_rank{rank}": QuantSparseAttention(QSAConfig(order=2, rank=rank,
+                                                                           **cfg))}
+    r_tmp = torch.zeros_like(xs[0]["v"])
+    dr_tmp = torch.zeros_like(r_tmp)
+    nb, L, bs = w.n_blocks, w.seq_len, w.block
+    blocks = sorted({0, nb // 2, nb - 1})[:check_blocks]
+    sm = oracle.default_sm_scale(w.head_dim)
+    per_step, worst_ref = [], 0.0
+
+    def rel(a, b):
+        return (torch.linalg.vector_norm((a.float() - b.float()).flatten(), dtype=torch.float64)
+                / torch.linalg.vector_norm(b.float().flatten(), dtype=torch.float64)).item()
+
+    for s, kind in enumerate(sched):
+        x = xs[s]
+        outs = {k: lay.step(x["q"], x["k"], x["v"], refresh=(kind == "F"))
+                for k, lay in variants.items()}
+        lb = variants["second_order"].last
+        full = Bn.qsa_full_attn_residual(lb.q_codes, lb.q_scales, lb.k_codes, lb.k_scales,
+                                         x["v"], lb.kept_idx, lb.kept_cnt, bs, r_tmp, dr_tmp, 0)
+        sparse = Bn.qsa_sparse_attn(lb.q_codes, lb.q_scales, lb.k_codes, lb.k_scales, x["v"],
+                                    lb.kept_idx, lb.kept_cnt, bs)
+        torch.cuda.synchronize()
+        # the reference against the oracle (head 0, sampled query blocks)
+        qc = lb.q_codes[:, :1].cpu().numpy()
+        kc = lb.k_codes[:, :1].cpu().numpy()
+        qs = lb.q_scales[:, :1].cpu().numpy()
+        ks = lb.k_scales[:, :1].cpu().numpy()
+        vb = x["v"][:, :1].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+        fi, fc = oracle.full_kept_lists(1, 1, nb)
+        ref = oracle.attention(qc, qs, kc, ks, vb, fi, fc, bs, sm,
+                               which=[(0, 0, i) for i in blocks])
+        for (b, h, i), o in ref.items():
+            got = full[0, 0, i * bs: i * bs + o.shape[0]].float().cpu().numpy()
+            worst_ref = max(worst_ref, float(np.linalg.norm(got - o) / np.linalg.norm(o)))
+        row = {"step": s, "kind": kind}
+        if kind == "F":
+            last_f = s
+        else:
+            lay = variants["second_order"]
+            # diagnostic, not the method: dr scaled by the steps since the
+            # refresh over the refresh period (a linear extrapolation of r)
+            k = (s - last_f) / 5.0
+            lin = sparse.float() + lay.r.float() + k * lay.dr.float()
+            row["rel_l2"] = {"sparse": round(rel(sparse, full), 6),
+                             **{k_: round(rel(o, full), 6) for k_, o in outs.items()},
+                             "diagnostic_dr_scaled_by_steps_over_period": round(rel(lin, full), 6)}
+            del lin
+        per_step.append(row)
+        del outs, full, sparse
+    s_rows = [r for r in per_step if r["kind"] == "S"]
+    keys = list(s_rows[0]["rel_l2"])
+    after = [r for r in s_rows if r["step"] > 5]
+    return {
+        "workload": w.name, "schedule": sched, "drift": drift,
+        "reference": "full attention on the same int8 codes (refresh kernel output)",
+        "reference_vs_oracle_max_rel_l2": round(worst_ref, 6),
+        "per_step": per_step,
+        "mean_rel_l2_all_sparse_steps": {k: round(float(np.mean([r["rel_l2"][k] for r in s_rows])),
+                                                  6) for k in keys},
+        "mean_rel_l2_after_second_refresh": {
+            k: round(float(np.mean([r["rel_l2"][k] for r in after])), 6) for k in keys},
+    }
 
 
 def main():
@@ -451,6 +563,9 @@ def main():
         del inputs, qc, kc, qp, kp, kept, out, r, dr
         torch.cuda.empty_cache()
         res["squad"] = squad_measure(Bn, max(3, args.steps), 1)
+    if args.ssar:
+        sw = qsa_gen.get_workload(args.ssar_workload or args.workload)
+        res["ssar"] = [ssar_measure(sw, drift) for drift in ("walk", "coherent")]
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, args.rotate)
     print(json.dumps(res), flush=True)
