@@ -55,6 +55,9 @@ def parse():
                    help="also run the adaptive-refresh L1 change after every step (timed apart)")
     p.add_argument("--squad", action="store_true",
                    help="also time SQuad two-pass attention on a 65,536-token, 24-head sequence")
+    p.add_argument("--cold-cycles", type=int, default=1,
+                   help="cycles of the cold pass (a 1 GiB scrub before every layer step), "
+                        "reported apart from the headline; 0 skips it")
     p.add_argument("--ssar", action="store_true",
                    help="also measure the residual corrections' error against full attention "
                         "over a ten-step drifting schedule (F SSSS F SSSS)")
@@ -109,6 +112,7 @@ def measured_peaks(stream, blocks=2048, iters=40000):
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_sparse_attn_wan14b_720p.json")
+REFRESH_TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_refresh_wan14b_720p.json")
 ATTN_SOURCE = os.path.join(ROOT, "quantized_sparse_attention_amd", "csrc", "attn.hip")
 # the processing order decides which tiles neighbouring workgroups share
 ORDER_SOURCE = os.path.join(ROOT, "quantized_sparse_attention_amd", "csrc", "order.hip")
@@ -120,12 +124,12 @@ def source_digest(path):
         return hashlib.sha256(f.read()).hexdigest()
 
 
-def measured_traffic(workload):
-    """HBM bytes per launch of the sparse attention kernel from the committed
-    PMC record, or None when there is none for this workload or the kernel or
+def measured_traffic(workload, record=TRAFFIC_RECORD):
+    """HBM bytes per launch of an attention kernel from its committed PMC
+    record, or None when there is none for this workload or the kernel or
     ordering source changed since the counters were taken."""
     try:
-        with open(TRAFFIC_RECORD) as f:
+        with open(record) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
@@ -134,6 +138,28 @@ def measured_traffic(workload):
             or rec.get("order_source_sha256") != source_digest(ORDER_SOURCE)):
         return None
     return rec.get("traffic_bytes_per_launch")
+
+
+def stats(xs):
+    """mean, median, min and p90 (nearest rank) of a list of times in ms."""
+    if not xs:
+        return None
+    v = sorted(xs)
+    p90 = v[min(len(v) - 1, max(0, int(-(-0.9 * len(v) // 1)) - 1))]
+    med = v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+    return {"mean": round(sum(v) / len(v), 4), "median": round(med, 4), "min": round(v[0], 4),
+            "p90": round(p90, 4), "n": len(v)}
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def kept_tile_ops(kept_idx, kept_cnt, seq_len, block, head_dim):
@@ -198,6 +224,8 @@ def cpu_baseline(w, budget_s: float, rotate: bool = False):
                    f"({t_attn:.1f} s); scaled x{nb}/{done} blocks and x{w.heads * w.batch} heads "
                    f"(extrapolated)"),
         "host_cpus": os.cpu_count(),
+        "affinity_cpus": len(os.sched_getaffinity(0)),
+        "cpu_model": cpu_model(),
     }
 
 
@@ -460,22 +488,52 @@ def main():
     def mean(xs):
         return sum(xs) / len(xs) if xs else float("nan")
 
-    t_quant, t_sel, t_sparse, t_full, t_order, step_sp, step_f = [], [], [], [], [], [], []
-    t_proj, t_l1 = [], []
-    for kind, s, e, projected in recs:
-        if args.l1_change:
-            t_l1.append(e[6].elapsed_time(e[7]))
-        t_quant.append(e[0].elapsed_time(e[1]))
-        t_sel.append(e[1].elapsed_time(e[2]))
-        if kind == "S":
-            t_order.append(e[2].elapsed_time(e[4]))
-            t_sparse.append(e[4].elapsed_time(e[3]))  # the attention launch alone
-        else:
-            t_order.append(e[2].elapsed_time(e[8]))
-            t_full.append(e[8].elapsed_time(e[4]))  # the refresh launch alone
-            if projected:
-                t_proj.append(e[4].elapsed_time(e[5]))
-        (step_sp if kind == "S" else step_f).append(e[0].elapsed_time(e[3]))
+    def collect(records):
+        """Per-launch and per-step times (ms) from the HIP events of a run."""
+        t = {k: [] for k in ("quant_pair", "select", "order", "sparse", "full", "proj", "l1",
+                             "step_sparse", "step_refresh")}
+        for kind, s, e, projected in records:
+            if args.l1_change:
+                t["l1"].append(e[6].elapsed_time(e[7]))
+            t["quant_pair"].append(e[0].elapsed_time(e[1]))
+            t["select"].append(e[1].elapsed_time(e[2]))
+            if kind == "S":
+                t["order"].append(e[2].elapsed_time(e[4]))
+                t["sparse"].append(e[4].elapsed_time(e[3]))  # the attention launch alone
+            else:
+                t["order"].append(e[2].elapsed_time(e[8]))
+                t["full"].append(e[8].elapsed_time(e[4]))  # the refresh launch alone
+                if projected:
+                    t["proj"].append(e[4].elapsed_time(e[5]))
+            t["step_sparse" if kind == "S" else "step_refresh"].append(e[0].elapsed_time(e[3]))
+        return t
+
+    tt = collect(recs)
+    t_quant, t_sel, t_sparse, t_full = tt["quant_pair"], tt["select"], tt["sparse"], tt["full"]
+    t_order, step_sp, step_f, t_proj, t_l1 = (tt["order"], tt["step_sparse"], tt["step_refresh"],
+                                              tt["proj"], tt["l1"])
+    # cold pass (not part of the headline): a 1 GiB write between consecutive
+    # layer steps evicts the L2s and the memory-side cache, so every launch
+    # starts from HBM
+    cold = None
+    if args.cold_cycles > 0:
+        scrub = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev)
+        crecs = []
+        for _ in range(args.cold_cycles):
+            for s, kind in enumerate(schedule):
+                scrub.fill_(float(s))
+                layer_step(s, kind, crecs)
+        torch.cuda.synchronize()
+        ct = collect(crecs)
+        cold = {"scrub": "1 GiB written before every layer step",
+                "cycles": args.cold_cycles,
+                "sparse_step_ms": stats(ct["step_sparse"]),
+                "refresh_step_ms": stats(ct["step_refresh"]),
+                "qsa_sparse_attn_ordered_ms": stats(ct["sparse"]),
+                "qsa_full_attn_residual_ms": stats(ct["full"]),
+                "qsa_select_blocks_ms": stats(ct["select"]),
+                "qsa_quantize_pair_ms": stats(ct["quant_pair"])}
+        del scrub
 
     # kept-tile work of the sparse steps (exact, from this run's kept lists)
     sp_steps = [s for s, k in enumerate(schedule) if k == "S"]
@@ -522,6 +580,19 @@ def main():
         "sparse_step_ms_per_layer": round(ms_sparse, 4),
         "refresh_step_ms_per_layer": round(ms_refresh, 4),
         "cycle_avg_ms_per_layer": round(ms_per_step / len(schedule), 4),
+        "secondary": {"metric": "ms/layer averaged over the %s cycle (refresh included)" % schedule,
+                      "value": round(ms_per_step / len(schedule), 4), "unit": "ms/layer",
+                      "higher_is_better": False},
+        "timing": {
+            "warm": "back-to-back steps; per launch and per step over the timed region",
+            "sparse_step_ms": stats(step_sp),
+            "refresh_step_ms": stats(step_f),
+            "qsa_sparse_attn_ordered_ms": stats(t_sparse),
+            "qsa_full_attn_residual_ms": stats(t_full),
+            "qsa_select_blocks_ms": stats(t_sel),
+            "qsa_order_query_blocks_ms": stats(t_order),
+            "qsa_quantize_pair_ms": stats(t_quant),
+        },
         "kernels_ms": {
             quant.__name__: round(t_q1 * 1e3, 4),
             "qsa_select_blocks": round(mean(t_sel), 4),
@@ -547,13 +618,16 @@ def main():
             "qsa_full_attn_residual": {
                 "bound": "mfma", "achieved": round(2 * dops / t_ref / 1e12, 1) if t_ref else None,
                 "peak": round(ref_peak / 1e12, 1), "unit": "TFLOP/s",
-                "frac": round(2 * dops / t_ref / ref_peak, 4) if t_ref else None},
+                "frac": round(2 * dops / t_ref / ref_peak, 4) if t_ref else None,
+                "traffic": measured_traffic(w.name, REFRESH_TRAFFIC_RECORD)},
             quant.__name__: {
                 "bound": "hbm", "achieved": round(q_bytes / t_q1 / 1e9, 1) if t_q1 else None,
                 "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
                 "frac": round(q_bytes / t_q1 / PEAK_HBM_BYTES, 4) if t_q1 else None},
         },
     }
+    if cold is not None:
+        res["cold"] = cold
     if not args.no_peaks:
         pk = measured_peaks(stream)
         if "mixed_tops" in pk and t_attn > 0:

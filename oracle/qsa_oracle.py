@@ -74,7 +74,11 @@ R11 SQuad two-pass attention (SQuad, gist.science/es/paper/2608.16585,
     the local pass quantises Q and K in the natural order, the global pass in
     position-major order (token s of window k at index p*(n/w) + k), so that
     each pass's groups are runs of whole 64-token blocks; w and n/w must be
-    multiples of the block.  The page sets w = sqrt(n).
+    multiples of the block.  The page sets w = sqrt(n).  The page does not
+    say whether the global pass sees the same quantisation; re-quantising per
+    pass is the reading that fits a per-block-scale attention core.  The
+    other reading, one quantisation shared by both passes, changes only the
+    global pass's scales and is not the one taken here.
 """
 from __future__ import annotations
 

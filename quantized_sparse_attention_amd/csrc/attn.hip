@@ -999,10 +999,12 @@ hipError_t launch_t(const qsa_dims& d, const AttnArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Query blocks per workgroup: the sparse kernel groups blocks so that key
-// tiles kept by several of them are loaded once (the waves of a group split
-// each tile's loads evenly, which bounds the group size); the refresh kernel
-// runs one block per workgroup.
+// Query blocks per workgroup, the same for the sparse and the refresh kernel:
+// a group's blocks share every key tile that more than one of them needs
+// (kept tiles in the sparse walk; in the refresh, also the tiles outside
+// their kept sets), and the waves of a group split each tile's loads evenly,
+// which bounds the group size.  Two 64-token blocks for the 64-token kernels
+// and for 128-token blocks with D = 128, one for 128-token blocks with D = 64.
 template <bool REFRESH>
 hipError_t dispatch(const qsa_dims& d, const AttnArgs& a, hipStream_t s) {
   constexpr int Q64 = QSA_ATTN_QB;
