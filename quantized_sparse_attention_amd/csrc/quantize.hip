@@ -25,12 +25,16 @@
 // above.  Since H_D H_D^T = D I, (q H)(k H)^T = D (q k^T): attention on
 // rotated codes uses sm_scale / D.  A lane holds 8 consecutive channels, so
 // stages h < 8 run in registers and h >= 8 exchange with the lane h/8 away.
+#include <type_traits>
+
 #include "qsa_internal.h"
 
 #pragma clang fp contract(off)
 
 namespace qsa {
 namespace {
+
+typedef short v2s16 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -39,7 +43,8 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // code = clamp(rint(fl32(x / s)), -127, 127) for a block scale s > 0 with
-// |x| <= 127 s (the clamp only guards the contract).
+// |x| <= 127 s (the clamp only guards the contract), returned as the fp32
+// value of that integer.
 //
 // Without a division per element: with inv = fl32(1 / s), p = fl32(x * inv)
 // is within 127 * 2^-23 < 2^-16 of the exact quotient q = x / s, and so is
@@ -50,27 +55,67 @@ __device__ __forceinline__ float wave_max(float v) {
 // test move it by less than 2^-23 s), so c is right; otherwise the element
 // takes the IEEE division.  Needs 1 / s finite and s 2^-14 normal: the caller
 // takes the division for every element when s < 2^-100.
+__device__ __forceinline__ bool near_half(float x, float c, float s) {
+  const float d = __builtin_fmaf(-c, s, x);
+  return !(fabsf(fabsf(d) - 0.5f * s) > s * 0x1p-14f);
+}
+
 __device__ __forceinline__ void codes8(const float (&x)[8], float s, float inv, bool fast,
-                                       int (&c)[8]) {
-  float q[8];
-  bool any_div = !fast;
-  uint32_t div = fast ? 0u : 0xffu;  // elements that take the division
+                                       float (&q)[8]) {
+  bool any_div = !fast;  // one flag per lane; the rare branch re-tests each element
   if (fast) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       q[e] = __builtin_rintf(x[e] * inv);
-      const float d = __builtin_fmaf(-q[e], s, x[e]);
-      if (!(fabsf(fabsf(d) - 0.5f * s) > s * 0x1p-14f)) div |= 1u << e;
+      any_div |= near_half(x[e], q[e], s);
     }
-    any_div = div != 0u;
   }
   if (any_div) {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      if ((div >> e) & 1u) q[e] = __builtin_rintf(x[e] / s);
+      if (!fast || near_half(x[e], q[e], s)) q[e] = __builtin_rintf(x[e] / s);
   }
 #pragma unroll
-  for (int e = 0; e < 8; ++e) c[e] = (int)fminf(fmaxf(q[e], -127.0f), 127.0f);
+  for (int e = 0; e < 8; ++e) q[e] = __builtin_amdgcn_fmed3f(q[e], -127.0f, 127.0f);
+}
+
+// Eight integer-valued floats in [-127, 127] to their int8 bytes (lo: e 0-3,
+// hi: e 4-7) and to four pairs of int16 (pairs[k] holds elements 2k, 2k+1).
+// Adding 1.5 * 2^23 is exact and leaves the integer's two's complement in the
+// low mantissa bits; byte permutes then gather them.
+__device__ __forceinline__ void pack_codes(const float (&q)[8], uint32_t& lo, uint32_t& hi,
+                                           uint32_t (&pairs)[4]) {
+  uint32_t b[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) b[e] = __float_as_uint(q[e] + 0x1.8p23f);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) pairs[k] = __builtin_amdgcn_perm(b[2 * k + 1], b[2 * k], 0x05040100u);
+  lo = __builtin_amdgcn_perm(pairs[1], pairs[0], 0x06040200u);
+  hi = __builtin_amdgcn_perm(pairs[3], pairs[2], 0x06040200u);
+}
+
+__device__ __forceinline__ uint32_t add_i16x2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_bit_cast(v2s16, a) + __builtin_bit_cast(v2s16, b));
+}
+
+// The value of lane (lane ^ M) for M < 16, moved with DPP inside the lane's
+// row of 16 (no LDS crossbar): lane distances 1 and 2 by quad permutes, 8 by
+// a rotate of the row by 8 (its own inverse); 4 by the row rotate by 4 or by
+// 12, whichever brings lane ^ 4 (take4: this lane's choice, found once by
+// moving the lane ids themselves).
+template <int M>
+__device__ __forceinline__ float lane_xor(float v, bool take4) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8, "partners inside a row of 16 lanes");
+  const int x = __float_as_int(v);
+  if constexpr (M == 4) {
+    const int a = __builtin_amdgcn_update_dpp(0, x, 0x124, 0xF, 0xF, true);  // row_ror:4
+    const int b = __builtin_amdgcn_update_dpp(0, x, 0x12C, 0xF, 0xF, true);  // row_ror:12
+    return __int_as_float(take4 ? a : b);
+  } else {
+    // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_ror:8
+    constexpr int ctrl = M == 1 ? 0xB1 : M == 2 ? 0x4E : 0x128;
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, x, ctrl, 0xF, 0xF, true));
+  }
 }
 
 // In-place fast Walsh-Hadamard transform of one token row held 8 channels
@@ -87,15 +132,20 @@ __device__ __forceinline__ void fwht_row(float (&v)[8], int lane) {
       v[e + h] = a - b;
     }
   }
+  const bool take4 = __builtin_amdgcn_update_dpp(0, lane, 0x124, 0xF, 0xF, true) == (lane ^ 4);
+  auto stage = [&](auto mc) {  // h = 8 m: the partner lane is lane ^ m
+    constexpr int m = decltype(mc)::value;
+    // lower lane: v_j + v_{j+h}; upper lane: v_j - v_{j+h}.  One fused
+    // multiply-add by +-1 rounds exactly as that sum or difference.
+    const float sgn = (lane & m) != 0 ? -1.0f : 1.0f;
 #pragma unroll
-  for (int m = 1; m < CPR; m <<= 1) {  // h = 8 m: the partner lane is lane ^ m
-    const bool upper = (lane & m) != 0;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float o = __shfl_xor(v[e], m, 64);
-      v[e] = upper ? o - v[e] : v[e] + o;  // lower: v_j + v_{j+h}; upper: v_j - v_{j+h}
-    }
-  }
+    for (int e = 0; e < 8; ++e) v[e] = __builtin_fmaf(sgn, v[e], lane_xor<m>(v[e], take4));
+  };
+  if constexpr (CPR > 1) stage(std::integral_constant<int, 1>{});
+  if constexpr (CPR > 2) stage(std::integral_constant<int, 2>{});
+  if constexpr (CPR > 4) stage(std::integral_constant<int, 4>{});
+  if constexpr (CPR > 8) stage(std::integral_constant<int, 8>{});
+  static_assert(CPR <= 16, "rows of at most 16 lanes");
 }
 
 // MAP: the rows are quantised in position-major order of windows of w tokens
@@ -157,29 +207,26 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   const bool fast = s >= 0x1p-100f;
   const float inv = fast ? 1.0f / s : 0.0f;
 
-  int psum[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) psum[e] = 0;
+  // per-channel code sums as packed int16 pairs: a block sum is at most
+  // 127 * BS in magnitude
+  static_assert(127 * BS <= 32767, "block code sums must fit int16");
+  uint32_t psum[4] = {0u, 0u, 0u, 0u};
 
 #pragma unroll
   for (int p = 0; p < PASSES; ++p) {
     const int row = r0 + p * RPP;
     if (row < n) {
-      int c[8];
+      float q[8];
       if (s > 0.0f) {
-        codes8(y[p], s, inv, fast, c);
+        codes8(y[p], s, inv, fast, q);
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) c[e] = 0;
+        for (int e = 0; e < 8; ++e) q[e] = 0.0f;
       }
-      uint32_t lo = 0, hi = 0;
+      uint32_t lo, hi, pairs[4];
+      pack_codes(q, lo, hi, pairs);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        lo |= (uint32_t)(c[e] & 0xff) << (8 * e);
-        hi |= (uint32_t)(c[4 + e] & 0xff) << (8 * e);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) psum[e] += c[e];
+      for (int k = 0; k < 4; ++k) psum[k] = add_i16x2(psum[k], pairs[k]);
       *reinterpret_cast<uint2*>(cb + (size_t)row * D) = make_uint2(lo, hi);
     }
   }
@@ -188,11 +235,15 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
 #pragma unroll
   for (int o = CPR; o < 64; o <<= 1) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) psum[e] += __shfl_xor(psum[e], o, 64);
+    for (int k = 0; k < 4; ++k)
+      psum[k] = add_i16x2(psum[k], (uint32_t)__shfl_xor((int)psum[k], o, 64));
   }
   if (lane < CPR) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) s_pool[wave][lane * 8 + e] = psum[e];
+    for (int k = 0; k < 4; ++k) {
+      s_pool[wave][lane * 8 + 2 * k] = (int16_t)(psum[k] & 0xffffu);
+      s_pool[wave][lane * 8 + 2 * k + 1] = (int16_t)(psum[k] >> 16);
+    }
   }
   __syncthreads();
   const uint64_t blk = bh * (uint64_t)nb + i;
