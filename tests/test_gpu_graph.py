@@ -1,0 +1,116 @@
+"""HIP-graph capture of the hot path's two step kinds.
+
+Every entry point takes its buffers from the caller, allocates nothing and
+records no memset, so a sparse step (quantise Q and K, select, order, the
+sparse attention with the cached r and dr) and a refresh step (the same front
+end, then full + sparse attention writing r and dr in place) can each be
+captured once and replayed on new inputs copied into the captured buffers.
+A serving loop would do this to drop the per-launch host cost.  Every replay
+must be bit-identical to the same calls made eagerly on the same inputs, over
+a drifting F S F S S schedule (the first refresh eager on both sides) with the
+residual cache carried from step to step on both sides; the replays alternate
+with eager work and synchronisations.
+"""
+import pytest
+import torch
+
+import qsa_gen
+from quantized_sparse_attention_amd import binding as B
+from tests.gpu_util import dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+# Wan2.1 480p recipe on a short ragged sequence: 1,581 tokens, 25 blocks of 64
+W = qsa_gen.get_workload("wan13b_480p").with_(grid=(3, 17, 31), heads=4)
+
+
+class StepBuffers:
+    """Every buffer one step reads or writes, allocated once."""
+
+    def __init__(self, shape, dev):
+        Bn, H, L, D = shape
+        nb = B.n_blocks(L, W.block)
+        self.q, self.k, self.v = (torch.empty(shape, dtype=torch.bfloat16, device=dev)
+                                  for _ in range(3))
+        self.qc = torch.empty(shape, dtype=torch.int8, device=dev)
+        self.kc = torch.empty(shape, dtype=torch.int8, device=dev)
+        self.qs = torch.empty((Bn, H, nb), dtype=torch.float32, device=dev)
+        self.ks = torch.empty((Bn, H, nb), dtype=torch.float32, device=dev)
+        self.qp = torch.empty((Bn, H, nb, D), dtype=torch.int32, device=dev)
+        self.kp = torch.empty((Bn, H, nb, D), dtype=torch.int32, device=dev)
+        self.idx = torch.empty((Bn, H, nb, W.kmax), dtype=torch.int32, device=dev)
+        self.cnt = torch.empty((Bn, H, nb), dtype=torch.int32, device=dev)
+        self.order = torch.empty((Bn, H, nb), dtype=torch.int32, device=dev)
+        self.r = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+        self.dr = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        self.L, self.D = L, D
+
+    def load(self, x):
+        self.q.copy_(x["q"])
+        self.k.copy_(x["k"])
+        self.v.copy_(x["v"])
+
+    def step(self, refresh: bool, has_prev: bool = True):
+        B.qsa_quantize(self.q, W.block, self.qc, self.qs, self.qp)
+        B.qsa_quantize(self.k, W.block, self.kc, self.ks, self.kp)
+        B.qsa_select_blocks(self.qp, self.qs, self.kp, self.ks, self.L, W.block, W.topk,
+                            W.band, W.kmax, self.idx, self.cnt)
+        B.qsa_order_query_blocks(self.idx, self.cnt, self.L, W.block, self.D, self.order)
+        args = (self.qc, self.qs, self.kc, self.ks, self.v, self.idx, self.cnt)
+        if refresh:
+            B.qsa_full_attn_residual(*args, W.block, self.r, self.dr, has_prev,
+                                     out_full=self.out, order=self.order)
+        else:
+            B.qsa_sparse_attn_ordered(*args, self.order, W.block, r=self.r, dr=self.dr,
+                                      out=self.out)
+
+    def snapshot(self):
+        names = ("qc", "qs", "qp", "kc", "ks", "kp", "idx", "cnt", "order", "r", "dr", "out")
+        return {n: getattr(self, n).clone() for n in names}
+
+
+def _same(a: torch.Tensor, b: torch.Tensor) -> bool:
+    return torch.equal(a.view(torch.uint8) if a.dtype == torch.bfloat16 else a,
+                       b.view(torch.uint8) if b.dtype == torch.bfloat16 else b)
+
+
+def test_captured_steps_replay_bit_identical():
+    steps = qsa_gen.make_qkv_steps(W, 5)
+    xs = [{t: dev_bf16(st[t]) for t in "qkv"} for st in steps]
+    shape = tuple(xs[0]["q"].shape)
+    dev = xs[0]["q"].device
+    g_buf, e_buf = StepBuffers(shape, dev), StepBuffers(shape, dev)
+
+    # step 0 (the first refresh, no previous one) runs eagerly on both sides;
+    # it also makes each entry point's one-time device check before capture
+    for b in (g_buf, e_buf):
+        b.load(xs[0])
+        b.step(refresh=True, has_prev=False)
+    torch.cuda.synchronize()
+    assert all(_same(u, v) for u, v in zip(g_buf.snapshot().values(),
+                                           e_buf.snapshot().values()))
+
+    sparse_g, refresh_g = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(sparse_g):
+        g_buf.step(refresh=False)
+    with torch.cuda.graph(refresh_g):
+        g_buf.step(refresh=True, has_prev=True)
+    torch.cuda.synchronize()
+
+    outs = []
+    for s, kind in zip(range(1, 5), "SFSS"):
+        g_buf.load(xs[s])
+        (refresh_g if kind == "F" else sparse_g).replay()
+        e_buf.load(xs[s])
+        e_buf.step(refresh=(kind == "F"), has_prev=True)
+        torch.cuda.synchronize()
+        got, want = g_buf.snapshot(), e_buf.snapshot()
+        for n in want:
+            assert _same(got[n], want[n]), f"step {s} ({kind}): {n} differs from the eager run"
+        # eager work of the program's own between replays
+        assert torch.isfinite(got["out"].float()).all()
+        outs.append(got["out"])
+        torch.cuda.synchronize()
+    # the replays did run on the new inputs
+    assert not _same(outs[0], outs[2])
