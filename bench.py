@@ -63,6 +63,9 @@ def parse():
                         "over a ten-step drifting schedule (F SSSS F SSSS)")
     p.add_argument("--ssar-workload", default=None,
                    help="workload of --ssar (default: the bench workload)")
+    p.add_argument("--no-select-work", action="store_true",
+                   help="select with qsa_select_blocks (keys in LDS, one pass) instead of "
+                        "qsa_select_blocks_work (score keys of every slice in a workspace)")
     p.add_argument("--no-peaks", action="store_true",
                    help="skip the MFMA-rate probe (libqsa_probe.so) reported as measured_peaks")
     p.add_argument("--calib-copy-mb", type=int, default=0,
@@ -419,6 +422,9 @@ def main():
     r = torch.zeros((B, H, L, D), dtype=torch.bfloat16, device=dev)
     dr = torch.zeros_like(r)
     state = {"has_prev": False}
+    # the select's score keys, every (batch, head) slice in one pass
+    sel_work = (None if args.no_select_work else
+                mk((Bn.qsa_select_slice_bytes(B, H, L, D, bs) * B * H,), torch.uint8))
     if args.l1_change:
         prev_out = torch.zeros_like(r)
         l1_sums = mk((2,), torch.float64)
@@ -443,7 +449,7 @@ def main():
         quant(x["q"], bs, qc, qs, qp)
         quant(x["k"], bs, kc, ks, kp)
         e[1].record(stream)
-        Bn.qsa_select_blocks(qp, qs, kp, ks, L, bs, w.topk, w.band, kmax, idx, cnt)
+        Bn.qsa_select_blocks(qp, qs, kp, ks, L, bs, w.topk, w.band, kmax, idx, cnt, work=sel_work)
         e[2].record(stream)
         if kind == "F":
             Bn.qsa_order_query_blocks(idx, cnt, L, bs, D, order)
@@ -573,6 +579,8 @@ def main():
                    "block": bs, "topk": w.topk, "band": list(w.band),
                    "density_kept": round(density, 4), "schedule": schedule,
                    "rotated_quantisation": bool(args.rotate),
+                   "select": ("qsa_select_blocks" if args.no_select_work else
+                              "qsa_select_blocks_work, score keys of all slices in one pass"),
                    "residual_rank": args.rank,
                    "step": "one denoising cycle (%s) of one attention layer" % schedule},
         "effective_tops": round(achieved / 1e12, 1),

@@ -22,8 +22,8 @@
  *   - Every tensor pointer must be 16-byte aligned (QSA_ERR_ALIGN).
  *   - The caller owns all memory.  The library allocates nothing and keeps no
  *     state between calls; calls are re-entrant.  Only qsa_project_residual,
- *     qsa_l1_change and qsa_squad_attention need scratch memory, which their
- *     caller passes in.
+ *     qsa_l1_change, qsa_squad_attention and qsa_select_blocks_work use
+ *     scratch memory, which their caller passes in.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream)
  *     and runs asynchronously.  Argument errors are detected on the host
  *     before anything is enqueued; device faults surface at the caller's next
@@ -149,6 +149,34 @@ int qsa_select_blocks(const qsa_dims* dims, const int32_t* pooled_q, const float
                       const int32_t* pooled_k, const float* scale_k, int32_t topk,
                       const int32_t* band_offsets, int32_t n_band, int32_t kmax,
                       int32_t* kept_idx, int32_t* kept_cnt, void* stream);
+
+/*
+ * qsa_select_blocks_work -- qsa_select_blocks through a caller-provided
+ * workspace, with the same kept_idx and kept_cnt bit for bit (the mask of
+ * technical summary §1, §2A and §4, as above).  The scores of whole (b, h)
+ * slices are written to `work` as 64-bit order keys (nb rows of nb keys,
+ * padded to a multiple of 16: qsa_select_slice_bytes per slice), then each
+ * query block's top-k is selected
+ * from them; a pass takes as many slices as work_bytes holds.  That spends
+ * device memory and two passes over the keys in HBM on parallelism:
+ * qsa_select_blocks keeps the keys of 16 query blocks in LDS, so one
+ * workgroup fills a CU.  With work = NULL, work_bytes below one slice, or
+ * nb > 2048, it runs as qsa_select_blocks.
+ *
+ *   work        in: device scratch, 16-byte aligned, or NULL; its contents are
+ *                   undefined afterwards.  Calls that share it must not overlap.
+ *   work_bytes  in: its size in bytes
+ * Errors as qsa_select_blocks; QSA_ERR_ALIGN if work is not 16-byte aligned.
+ */
+int qsa_select_blocks_work(const qsa_dims* dims, const int32_t* pooled_q, const float* scale_q,
+                           const int32_t* pooled_k, const float* scale_k, int32_t topk,
+                           const int32_t* band_offsets, int32_t n_band, int32_t kmax,
+                           int32_t* kept_idx, int32_t* kept_cnt, void* work,
+                           uint64_t work_bytes, void* stream);
+
+/* Bytes of one (b, h) slice of qsa_select_blocks_work's keys:
+   nb * ceil(nb / 16) * 16 * 8 (0 for invalid dims). */
+uint64_t qsa_select_slice_bytes(const qsa_dims* dims);
 
 /*
  * qsa_sparse_attn -- block-sparse attention on int8 Q/K codes, with the

@@ -37,6 +37,7 @@ EXPORTED = ("qsa_quantize", "qsa_select_blocks", "qsa_sparse_attn", "qsa_full_at
             "qsa_l1_change", "qsa_l1_change_noalloc", "qsa_window_kept", "qsa_reorder_windows",
             "qsa_squad_attention",
             "qsa_squad_work_bytes", "qsa_full_attn_residual_ordered",
+            "qsa_select_blocks_work", "qsa_select_slice_bytes",
             "qsa_status_string", "qsa_last_error_detail", "qsa_version")
 
 
@@ -71,6 +72,10 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.qsa_quantize.argtypes = [pd, vp, vp, vp, vp, vp]
     lib.qsa_quantize_rotated.argtypes = [pd, vp, vp, vp, vp, vp]
     lib.qsa_select_blocks.argtypes = [pd, vp, vp, vp, vp, i32, vp, i32, i32, vp, vp, vp]
+    lib.qsa_select_blocks_work.argtypes = [pd, vp, vp, vp, vp, i32, vp, i32, i32, vp, vp, vp,
+                                           ctypes.c_uint64, vp]
+    lib.qsa_select_slice_bytes.argtypes = [pd]
+    lib.qsa_select_slice_bytes.restype = ctypes.c_uint64
     lib.qsa_sparse_attn.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, i32, f32, vp, vp, vp, vp]
     lib.qsa_full_attn_residual.argtypes = [pd, vp, vp, vp, vp, vp, vp, vp, i32, f32, i32, vp, vp,
                                            vp, vp]
@@ -90,7 +95,8 @@ def load_library(path: str | None = None) -> ctypes.CDLL:
     lib.qsa_squad_work_bytes.restype = ctypes.c_uint64
     lib.qsa_project_work_bytes.argtypes = [pd, i32]
     lib.qsa_project_work_bytes.restype = ctypes.c_uint64
-    for f in ("qsa_quantize", "qsa_quantize_rotated", "qsa_select_blocks", "qsa_sparse_attn",
+    for f in ("qsa_quantize", "qsa_quantize_rotated", "qsa_select_blocks",
+              "qsa_select_blocks_work", "qsa_sparse_attn",
               "qsa_full_attn_residual", "qsa_apply_residual", "qsa_order_query_blocks",
               "qsa_sparse_attn_ordered", "qsa_project_residual", "qsa_l1_change",
               "qsa_l1_change_noalloc",
@@ -177,8 +183,10 @@ def qsa_quantize_rotated(x: torch.Tensor, block: int, codes=None, scales=None, p
 
 def qsa_select_blocks(pooled_q, scale_q, pooled_k, scale_k, seq_len: int, block: int, topk: int,
                       band=(0,), kmax: int | None = None, kept_idx=None, kept_cnt=None,
-                      stream=None):
-    """Kept key-block lists [B,H,nb,kmax] (ascending, -1 padded) and counts [B,H,nb]."""
+                      stream=None, work=None):
+    """Kept key-block lists [B,H,nb,kmax] (ascending, -1 padded) and counts [B,H,nb].
+    With ``work`` (a uint8 device tensor) the call is qsa_select_blocks_work,
+    which writes the scores' order keys there (same outputs)."""
     B, H, nb, D = pooled_q.shape
     if nb != n_blocks(seq_len, block):
         raise ValueError("pooled_q block count does not match seq_len/block")
@@ -198,10 +206,26 @@ def qsa_select_blocks(pooled_q, scale_q, pooled_k, scale_k, seq_len: int, block:
     _need(kept_cnt, "kept_cnt", torch.int32, (B, H, nb))
     arr = (ctypes.c_int32 * max(1, len(band)))(*band) if band else None
     d = make_dims(B, H, seq_len, D, block)
-    _check(load_library().qsa_select_blocks(
-        ctypes.byref(d), _ptr(pooled_q), _ptr(scale_q), _ptr(pooled_k), _ptr(scale_k), int(topk),
-        arr, len(band), int(kmax), _ptr(kept_idx), _ptr(kept_cnt), _stream(stream)))
+    lib = load_library()
+    if work is None:
+        _check(lib.qsa_select_blocks(
+            ctypes.byref(d), _ptr(pooled_q), _ptr(scale_q), _ptr(pooled_k), _ptr(scale_k),
+            int(topk), arr, len(band), int(kmax), _ptr(kept_idx), _ptr(kept_cnt),
+            _stream(stream)))
+    else:
+        _need(work, "work", torch.uint8)
+        _check(lib.qsa_select_blocks_work(
+            ctypes.byref(d), _ptr(pooled_q), _ptr(scale_q), _ptr(pooled_k), _ptr(scale_k),
+            int(topk), arr, len(band), int(kmax), _ptr(kept_idx), _ptr(kept_cnt), _ptr(work),
+            ctypes.c_uint64(work.numel()), _stream(stream)))
     return kept_idx, kept_cnt
+
+
+def qsa_select_slice_bytes(B: int, H: int, L: int, D: int, block: int) -> int:
+    """Workspace bytes of one (b, h) slice of qsa_select_blocks_work
+    (nb rows of nb keys padded to a multiple of 16, 8 bytes each)."""
+    d = make_dims(B, H, L, D, block)
+    return int(load_library().qsa_select_slice_bytes(ctypes.byref(d)))
 
 
 def default_sm_scale(head_dim: int) -> float:

@@ -166,11 +166,12 @@ int qsa_quantize_rotated(const qsa_dims* dims, const uint16_t* x, int8_t* codes,
                                            static_cast<hipStream_t>(stream)));
 }
 
-int qsa_select_blocks(const qsa_dims* dims, const int32_t* pooled_q, const float* scale_q,
-                      const int32_t* pooled_k, const float* scale_k, int32_t topk,
-                      const int32_t* band_offsets, int32_t n_band, int32_t kmax,
-                      int32_t* kept_idx, int32_t* kept_cnt, void* stream) {
-  const char* fn = "qsa_select_blocks";
+namespace {
+// Arguments of both select entry points; fills band on success.
+int check_select(const char* fn, const qsa_dims* dims, const int32_t* pooled_q,
+                 const float* scale_q, const int32_t* pooled_k, const float* scale_k,
+                 int32_t topk, const int32_t* band_offsets, int32_t n_band, int32_t kmax,
+                 int32_t* kept_idx, int32_t* kept_cnt, qsa::Band& band) {
   int st = check_dims(fn, dims);
   if (st) return st;
   REQUIRE_PTR(pooled_q);
@@ -188,7 +189,7 @@ int qsa_select_blocks(const qsa_dims* dims, const int32_t* pooled_q, const float
     return fail(QSA_ERR_PARAM, "%s: n_band=%d must be in [0, %d]", fn, n_band, QSA_MAX_BAND);
   if (n_band > 0 && band_offsets == nullptr)
     return fail(QSA_ERR_NULL, "%s: band_offsets is NULL with n_band=%d", fn, n_band);
-  qsa::Band band{};
+  band = qsa::Band{};
   bool has_diag = false;
   for (int b = 0; b < n_band; ++b) {
     band.off[b] = band_offsets[b];
@@ -201,11 +202,47 @@ int qsa_select_blocks(const qsa_dims* dims, const int32_t* pooled_q, const float
   if (kmax < 1 || kmax < need)
     return fail(QSA_ERR_PARAM, "%s: kmax=%d must be >= min(nb, topk + n_band)=%lld", fn, kmax,
                 (long long)need);
+  return QSA_OK;
+}
+}  // namespace
+
+int qsa_select_blocks(const qsa_dims* dims, const int32_t* pooled_q, const float* scale_q,
+                      const int32_t* pooled_k, const float* scale_k, int32_t topk,
+                      const int32_t* band_offsets, int32_t n_band, int32_t kmax,
+                      int32_t* kept_idx, int32_t* kept_cnt, void* stream) {
+  const char* fn = "qsa_select_blocks";
+  qsa::Band band;
+  int st = check_select(fn, dims, pooled_q, scale_q, pooled_k, scale_k, topk, band_offsets,
+                        n_band, kmax, kept_idx, kept_cnt, band);
+  if (st) return st;
   if ((st = check_device(fn))) return st;
   (void)hipGetLastError();
   return launched(fn, qsa::launch_select(*dims, pooled_q, scale_q, pooled_k, scale_k, topk, band,
                                          kmax, kept_idx, kept_cnt,
                                          static_cast<hipStream_t>(stream)));
+}
+
+uint64_t qsa_select_slice_bytes(const qsa_dims* dims) {
+  if (check_dims("qsa_select_slice_bytes", dims)) return 0;
+  return qsa::select_slice_bytes(*dims);
+}
+
+int qsa_select_blocks_work(const qsa_dims* dims, const int32_t* pooled_q, const float* scale_q,
+                           const int32_t* pooled_k, const float* scale_k, int32_t topk,
+                           const int32_t* band_offsets, int32_t n_band, int32_t kmax,
+                           int32_t* kept_idx, int32_t* kept_cnt, void* work,
+                           uint64_t work_bytes, void* stream) {
+  const char* fn = "qsa_select_blocks_work";
+  qsa::Band band;
+  int st = check_select(fn, dims, pooled_q, scale_q, pooled_k, scale_k, topk, band_offsets,
+                        n_band, kmax, kept_idx, kept_cnt, band);
+  if (st) return st;
+  OPTIONAL_PTR(work);
+  if ((st = check_device(fn))) return st;
+  (void)hipGetLastError();
+  return launched(fn, qsa::launch_select_work(*dims, pooled_q, scale_q, pooled_k, scale_k, topk,
+                                              band, kmax, kept_idx, kept_cnt, work, work_bytes,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 int qsa_sparse_attn(const qsa_dims* dims, const int8_t* q_codes, const float* q_scales,

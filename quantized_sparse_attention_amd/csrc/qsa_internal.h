@@ -68,6 +68,16 @@ hipError_t launch_select(const qsa_dims& d, const int32_t* pooled_q, const float
                          const Band& band, int32_t kmax, int32_t* kept_idx, int32_t* kept_cnt,
                          hipStream_t s);
 
+// launch_select through a workspace: the order keys of whole (b, h) slices
+// (select_slice_bytes each) are written to `work`, then selected one query
+// block per wave; as many slices per pass as work_bytes holds.  With no room
+// for one slice, or more than 2048 blocks, it is launch_select.
+uint64_t select_slice_bytes(const qsa_dims& d);
+hipError_t launch_select_work(const qsa_dims& d, const int32_t* pooled_q, const float* scale_q,
+                              const int32_t* pooled_k, const float* scale_k, int32_t topk,
+                              const Band& band, int32_t kmax, int32_t* kept_idx,
+                              int32_t* kept_cnt, void* work, uint64_t work_bytes, hipStream_t s);
+
 struct AttnArgs {
   const int8_t* q_codes;
   const float* q_scales;

@@ -37,6 +37,10 @@ namespace qsa {
 namespace {
 
 constexpr int kSelMaxThreads = 512;
+// waves per SIMD the row-select kernel is compiled for (its register budget)
+#ifndef QSA_SEL_ROWS_WAVES
+#define QSA_SEL_ROWS_WAVES 4
+#endif
 constexpr int kHist = 256;
 
 __device__ __forceinline__ uint64_t order_key(double score) {
@@ -95,6 +99,344 @@ __device__ __forceinline__ void each_key(const uint64_t* keys, const uint64_t (&
   }
 }
 
+// Order keys of one 16-column tile of scores: this lane's accumulator rows
+// 4g + r (r = 0..3) of the row block whose pooled-Q digits are a_hi/a_lo,
+// against column j (pooled-K digits b_hi/b_lo, scale skj, nj tokens).
+// a_sq[r] and a_n[r] are the rows' query scales and token counts.
+template <int KSTEPS>
+__device__ __forceinline__ void score_tile(const v4i (&a_hi)[KSTEPS], const v4i (&a_lo)[KSTEPS],
+                                           const v4i (&b_hi)[KSTEPS], const v4i (&b_lo)[KSTEPS],
+                                           double skj, int nj, const double (&a_sq)[4],
+                                           const int (&a_n)[4], uint64_t (&key)[4]) {
+  v4i hh = {0, 0, 0, 0}, mid = {0, 0, 0, 0}, ll = {0, 0, 0, 0};
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) {
+    hh = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_hi[ks], b_hi[ks], hh, 0, 0, 0);
+    mid = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_hi[ks], b_lo[ks], mid, 0, 0, 0);
+    mid = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_lo[ks], b_hi[ks], mid, 0, 0, 0);
+    ll = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_lo[ks], b_lo[ks], ll, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const double S = (double)hh[r] * 16384.0 + (double)mid[r] * 128.0 + (double)ll[r];
+    const double a = a_sq[r] * skj;
+    const double b = S * a;
+    const int ci = a_n[r] * nj;
+    // a power of two 2^e (every pair of full blocks) divides exactly as a
+    // scaling by 2^-e: the same IEEE result as b / c (b's magnitude is far
+    // from the subnormal range); other counts (short last blocks) divide
+    double q = 0.0;
+    if (__builtin_expect(ci > 0 && (ci & (ci - 1)) == 0, 1))
+      q = __builtin_ldexp(b, -__builtin_ctz((unsigned)ci));
+    else if (ci > 0)
+      q = b / (double)ci;
+    key[r] = order_key(q);
+  }
+}
+
+// The pooled-Q digits, scales and token counts of the lane's rows of the row
+// block starting at query block r0 (rows past nb or past tr are zero).
+template <int KSTEPS>
+__device__ __forceinline__ void load_rows(const int32_t* __restrict__ pqh,
+                                          const float* __restrict__ sqh, int r0, int tr, int nb,
+                                          int L, int bs, int lane, v4i (&a_hi)[KSTEPS],
+                                          v4i (&a_lo)[KSTEPS], double (&a_sq)[4], int (&a_n)[4]) {
+  constexpr int D = KSTEPS * 64;
+  const int g = lane >> 4;
+  const int arow = lane & 15;
+  const int i = r0 + arow;
+  const bool ok = arow < tr && i < nb;
+  int4 raw[KSTEPS][4];
+  load16<KSTEPS>(pqh + (uint64_t)(ok ? i : 0) * D + g * 16, raw);
+#pragma unroll
+  for (int ks = 0; ks < KSTEPS; ++ks) split16(raw[ks], ok, a_hi[ks], a_lo[ks]);
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int ir = r0 + 4 * g + r;
+    const bool okr = 4 * g + r < tr && ir < nb;
+    a_sq[r] = okr ? (double)sqh[ir] : 0.0;
+    a_n[r] = okr ? min(bs, L - ir * bs) : 0;
+  }
+}
+
+// Top-k + band selection of query block i from its nb keys (kr in registers
+// when NPL > 0, else keys[j]), written ascending to out (kmax entries, -1
+// padded) with the count to *cnt.  Every lane of the wave takes part;
+// s_hist is this wave's own kHist-bin histogram.
+//
+// The k-th largest key is found in its sign class first: with npos keys of
+// score >= 0 (keys >= 2^63), it is among them if npos >= k, else all of them
+// are taken and the rest is chosen among the negative keys.  Inside the
+// class, t = key - (smallest key of the class) preserves the order and the
+// radix digits start at the top bit of the class's range, so the first
+// histogram already spreads the keys (the top bits of a key are the sign and
+// the exponent, shared by many keys).
+template <int NPL>
+__device__ __forceinline__ void select_row_lds(const uint64_t* keys,
+                                           const uint64_t (&kr)[NPL > 0 ? NPL : 1], int nb,
+                                           int lane, uint32_t* s_hist, int i, int topk,
+                                           const Band& band, int kmax, int32_t* out,
+                                           int32_t* cnt) {
+  const int k_eff = min(topk, nb);
+  constexpr uint64_t kSign = 0x8000000000000000ull;
+  int need = k_eff;  // how many still to take among the candidates
+  const bool do_select = k_eff > 0 && k_eff < nb;
+  bool pos_class = true;     // candidates: keys >= 2^63, else keys < 2^63
+  uint64_t lo = 0;           // smallest candidate key
+  uint64_t prefix = 0, pmask = 0;  // decided high bits of t and their value
+  int lowbit = 0;            // undecided low bits of t
+  if (do_select) {
+    int npos = 0;
+    each_key<NPL>(keys, kr, nb, lane, [&](int, bool v, uint64_t key) {
+      npos += __popcll(__ballot(v && key >= kSign));
+    });
+    pos_class = npos >= need;
+    if (!pos_class) need -= npos;
+    uint64_t kmin = ~0ull, kmax_ = 0ull;
+    each_key<NPL>(keys, kr, nb, lane, [&](int, bool v, uint64_t key) {
+      if (v && (key >= kSign) == pos_class) {
+        kmin = key < kmin ? key : kmin;
+        kmax_ = key > kmax_ ? key : kmax_;
+      }
+    });
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint64_t a = __shfl_xor(kmin, o, 64), b = __shfl_xor(kmax_, o, 64);
+      kmin = a < kmin ? a : kmin;
+      kmax_ = b > kmax_ ? b : kmax_;
+    }
+    lo = kmin;
+    const uint64_t range = kmax_ - kmin;
+    lowbit = range ? 64 - __clzll((long long)range) : 0;
+    pmask = lowbit == 64 ? 0ull : ~0ull << lowbit;  // bits >= lowbit are 0 for every t
+  }
+  while (lowbit > 0) {
+    const int width = min(8, lowbit);
+    const int shift = lowbit - width;
+    const uint64_t dmask = (1ull << width) - 1;
+    // The histogram is this wave's own: LDS operations of one wave are
+    // performed in order, so waiting for them (lgkmcnt) orders the zeroing,
+    // the counting and the reads without a workgroup barrier.
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s_hist[lane * 4 + e] = 0;
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+    each_key<NPL>(keys, kr, nb, lane, [&](int, bool v, uint64_t key) {
+      const uint64_t t = key - lo;
+      if (v && (key >= kSign) == pos_class && (t & pmask) == prefix)
+        atomicAdd(&s_hist[(t >> shift) & dmask], 1u);
+    });
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    uint32_t c[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c[e] = s_hist[lane * 4 + e];
+    const uint32_t mine = c[0] + c[1] + c[2] + c[3];
+    // inclusive suffix sum over lanes (lanes >= this one)
+    uint32_t suf = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t v = __shfl_down(suf, o, 64);
+      if (lane + o < 64) suf += v;
+    }
+    const uint32_t above = suf - mine;  // candidates in higher digit bins
+    const bool here = above < (uint32_t)need && (uint32_t)need <= suf;
+    int digit = 0;
+    uint32_t cnt_above = above;
+    if (here) {
+      for (int e = 3; e >= 0; --e) {
+        if (cnt_above + c[e] >= (uint32_t)need) {
+          digit = lane * 4 + e;
+          break;
+        }
+        cnt_above += c[e];
+      }
+    }
+    const uint64_t who = __ballot(here);
+    const int src = __ffsll((unsigned long long)who) - 1;
+    digit = __shfl(digit, src, 64);
+    cnt_above = __shfl(cnt_above, src, 64);
+    const uint32_t in_bin = s_hist[digit];
+    need -= (int)cnt_above;
+    prefix |= (uint64_t)digit << shift;
+    pmask |= dmask << shift;
+    lowbit = shift;
+    // every candidate of the chosen bin is taken: no finer digit can matter
+    if ((uint32_t)need == in_bin) break;
+  }
+
+  int pos = 0, ties_seen = 0;
+  each_key<NPL>(keys, kr, nb, lane, [&](int j, bool valid, uint64_t key) {
+    bool in_band = false;
+    for (int b = 0; b < band.n; ++b) in_band |= (j - i) == band.off[b];
+    bool sel;
+    if (k_eff == 0) {
+      sel = false;
+    } else if (k_eff == nb) {
+      sel = true;
+    } else {
+      // keys of the class above the candidates' are all taken; the
+      // candidates compare on the decided digits only (all of them unless
+      // the select stopped at a bin taken whole)
+      const bool in_cls = (key >= kSign) == pos_class;
+      const uint64_t mk = (key - lo) & pmask;
+      const bool eq = in_cls && mk == prefix;
+      const uint64_t eqb = __ballot(valid && eq);
+      const int rank = ties_seen + __popcll(eqb & lanemask_lt(lane));
+      sel = (!pos_class && key >= kSign) || (in_cls && mk > prefix) || (eq && rank < need);
+      ties_seen += __popcll(eqb);
+    }
+    sel = valid && (sel || in_band);
+    const uint64_t selb = __ballot(sel);
+    const int p = pos + __popcll(selb & lanemask_lt(lane));
+    if (sel && p < kmax) out[p] = j;
+    pos += __popcll(selb);
+  });
+  for (int p = pos + lane; p < kmax; p += 64) out[p] = -1;
+  if (lane == 0) *cnt = min(pos, kmax);
+}
+
+// The same selection with the row's keys in registers (nb <= 64 * NPL, kr[e]
+// = key of j = 64e + lane, 0 for j >= nb; kr is overwritten).  Per-slot
+// conditions are kept as per-lane bitmasks (bit e for slot e) rather than as
+// execution masks, and after the class is decided each slot holds
+// t = key - lo (all ones outside the class: the class's range is below 2^63,
+// so that value never matches a prefix), so a radix pass tests one prefix
+// per slot.  Invalid slots (key 0) are in neither class.
+template <int NPL>
+__device__ __forceinline__ void select_row_regs(uint64_t (&kr)[NPL], int nb, int lane,
+                                                uint32_t* s_hist, int i, int topk,
+                                                const Band& band, int kmax, int32_t* out,
+                                                int32_t* cnt) {
+  static_assert(NPL > 0 && NPL <= 32, "one bit per slot");
+  constexpr uint64_t kSign = 0x8000000000000000ull;
+  const int k_eff = min(topk, nb);
+  uint32_t vbits = 0;  // slots j < nb
+#pragma unroll
+  for (int e = 0; e < NPL; ++e)
+    if (64 * e + lane < nb) vbits |= 1u << e;
+  int need = k_eff;
+  const bool do_select = k_eff > 0 && k_eff < nb;
+  bool pos_class = true;
+  uint32_t cbits = 0, abits = 0;   // slots in the candidate class / the class above it
+  uint64_t prefix = 0, pmask = 0;
+  int lowbit = 0;
+  if (do_select) {
+    int npos = 0;
+#pragma unroll
+    for (int e = 0; e < NPL; ++e)
+      if (64 * e < nb) npos += __popcll(__ballot(kr[e] >= kSign));  // key 0: not counted
+    pos_class = npos >= need;
+    if (!pos_class) need -= npos;
+    uint64_t kmin = ~0ull, kmax_ = 0ull;
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) {
+      const bool hi = kr[e] >= kSign;
+      const bool in = ((vbits >> e) & 1u) && hi == pos_class;
+      cbits |= (uint32_t)in << e;
+      abits |= (uint32_t)(!pos_class && hi) << e;
+      if (in) {
+        kmin = kr[e] < kmin ? kr[e] : kmin;
+        kmax_ = kr[e] > kmax_ ? kr[e] : kmax_;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint64_t x = __shfl_xor(kmin, o, 64), y = __shfl_xor(kmax_, o, 64);
+      kmin = x < kmin ? x : kmin;
+      kmax_ = y > kmax_ ? y : kmax_;
+    }
+    const uint64_t range = kmax_ - kmin;
+    lowbit = range ? 64 - __clzll((long long)range) : 0;
+    pmask = lowbit == 64 ? 0ull : ~0ull << lowbit;
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) kr[e] = ((cbits >> e) & 1u) ? kr[e] - kmin : ~0ull;
+  }
+  while (lowbit > 0) {
+    const int width = min(8, lowbit);
+    const int shift = lowbit - width;
+    const uint64_t dmask = (1ull << width) - 1;
+    // this wave's own histogram: its LDS operations are performed in order
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s_hist[lane * 4 + e] = 0;
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int e = 0; e < NPL; ++e)
+      if (64 * e < nb && (kr[e] & pmask) == prefix)
+        atomicAdd(&s_hist[(kr[e] >> shift) & dmask], 1u);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_wave_barrier();
+    uint32_t c[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) c[e] = s_hist[lane * 4 + e];
+    const uint32_t mine = c[0] + c[1] + c[2] + c[3];
+    uint32_t suf = mine;  // inclusive suffix sum over lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t v = __shfl_down(suf, o, 64);
+      if (lane + o < 64) suf += v;
+    }
+    const uint32_t above = suf - mine;
+    const bool here = above < (uint32_t)need && (uint32_t)need <= suf;
+    int digit = 0;
+    uint32_t cnt_above = above;
+    if (here) {
+      for (int e = 3; e >= 0; --e) {
+        if (cnt_above + c[e] >= (uint32_t)need) {
+          digit = lane * 4 + e;
+          break;
+        }
+        cnt_above += c[e];
+      }
+    }
+    const uint64_t who = __ballot(here);
+    const int src = __ffsll((unsigned long long)who) - 1;
+    digit = __shfl(digit, src, 64);
+    cnt_above = __shfl(cnt_above, src, 64);
+    const uint32_t in_bin = s_hist[digit];
+    need -= (int)cnt_above;
+    prefix |= (uint64_t)digit << shift;
+    pmask |= dmask << shift;
+    lowbit = shift;
+    if ((uint32_t)need == in_bin) break;
+  }
+
+  uint32_t bbits = 0;  // band slots of this lane
+  for (int b = 0; b < band.n; ++b) {
+    const int jb = i + band.off[b];
+    if (jb >= 0 && jb < nb && (jb & 63) == lane) bbits |= 1u << (jb >> 6);
+  }
+  int pos = 0, ties_seen = 0;
+#pragma unroll
+  for (int e = 0; e < NPL; ++e) {
+    if (64 * e >= nb) break;  // wave-uniform
+    const int j = 64 * e + lane;
+    const bool valid = (vbits >> e) & 1u;
+    bool sel;
+    if (k_eff == 0) {
+      sel = false;
+    } else if (k_eff == nb) {
+      sel = true;
+    } else {
+      const bool in_cls = (cbits >> e) & 1u;
+      const uint64_t mk = kr[e] & pmask;
+      const bool eq = in_cls && mk == prefix;
+      const uint64_t eqb = __ballot(eq);
+      const int rank = ties_seen + __popcll(eqb & lanemask_lt(lane));
+      sel = ((abits >> e) & 1u) || (in_cls && mk > prefix) || (eq && rank < need);
+      ties_seen += __popcll(eqb);
+    }
+    sel = valid && (sel || ((bbits >> e) & 1u));
+    const uint64_t selb = __ballot(sel);
+    const int p = pos + __popcll(selb & lanemask_lt(lane));
+    if (sel && p < kmax) out[p] = j;
+    pos += __popcll(selb);
+  }
+  for (int p = pos + lane; p < kmax; p += 64) out[p] = -1;
+  if (lane == 0) *cnt = min(pos, kmax);
+}
+
 template <int D, int NPL>
 __global__ __launch_bounds__(kSelMaxThreads) void select_kernel(
     const int32_t* __restrict__ pq, const float* __restrict__ sq, const int32_t* __restrict__ pk,
@@ -118,25 +460,9 @@ __global__ __launch_bounds__(kSelMaxThreads) void select_kernel(
   // ---- 1+2: scores of TR query blocks against every key block -------------
   const int g = lane >> 4;  // k-group of the 16x16x64 MFMA operands
   v4i a_hi[KSTEPS], a_lo[KSTEPS];
-  {
-    const int arow = lane & 15;
-    const int i = r0 + arow;
-    const bool ok = arow < TR && i < nb;
-    int4 raw[KSTEPS][4];
-    load16<KSTEPS>(pqh + (uint64_t)(ok ? i : 0) * D + g * 16, raw);
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) split16(raw[ks], ok, a_hi[ks], a_lo[ks]);
-  }
-  // this lane's accumulator rows 4g + r: their query scale and token count
-  double a_sq[4];
+  double a_sq[4];  // this lane's accumulator rows 4g + r: query scale, tokens
   int a_n[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = r0 + 4 * g + r;
-    const bool ok = 4 * g + r < TR && i < nb;
-    a_sq[r] = ok ? (double)sqh[i] : 0.0;
-    a_n[r] = ok ? min(bs, L - i * bs) : 0;
-  }
+  load_rows<KSTEPS>(pqh, sqh, r0, TR, nb, L, bs, lane, a_hi, a_lo, a_sq, a_n);
   // Column tiles ct = wave, wave + nwaves, ...; the pooled sums and scale of
   // the next tile are loaded while this one is scored.
   const int n_ctiles = (nb + 15) / 16;
@@ -156,42 +482,26 @@ __global__ __launch_bounds__(kSelMaxThreads) void select_kernel(
     for (int ks = 0; ks < KSTEPS; ++ks) split16(raw[ks], okj, b_hi[ks], b_lo[ks]);
     const double skj = (double)skv;
     if (ct + nwaves < n_ctiles) fetch(ct + nwaves);
-    v4i hh = {0, 0, 0, 0}, mid = {0, 0, 0, 0}, ll = {0, 0, 0, 0};
-#pragma unroll
-    for (int ks = 0; ks < KSTEPS; ++ks) {
-      hh = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_hi[ks], b_hi[ks], hh, 0, 0, 0);
-      mid = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_hi[ks], b_lo[ks], mid, 0, 0, 0);
-      mid = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_lo[ks], b_hi[ks], mid, 0, 0, 0);
-      ll = __builtin_amdgcn_mfma_i32_16x16x64_i8(a_lo[ks], b_lo[ks], ll, 0, 0, 0);
-    }
+    uint64_t key[4];
+    score_tile<KSTEPS>(a_hi, a_lo, b_hi, b_lo, skj, okj ? min(bs, L - j * bs) : 0, a_sq, a_n,
+                       key);
     if (okj) {
-      const int nj = min(bs, L - j * bs);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int row = 4 * g + r;  // accumulator row of this lane
-        if (row < TR && r0 + row < nb) {
-          const double S = (double)hh[r] * 16384.0 + (double)mid[r] * 128.0 + (double)ll[r];
-          const double a = a_sq[r] * skj;
-          const double b = S * a;
-          const int ci = a_n[r] * nj;
-          // a power of two (every pair of full blocks) divides exactly by a
-          // multiplication with its inverse: the same IEEE result as b / c
-          const double q = (ci & (ci - 1)) == 0 ? b * (1.0 / (double)ci) : b / (double)ci;
-          s_keys[(uint64_t)row * nb + j] = order_key(q);
-        }
+        if (row < TR && r0 + row < nb) s_keys[(uint64_t)row * nb + j] = key[r];
       }
     }
   }
   __syncthreads();
 
   // ---- 3+4: per-row radix select and ascending compaction -----------------
-  const int k_eff = min(topk, nb);
   const int rows_per_wave = (TR + nwaves - 1) / nwaves;
   for (int it = 0; it < rows_per_wave; ++it) {
     const int row = it * nwaves + wave;
     const int i = r0 + row;
-    const bool active = row < TR && i < nb;
-    const uint64_t* keys = s_keys + (uint64_t)(active ? row : 0) * nb;
+    if (!(row < TR && i < nb)) continue;  // wave-uniform
+    const uint64_t* keys = s_keys + (uint64_t)row * nb;
     uint64_t kr[NPL > 0 ? NPL : 1];
     if constexpr (NPL > 0) {
 #pragma unroll
@@ -200,134 +510,142 @@ __global__ __launch_bounds__(kSelMaxThreads) void select_kernel(
         kr[e] = j < nb ? keys[j] : 0ull;
       }
     }
-
-    // The k-th largest key is found in its sign class first: with npos keys
-    // of score >= 0 (keys >= 2^63), it is among them if npos >= k, else all
-    // of them are taken and the rest is chosen among the negative keys.
-    // Inside the class, t = key - (smallest key of the class) preserves the
-    // order and the radix digits start at the top bit of the class's range,
-    // so the first histogram already spreads the keys (the top bits of a
-    // key are the sign and the exponent, shared by many keys).
-    constexpr uint64_t kSign = 0x8000000000000000ull;
-    int need = k_eff;  // how many still to take among the candidates
-    const bool do_select = active && k_eff > 0 && k_eff < nb;
-    bool pos_class = true;     // candidates: keys >= 2^63, else keys < 2^63
-    uint64_t lo = 0;           // smallest candidate key
-    uint64_t prefix = 0, pmask = 0;  // decided high bits of t and their value
-    int lowbit = 0;            // undecided low bits of t
-    if (do_select) {
-      int npos = 0;
-      each_key<NPL>(keys, kr, nb, lane, [&](int, bool v, uint64_t key) {
-        npos += __popcll(__ballot(v && key >= kSign));
-      });
-      pos_class = npos >= need;
-      if (!pos_class) need -= npos;
-      uint64_t kmin = ~0ull, kmax_ = 0ull;
-      each_key<NPL>(keys, kr, nb, lane, [&](int, bool v, uint64_t key) {
-        if (v && (key >= kSign) == pos_class) {
-          kmin = key < kmin ? key : kmin;
-          kmax_ = key > kmax_ ? key : kmax_;
-        }
-      });
-#pragma unroll
-      for (int o = 32; o >= 1; o >>= 1) {
-        const uint64_t a = __shfl_xor(kmin, o, 64), b = __shfl_xor(kmax_, o, 64);
-        kmin = a < kmin ? a : kmin;
-        kmax_ = b > kmax_ ? b : kmax_;
-      }
-      lo = kmin;
-      const uint64_t range = kmax_ - kmin;
-      lowbit = range ? 64 - __clzll((long long)range) : 0;
-      pmask = lowbit == 64 ? 0ull : ~0ull << lowbit;  // bits >= lowbit are 0 for every t
-    }
-    while (lowbit > 0) {
-      const int width = min(8, lowbit);
-      const int shift = lowbit - width;
-      const uint64_t dmask = (1ull << width) - 1;
-      // The histogram is this wave's own: LDS operations of one wave are
-      // performed in order, so waiting for them (lgkmcnt) orders the zeroing,
-      // the counting and the reads without a workgroup barrier.
-#pragma unroll
-      for (int e = 0; e < 4; ++e) s_hist[lane * 4 + e] = 0;
-      __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
-      __builtin_amdgcn_wave_barrier();
-      each_key<NPL>(keys, kr, nb, lane, [&](int, bool v, uint64_t key) {
-        const uint64_t t = key - lo;
-        if (v && (key >= kSign) == pos_class && (t & pmask) == prefix)
-          atomicAdd(&s_hist[(t >> shift) & dmask], 1u);
-      });
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-      __builtin_amdgcn_wave_barrier();
-      uint32_t c[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) c[e] = s_hist[lane * 4 + e];
-      const uint32_t mine = c[0] + c[1] + c[2] + c[3];
-      // inclusive suffix sum over lanes (lanes >= this one)
-      uint32_t suf = mine;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t v = __shfl_down(suf, o, 64);
-        if (lane + o < 64) suf += v;
-      }
-      const uint32_t above = suf - mine;  // candidates in higher digit bins
-      const bool here = above < (uint32_t)need && (uint32_t)need <= suf;
-      int digit = 0;
-      uint32_t cnt_above = above;
-      if (here) {
-        for (int e = 3; e >= 0; --e) {
-          if (cnt_above + c[e] >= (uint32_t)need) {
-            digit = lane * 4 + e;
-            break;
-          }
-          cnt_above += c[e];
-        }
-      }
-      const uint64_t who = __ballot(here);
-      const int src = __ffsll((unsigned long long)who) - 1;
-      digit = __shfl(digit, src, 64);
-      cnt_above = __shfl(cnt_above, src, 64);
-      const uint32_t in_bin = s_hist[digit];
-      need -= (int)cnt_above;
-      prefix |= (uint64_t)digit << shift;
-      pmask |= dmask << shift;
-      lowbit = shift;
-      // every candidate of the chosen bin is taken: no finer digit can matter
-      if ((uint32_t)need == in_bin) break;
-    }
-
-    if (active) {
-      int32_t* out = kept_idx + ((bh * (uint64_t)nb) + i) * (uint64_t)kmax;
-      int pos = 0, ties_seen = 0;
-      each_key<NPL>(keys, kr, nb, lane, [&](int j, bool valid, uint64_t key) {
-        bool in_band = false;
-        for (int b = 0; b < band.n; ++b) in_band |= (j - i) == band.off[b];
-        bool sel;
-        if (k_eff == 0) {
-          sel = false;
-        } else if (k_eff == nb) {
-          sel = true;
-        } else {
-          // keys of the class above the candidates' are all taken; the
-          // candidates compare on the decided digits only (all of them unless
-          // the select stopped at a bin taken whole)
-          const bool in_cls = (key >= kSign) == pos_class;
-          const uint64_t mk = (key - lo) & pmask;
-          const bool eq = in_cls && mk == prefix;
-          const uint64_t eqb = __ballot(valid && eq);
-          const int rank = ties_seen + __popcll(eqb & lanemask_lt(lane));
-          sel = (!pos_class && key >= kSign) || (in_cls && mk > prefix) || (eq && rank < need);
-          ties_seen += __popcll(eqb);
-        }
-        sel = valid && (sel || in_band);
-        const uint64_t selb = __ballot(sel);
-        const int p = pos + __popcll(selb & lanemask_lt(lane));
-        if (sel && p < kmax) out[p] = j;
-        pos += __popcll(selb);
-      });
-      for (int p = pos + lane; p < kmax; p += 64) out[p] = -1;
-      if (lane == 0) kept_cnt[bh * (uint64_t)nb + i] = min(pos, kmax);
-    }
+    const uint64_t rowi = bh * (uint64_t)nb + i;
+    if constexpr (NPL > 0)
+      select_row_regs<NPL>(kr, nb, lane, s_hist, i, topk, band, kmax,
+                           kept_idx + rowi * (uint64_t)kmax, kept_cnt + rowi);
+    else
+      select_row_lds<NPL>(keys, kr, nb, lane, s_hist, i, topk, band, kmax,
+                          kept_idx + rowi * (uint64_t)kmax, kept_cnt + rowi);
   }
+}
+
+// Keys per row of the workspace: nb rounded up to 16, so that the 16 keys a
+// column tile writes to a row fill one aligned 128-byte line.
+__host__ __device__ inline int key_stride(int nb) { return (nb + 15) & ~15; }
+
+// Scores of whole (b, h) slices as order keys in `keys` ([slice][nb][stride],
+// slice = bh - bh0).  A workgroup takes 64 query blocks (16 per wave) and the
+// column tiles [ct0, ct1) of its share (blockIdx.z of n_split); each pooled-K
+// tile of 16 key blocks is read once per workgroup with 16-byte loads that
+// cover whole rows, staged in LDS (rows padded by 16 bytes, two buffers, one
+// barrier per tile) and read from there in the MFMA operand layout.
+template <int D>
+__global__ __launch_bounds__(256) void score_keys_kernel(
+    const int32_t* __restrict__ pq, const float* __restrict__ sq, const int32_t* __restrict__ pk,
+    const float* __restrict__ sk, int L, int bs, int nb, uint64_t bh0, int n_split,
+    uint64_t* __restrict__ keys) {
+  constexpr int KSTEPS = D / 64;
+  constexpr int ROWB = D + 16;                   // bytes per padded LDS digit row
+  constexpr int CHUNKS = 16 * D / 4;             // int4 pieces of a tile
+  constexpr int PER_T = CHUNKS / 256;            // pieces per thread
+  static_assert(CHUNKS % 256 == 0, "whole pieces per thread");
+  // the tile's pooled-K sums as their two int8 digits (split16's), one plane each
+  __shared__ __attribute__((aligned(16))) int8_t s_hi[2][16 * ROWB];
+  __shared__ __attribute__((aligned(16))) int8_t s_lo[2][16 * ROWB];
+  __shared__ float s_sk[2][16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t bh = bh0 + blockIdx.y;
+  const int32_t* pkh = pk + bh * (uint64_t)nb * D;
+  const float* skh = sk + bh * (uint64_t)nb;
+  const int ks_row = key_stride(nb);
+  uint64_t* kh = keys + (uint64_t)blockIdx.y * nb * ks_row;
+  const int r0 = blockIdx.x * 64 + wave * 16;
+  const int g = lane >> 4, jj = lane & 15;
+  const int n_ct = (nb + 15) / 16;
+  const int per = (n_ct + n_split - 1) / n_split;
+  const int ct0 = blockIdx.z * per, ct1 = min(n_ct, ct0 + per);
+  if (ct0 >= ct1) return;  // workgroup-uniform, before any barrier
+
+  v4i a_hi[KSTEPS], a_lo[KSTEPS];
+  double a_sq[4];
+  int a_n[4];
+  load_rows<KSTEPS>(pq + bh * (uint64_t)nb * D, sq + bh * (uint64_t)nb, r0, 16, nb, L, bs, lane,
+                    a_hi, a_lo, a_sq, a_n);
+
+  int4 stage[PER_T];
+  float sk_stage = 0.0f;
+  auto fetch = [&](int ct) {  // this thread's pieces of tile ct (columns past nb: row nb - 1)
+#pragma unroll
+    for (int m = 0; m < PER_T; ++m) {
+      const int q = tid + 256 * m;
+      const int j = min(ct * 16 + q / (D / 4), nb - 1);
+      stage[m] = *reinterpret_cast<const int4*>(pkh + (uint64_t)j * D + 4 * (q % (D / 4)));
+    }
+    if (tid < 16) sk_stage = skh[min(ct * 16 + tid, nb - 1)];
+  };
+  auto put = [&](int buf) {  // split once per workgroup: P = 128 hi + lo, lo in [0, 127]
+#pragma unroll
+    for (int m = 0; m < PER_T; ++m) {
+      const int q = tid + 256 * m;
+      const int off = (q / (D / 4)) * ROWB + 4 * (q % (D / 4));
+      const int vv[4] = {stage[m].x, stage[m].y, stage[m].z, stage[m].w};
+      uint32_t h = 0, l = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        h |= (uint32_t)((vv[e] >> 7) & 0xff) << (8 * e);
+        l |= (uint32_t)(vv[e] & 127) << (8 * e);
+      }
+      *reinterpret_cast<uint32_t*>(&s_hi[buf][off]) = h;
+      *reinterpret_cast<uint32_t*>(&s_lo[buf][off]) = l;
+    }
+    if (tid < 16) s_sk[buf][tid] = sk_stage;
+  };
+  fetch(ct0);
+  put(0);
+  __syncthreads();
+  int buf = 0;
+  for (int ct = ct0; ct < ct1; ++ct) {
+    if (ct + 1 < ct1) fetch(ct + 1);  // lands while this tile is scored
+    const int j = ct * 16 + jj;
+    const bool okj = j < nb;
+    v4i b_hi[KSTEPS], b_lo[KSTEPS];
+#pragma unroll
+    for (int ks = 0; ks < KSTEPS; ++ks) {
+      const int off = jj * ROWB + ks * 64 + g * 16;
+      b_hi[ks] = *reinterpret_cast<const v4i*>(&s_hi[buf][off]);
+      b_lo[ks] = *reinterpret_cast<const v4i*>(&s_lo[buf][off]);
+    }
+    const double skj = (double)s_sk[buf][jj];
+    uint64_t key[4];
+    score_tile<KSTEPS>(a_hi, a_lo, b_hi, b_lo, skj, okj ? min(bs, L - j * bs) : 0, a_sq, a_n,
+                       key);
+    if (okj) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = r0 + 4 * g + r;
+        if (i < nb) kh[(uint64_t)i * ks_row + j] = key[r];
+      }
+    }
+    if (ct + 1 < ct1) put(buf ^ 1);  // that buffer was last read before the previous barrier
+    __syncthreads();
+    buf ^= 1;
+  }
+}
+
+// Selection from the keys of score_keys_kernel: one wave per query block,
+// its keys loaded into registers (nb <= 64 * NPL), one histogram per wave.
+template <int NPL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QSA_SEL_ROWS_WAVES))) void select_rows_kernel(const uint64_t* __restrict__ keys,
+                                                          int nb, uint64_t bh0, int topk,
+                                                          Band band, int kmax,
+                                                          int32_t* __restrict__ kept_idx,
+                                                          int32_t* __restrict__ kept_cnt) {
+  static_assert(NPL > 0, "keys in registers");
+  __shared__ uint32_t s_hist_all[4 * kHist];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = blockIdx.x * 4 + wave;
+  if (i >= nb) return;  // wave-uniform; no workgroup barrier follows
+  const uint64_t* row = keys + ((uint64_t)blockIdx.y * nb + i) * key_stride(nb);
+  uint64_t kr[NPL];
+#pragma unroll
+  for (int e = 0; e < NPL; ++e) {
+    const int j = 64 * e + lane;
+    kr[e] = j < nb ? row[j] : 0ull;
+  }
+  const uint64_t rowi = (bh0 + blockIdx.y) * (uint64_t)nb + i;
+  select_row_regs<NPL>(kr, nb, lane, s_hist_all + wave * kHist, i, topk, band, kmax,
+                       kept_idx + rowi * (uint64_t)kmax, kept_cnt + rowi);
 }
 
 }  // namespace
@@ -398,6 +716,64 @@ hipError_t launch_select(const qsa_dims& d, const int32_t* pooled_q, const float
     launch_select_d<64>(grid, threads, lds, lds_cap, s, pooled_q, scale_q, pooled_k, scale_k, d, nb, TR,
                         topk, band, kmax, kept_idx, kept_cnt);
   return hipGetLastError();
+}
+
+uint64_t select_slice_bytes(const qsa_dims& d) {
+  const uint64_t nb = (uint64_t)((d.seq_len + d.block - 1) / d.block);
+  return nb * (uint64_t)key_stride((int)nb) * sizeof(uint64_t);
+}
+
+namespace {
+template <int D, int NPL>
+void launch_two_pass(const qsa_dims& d, int nb, uint64_t bh0, uint32_t n, const int32_t* pooled_q,
+                     const float* scale_q, const int32_t* pooled_k, const float* scale_k,
+                     int32_t topk, const Band& band, int32_t kmax, int32_t* kept_idx,
+                     int32_t* kept_cnt, uint64_t* keys, hipStream_t s) {
+  // column shares per row block: about 4096 workgroups per pass
+  const int rb = (nb + 63) / 64, n_ct = (nb + 15) / 16;
+  const uint64_t want = (4096 + (uint64_t)rb * n - 1) / ((uint64_t)rb * n);
+  const int n_split = (int)(want < 1 ? 1 : want > (uint64_t)n_ct ? n_ct : want);
+  hipLaunchKernelGGL((score_keys_kernel<D>), dim3((uint32_t)rb, n, (uint32_t)n_split), dim3(256),
+                     0, s, pooled_q, scale_q, pooled_k, scale_k, d.seq_len, d.block, nb, bh0,
+                     n_split, keys);
+  hipLaunchKernelGGL((select_rows_kernel<NPL>), dim3((uint32_t)((nb + 3) / 4), n), dim3(256), 0, s,
+                     (const uint64_t*)keys, nb, bh0, topk, band, kmax, kept_idx, kept_cnt);
+}
+}  // namespace
+
+hipError_t launch_select_work(const qsa_dims& d, const int32_t* pooled_q, const float* scale_q,
+                              const int32_t* pooled_k, const float* scale_k, int32_t topk,
+                              const Band& band, int32_t kmax, int32_t* kept_idx,
+                              int32_t* kept_cnt, void* work, uint64_t work_bytes,
+                              hipStream_t s) {
+  const int nb = (d.seq_len + d.block - 1) / d.block;
+  const uint64_t slice = select_slice_bytes(d);
+  const uint64_t n_bh = (uint64_t)d.batch * d.heads;
+  const uint64_t per = work ? work_bytes / slice : 0;
+  if (nb > 64 * 32 || per == 0)
+    return launch_select(d, pooled_q, scale_q, pooled_k, scale_k, topk, band, kmax, kept_idx,
+                         kept_cnt, s);
+  const uint64_t chunk = per < n_bh ? (per < 65535 ? per : 65535) : (n_bh < 65535 ? n_bh : 65535);
+  uint64_t* keys = static_cast<uint64_t*>(work);
+  for (uint64_t bh0 = 0; bh0 < n_bh; bh0 += chunk) {
+    const uint32_t n = (uint32_t)(n_bh - bh0 < chunk ? n_bh - bh0 : chunk);
+#define QSA_TWO_PASS(DD, NPL)                                                                    \
+  launch_two_pass<DD, NPL>(d, nb, bh0, n, pooled_q, scale_q, pooled_k, scale_k, topk, band, kmax, \
+                           kept_idx, kept_cnt, keys, s)
+    if (d.head_dim == 128) {
+      if (nb <= 64 * 16) QSA_TWO_PASS(128, 16);
+      else if (nb <= 64 * 24) QSA_TWO_PASS(128, 24);
+      else QSA_TWO_PASS(128, 32);
+    } else {
+      if (nb <= 64 * 16) QSA_TWO_PASS(64, 16);
+      else if (nb <= 64 * 24) QSA_TWO_PASS(64, 24);
+      else QSA_TWO_PASS(64, 32);
+    }
+#undef QSA_TWO_PASS
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace qsa

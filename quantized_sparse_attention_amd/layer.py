@@ -37,6 +37,10 @@ class QSAConfig:
     # outputs passes it (DVD-Quant, gist.science/es/paper/2505.18663,
     # technical summary §2C); None keeps caller-chosen refresh steps
     adaptive_delta: float | None = None
+    # select through qsa_select_blocks_work with a workspace for every
+    # (batch, head) slice's score keys (same kept lists; the layer allocates
+    # it once per shape, 8 * nb * nb bytes per slice); False: qsa_select_blocks
+    select_workspace: bool = True
 
 
 @dataclass
@@ -72,6 +76,7 @@ class QuantSparseAttention:
         self.last_sums = None   # (sum|O_t - O_t-1|, sum|O_t-1|) of the last step
         self.l1_work = None
         self.l1_sums = None
+        self.sel_work = None    # score keys of qsa_select_blocks_work
 
     def reset(self):
         self.r = self.dr = None
@@ -110,7 +115,15 @@ class QuantSparseAttention:
         quant = B.qsa_quantize_rotated if c.rotate else B.qsa_quantize
         qc, qs, qp = quant(q, c.block)
         kc, ks, kp = quant(k, c.block)
-        idx, cnt = B.qsa_select_blocks(qp, qs, kp, ks, q.shape[2], c.block, c.topk, c.band)
+        work = None
+        if c.select_workspace:
+            Bn, H, L, D = q.shape
+            n = B.qsa_select_slice_bytes(Bn, H, L, D, c.block) * Bn * H
+            if self.sel_work is None or self.sel_work.numel() != n or self.sel_work.device != q.device:
+                self.sel_work = torch.empty(n, dtype=torch.uint8, device=q.device)
+            work = self.sel_work
+        idx, cnt = B.qsa_select_blocks(qp, qs, kp, ks, q.shape[2], c.block, c.topk, c.band,
+                                       work=work)
         self.last = StepBuffers(qc, qs, qp, kc, ks, kp, idx, cnt)
         return qc, qs, kc, ks, idx, cnt
 

@@ -36,11 +36,18 @@ CFGS = {
 }
 
 
-def _gpu_front(x, w, topk, band, kmax):
+def _gpu_front(x, w, topk, band, kmax, select_work=False):
+    """GPU quantise + select; select_work: through qsa_select_blocks_work with
+    room for every slice in one pass."""
     q, k = dev_bf16(x["q"]), dev_bf16(x["k"])
     qc, qs, qp = B.qsa_quantize(q, w.block)
     kc, ks, kp = B.qsa_quantize(k, w.block)
-    idx, cnt = B.qsa_select_blocks(qp, qs, kp, ks, w.seq_len, w.block, topk, band, kmax)
+    work = None
+    if select_work:
+        n = B.qsa_select_slice_bytes(w.batch, w.heads, w.seq_len, w.head_dim, w.block)
+        work = torch.empty(n * w.batch * w.heads, dtype=torch.uint8, device=q.device)
+    idx, cnt = B.qsa_select_blocks(qp, qs, kp, ks, w.seq_len, w.block, topk, band, kmax,
+                                   work=work)
     torch.cuda.synchronize()
     return dict(qc=qc, qs=qs, qp=qp, kc=kc, ks=ks, kp=kp, idx=idx, cnt=cnt)
 
@@ -64,9 +71,11 @@ def test_quantize_bit_exact(name):
     assert np.array_equal(g["kp"].cpu().numpy(), o["pk"])
 
 
+@pytest.mark.parametrize("select_work", [False, True])
 @pytest.mark.parametrize("name", list(CFGS))
-def test_select_bit_exact(name):
-    w, x, o, g = _setup(name)
+def test_select_bit_exact(name, select_work):
+    w, x, o, _ = _setup(name)
+    g = _gpu_front(x, w, o["topk"], o["band"], o["kmax"], select_work)
     assert np.array_equal(g["cnt"].cpu().numpy(), o["cnt"])
     assert np.array_equal(g["idx"].cpu().numpy(), o["idx"])
 
@@ -354,21 +363,23 @@ def test_hand_examples_on_gpu(name):
         assert np.max(np.abs(out[i * blk:(i + 1) * blk] - want)) <= 2e-2, (name, i, kept)
 
 
-def test_select_edges():
+@pytest.mark.parametrize("select_work", [False, True])
+def test_select_edges(select_work):
     w = TINY.with_(grid=(1, 9, 64), head_dim=128)  # 576 tokens, 9 blocks
     x = qsa_gen.make_qkv(w)
     # an all-zero key block gives +-0 scores that tie
     x["k"][0, 0, 128:192] = 0
     for topk, band in [(0, (0,)), (9, (0,)), (20, (0,)), (3, (-8, 0, 8)), (1, (0, 2, -2, 5))]:
         o = oracle_front(x, w, topk=topk, band=band, kmax=9)
-        g = _gpu_front(x, w, topk, band, 9)
+        g = _gpu_front(x, w, topk, band, 9, select_work)
         assert np.array_equal(g["idx"].cpu().numpy(), o["idx"]), (topk, band)
         assert np.array_equal(g["cnt"].cpu().numpy(), o["cnt"]), (topk, band)
     assert np.all(g["ks"].cpu().numpy()[0, 0, 2] == 0)
 
 
+@pytest.mark.parametrize("select_work", [False, True])
 @pytest.mark.parametrize("case", ["all_equal", "two_values", "few_values", "wide_range"])
-def test_select_ties_and_ranges(case):
+def test_select_ties_and_ranges(case, select_work):
     """Score rows with every key equal (no radix pass at all), two or a few
     distinct values (ties straddling the k-th place) and a wide exponent
     range (every pass): kept lists bit-exact."""
@@ -392,7 +403,7 @@ def test_select_ties_and_ranges(case):
         x["k"] = oracle.f64_to_bf16(kv)
     for topk, band in [(1, (0,)), (7, ()), (13, (0, 3)), (39, (0,))]:
         o = oracle_front(x, w, topk=topk, band=band)
-        g = _gpu_front(x, w, topk, band, o["kmax"])
+        g = _gpu_front(x, w, topk, band, o["kmax"], select_work)
         assert np.array_equal(g["cnt"].cpu().numpy(), o["cnt"]), (case, topk, band)
         assert np.array_equal(g["idx"].cpu().numpy(), o["idx"]), (case, topk, band)
 

@@ -135,6 +135,15 @@ def test_writes_stay_inside_their_buffers(cfg):
     B.qsa_select_blocks(qp.t, qs.t, kp.t, ks.t, L, bs, cfg["topk"], cfg["band"], kmax, idx.t,
                         cnt.t)
     done("qsa_select_blocks", idx, cnt)
+    # the workspace variant: its outputs and the workspace itself (one slice,
+    # the exact size) stay inside their buffers, and the lists are the same
+    slice_b = B.qsa_select_slice_bytes(1, 1, L, D, bs)
+    idx2, cnt2 = G((1, 1, nb, kmax), torch.int32), G((1, 1, nb), torch.int32)
+    wk = G((slice_b,), torch.uint8)
+    B.qsa_select_blocks(qp.t, qs.t, kp.t, ks.t, L, bs, cfg["topk"], cfg["band"], kmax, idx2.t,
+                        cnt2.t, work=wk.t)
+    done("qsa_select_blocks_work", idx2, cnt2, wk)
+    assert torch.equal(idx2.t, idx.t) and torch.equal(cnt2.t, cnt.t)
     order = G((1, 1, nb), torch.int32)
     B.qsa_order_query_blocks(idx.t, cnt.t, L, bs, D, order.t)
     done("qsa_order_query_blocks", order)
@@ -171,4 +180,4 @@ def test_writes_stay_inside_their_buffers(cfg):
     basis, vals = G((1, 1, D, rank), torch.float32), G((1, 1, rank), torch.float32)
     B.qsa_project_residual(dr_p.t, rank, basis.t, vals.t)
     done("qsa_project_residual", dr_p, basis, vals)
-    assert len(checks) == 13
+    assert len(checks) == 14
