@@ -296,75 +296,35 @@ __device__ __forceinline__ void select_row_lds(const uint64_t* keys,
   if (lane == 0) *cnt = min(pos, kmax);
 }
 
-// The same selection with the row's keys in registers (nb <= 64 * NPL, kr[e]
-// = key of j = 64e + lane, 0 for j >= nb; kr is overwritten).  Per-slot
-// conditions are kept as per-lane bitmasks (bit e for slot e) rather than as
-// execution masks, and after the class is decided each slot holds
-// t = key - lo (all ones outside the class: the class's range is below 2^63,
-// so that value never matches a prefix), so a radix pass tests one prefix
-// per slot.  Invalid slots (key 0) are in neither class.
-template <int NPL>
-__device__ __forceinline__ void select_row_regs(uint64_t (&kr)[NPL], int nb, int lane,
-                                                uint32_t* s_hist, int i, int topk,
-                                                const Band& band, int kmax, int32_t* out,
-                                                int32_t* cnt) {
-  static_assert(NPL > 0 && NPL <= 32, "one bit per slot");
-  constexpr uint64_t kSign = 0x8000000000000000ull;
-  const int k_eff = min(topk, nb);
-  uint32_t vbits = 0;  // slots j < nb
-#pragma unroll
-  for (int e = 0; e < NPL; ++e)
-    if (64 * e + lane < nb) vbits |= 1u << e;
-  int need = k_eff;
-  const bool do_select = k_eff > 0 && k_eff < nb;
-  bool pos_class = true;
-  uint32_t cbits = 0, abits = 0;   // slots in the candidate class / the class above it
-  uint64_t prefix = 0, pmask = 0;
-  int lowbit = 0;
-  if (do_select) {
-    int npos = 0;
-#pragma unroll
-    for (int e = 0; e < NPL; ++e)
-      if (64 * e < nb) npos += __popcll(__ballot(kr[e] >= kSign));  // key 0: not counted
-    pos_class = npos >= need;
-    if (!pos_class) need -= npos;
-    uint64_t kmin = ~0ull, kmax_ = 0ull;
-#pragma unroll
-    for (int e = 0; e < NPL; ++e) {
-      const bool hi = kr[e] >= kSign;
-      const bool in = ((vbits >> e) & 1u) && hi == pos_class;
-      cbits |= (uint32_t)in << e;
-      abits |= (uint32_t)(!pos_class && hi) << e;
-      if (in) {
-        kmin = kr[e] < kmin ? kr[e] : kmin;
-        kmax_ = kr[e] > kmax_ ? kr[e] : kmax_;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const uint64_t x = __shfl_xor(kmin, o, 64), y = __shfl_xor(kmax_, o, 64);
-      kmin = x < kmin ? x : kmin;
-      kmax_ = y > kmax_ ? y : kmax_;
-    }
-    const uint64_t range = kmax_ - kmin;
-    lowbit = range ? 64 - __clzll((long long)range) : 0;
-    pmask = lowbit == 64 ? 0ull : ~0ull << lowbit;
-#pragma unroll
-    for (int e = 0; e < NPL; ++e) kr[e] = ((cbits >> e) & 1u) ? kr[e] - kmin : ~0ull;
-  }
+// Radix select among the slots of a bitmask (bit e: slot e) over 32-bit
+// values t[e] < 2^lowbit: narrows (prefix, pmask), the decided high bits,
+// to the bin that holds the need-th largest value, with 8-bit digits from
+// the top.  On return `need` counts what is still to take from the slots
+// equal to prefix on pmask, and `whole` says that all of them are taken.
+// SENTINEL: slots outside `cand` hold t = ~0, which never matches a prefix
+// (lowbit < 32: pmask keeps bit 31 and prefix leaves it 0), so the mask need
+// not be tested.  The histogram is this wave's own: its LDS operations are
+// performed in order, so waits (lgkmcnt) order them without barriers.
+template <int NPL, bool SENTINEL>
+__device__ __forceinline__ void radix32(const uint32_t (&t)[NPL], uint32_t cand, int n_cand,
+                                        int nb, int lane, uint32_t* s_hist, int lowbit,
+                                        int& need, uint32_t& prefix, uint32_t& pmask,
+                                        bool& whole) {
+  prefix = 0;
+  pmask = lowbit >= 32 ? 0u : ~0u << lowbit;
+  int in_set = n_cand;  // slots equal to prefix on pmask
   while (lowbit > 0) {
     const int width = min(8, lowbit);
     const int shift = lowbit - width;
-    const uint64_t dmask = (1ull << width) - 1;
-    // this wave's own histogram: its LDS operations are performed in order
+    const uint32_t dmask = (1u << width) - 1u;
 #pragma unroll
     for (int e = 0; e < 4; ++e) s_hist[lane * 4 + e] = 0;
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int e = 0; e < NPL; ++e)
-      if (64 * e < nb && (kr[e] & pmask) == prefix)
-        atomicAdd(&s_hist[(kr[e] >> shift) & dmask], 1u);
+      if (64 * e < nb && (SENTINEL || ((cand >> e) & 1u)) && (t[e] & pmask) == prefix)
+        atomicAdd(&s_hist[(t[e] >> shift) & dmask], 1u);
     __builtin_amdgcn_s_waitcnt(0xc07f);
     __builtin_amdgcn_wave_barrier();
     uint32_t c[4];
@@ -394,12 +354,115 @@ __device__ __forceinline__ void select_row_regs(uint64_t (&kr)[NPL], int nb, int
     const int src = __ffsll((unsigned long long)who) - 1;
     digit = __shfl(digit, src, 64);
     cnt_above = __shfl(cnt_above, src, 64);
-    const uint32_t in_bin = s_hist[digit];
+    in_set = (int)s_hist[digit];
     need -= (int)cnt_above;
-    prefix |= (uint64_t)digit << shift;
+    prefix |= (uint32_t)digit << shift;
     pmask |= dmask << shift;
     lowbit = shift;
-    if ((uint32_t)need == in_bin) break;
+    if (need == in_set) break;  // every slot of the chosen bin is taken
+  }
+  whole = need == in_set;
+}
+
+// The smallest and largest of t[e] over the slots of `cand`, across the wave.
+template <int NPL>
+__device__ __forceinline__ void range32(const uint32_t (&t)[NPL], uint32_t cand, uint32_t& mn,
+                                        uint32_t& mx) {
+  mn = ~0u;
+  mx = 0u;
+#pragma unroll
+  for (int e = 0; e < NPL; ++e)
+    if ((cand >> e) & 1u) {
+      mn = min(mn, t[e]);
+      mx = max(mx, t[e]);
+    }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
+    mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+  }
+}
+
+__device__ __forceinline__ int popc_wave(uint32_t bits, int e) {
+  return __popcll(__ballot((bits >> e) & 1u));
+}
+
+// The selection of select_row_lds with the keys split in halves: hi[e] in
+// registers, the high 32 bits of slot e's order key (0 for j >= nb; hi is
+// overwritten), and lo_of(e), its low 32 bits, read only for the slots whose
+// high halves tie at the k-th place.  The high half is a monotone function
+// of the key, so every slot whose high half is above the k-th largest high
+// half is kept and every slot below it is not; the slots equal to it are
+// ordered by their low halves (equal full keys by index).  All arithmetic is
+// 32-bit.  Per-slot conditions are per-lane bitmasks (bit e: slot e).
+template <int NPL, typename LoOf>
+__device__ __forceinline__ void select_row_split(uint32_t (&hi)[NPL], LoOf&& lo_of, int nb,
+                                                 int lane, uint32_t* s_hist, int i, int topk,
+                                                 const Band& band, int kmax, int32_t* out,
+                                                 int32_t* cnt) {
+  static_assert(NPL > 0 && NPL <= 32, "one bit per slot");
+  constexpr uint32_t kSign = 0x80000000u;
+  const int k_eff = min(topk, nb);
+  uint32_t vbits = 0;  // slots j < nb
+#pragma unroll
+  for (int e = 0; e < NPL; ++e)
+    if (64 * e + lane < nb) vbits |= 1u << e;
+  const bool do_select = k_eff > 0 && k_eff < nb;
+  int need = k_eff;
+  uint32_t cbits = 0, abits = 0;     // candidate class / the class above it
+  uint32_t prefix = 0, pmask = 0;    // stage A: decided bits of t = hi - min
+  bool whole = true;
+  uint32_t ebits = 0;                // stage B: slots tied on all 32 high bits
+  uint32_t lo[NPL];
+  uint32_t prefix2 = 0, pmask2 = 0;  // stage B: decided bits of t2 = lo - min
+  bool stage_b = false;
+  if (do_select) {
+    int npos = 0;
+#pragma unroll
+    for (int e = 0; e < NPL; ++e)
+      if (64 * e < nb) npos += __popcll(__ballot(hi[e] >= kSign));  // hi 0: not counted
+    const bool pos_class = npos >= need;
+    if (!pos_class) need -= npos;
+    int n_cls = 0;
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) {
+      const bool up = hi[e] >= kSign;
+      cbits |= (uint32_t)(((vbits >> e) & 1u) && up == pos_class) << e;
+      abits |= (uint32_t)(!pos_class && up) << e;
+    }
+#pragma unroll
+    for (int e = 0; e < NPL; ++e)
+      if (64 * e < nb) n_cls += popc_wave(cbits, e);
+    uint32_t mn, mx;
+    range32<NPL>(hi, cbits, mn, mx);
+    const uint32_t range = mx - mn;  // < 2^31: one sign class
+    const int lowbit = range ? 32 - __clz((int)range) : 0;
+#pragma unroll
+    for (int e = 0; e < NPL; ++e) hi[e] = ((cbits >> e) & 1u) ? hi[e] - mn : ~0u;
+    radix32<NPL, true>(hi, cbits, n_cls, nb, lane, s_hist, lowbit, need, prefix, pmask, whole);
+    if (!whole) {
+      // every high bit is decided: the tied slots, ordered by their low halves
+      stage_b = true;
+      int n_e = 0;
+#pragma unroll
+      for (int e = 0; e < NPL; ++e) {
+        const bool tied = ((cbits >> e) & 1u) && hi[e] == prefix;
+        ebits |= (uint32_t)tied << e;
+        lo[e] = tied ? lo_of(e) : 0u;
+      }
+#pragma unroll
+      for (int e = 0; e < NPL; ++e)
+        if (64 * e < nb) n_e += popc_wave(ebits, e);
+      uint32_t mn2, mx2;
+      range32<NPL>(lo, ebits, mn2, mx2);
+      const uint32_t range2 = mx2 - mn2;
+      const int lowbit2 = range2 ? 32 - __clz((int)range2) : 0;
+#pragma unroll
+      for (int e = 0; e < NPL; ++e) lo[e] = lo[e] - mn2;
+      bool whole2;
+      radix32<NPL, false>(lo, ebits, n_e, nb, lane, s_hist, lowbit2, need, prefix2, pmask2,
+                          whole2);
+    }
   }
 
   uint32_t bbits = 0;  // band slots of this lane
@@ -412,7 +475,6 @@ __device__ __forceinline__ void select_row_regs(uint64_t (&kr)[NPL], int nb, int
   for (int e = 0; e < NPL; ++e) {
     if (64 * e >= nb) break;  // wave-uniform
     const int j = 64 * e + lane;
-    const bool valid = (vbits >> e) & 1u;
     bool sel;
     if (k_eff == 0) {
       sel = false;
@@ -420,14 +482,23 @@ __device__ __forceinline__ void select_row_regs(uint64_t (&kr)[NPL], int nb, int
       sel = true;
     } else {
       const bool in_cls = (cbits >> e) & 1u;
-      const uint64_t mk = kr[e] & pmask;
-      const bool eq = in_cls && mk == prefix;
+      const uint32_t mk = hi[e] & pmask;
+      bool eq;
+      if (!stage_b) {
+        sel = ((abits >> e) & 1u) || (in_cls && mk > prefix);
+        eq = in_cls && mk == prefix;
+      } else {
+        const bool tied = (ebits >> e) & 1u;
+        const uint32_t mk2 = lo[e] & pmask2;
+        sel = ((abits >> e) & 1u) || (in_cls && mk > prefix) || (tied && mk2 > prefix2);
+        eq = tied && mk2 == prefix2;
+      }
       const uint64_t eqb = __ballot(eq);
       const int rank = ties_seen + __popcll(eqb & lanemask_lt(lane));
-      sel = ((abits >> e) & 1u) || (in_cls && mk > prefix) || (eq && rank < need);
+      sel = sel || (eq && rank < need);
       ties_seen += __popcll(eqb);
     }
-    sel = valid && (sel || ((bbits >> e) & 1u));
+    sel = ((vbits >> e) & 1u) && (sel || ((bbits >> e) & 1u));
     const uint64_t selb = __ballot(sel);
     const int p = pos + __popcll(selb & lanemask_lt(lane));
     if (sel && p < kmax) out[p] = j;
@@ -502,21 +573,22 @@ __global__ __launch_bounds__(kSelMaxThreads) void select_kernel(
     const int i = r0 + row;
     if (!(row < TR && i < nb)) continue;  // wave-uniform
     const uint64_t* keys = s_keys + (uint64_t)row * nb;
-    uint64_t kr[NPL > 0 ? NPL : 1];
+    const uint64_t rowi = bh * (uint64_t)nb + i;
     if constexpr (NPL > 0) {
+      uint32_t hi[NPL];
 #pragma unroll
       for (int e = 0; e < NPL; ++e) {
         const int j = 64 * e + lane;
-        kr[e] = j < nb ? keys[j] : 0ull;
+        hi[e] = j < nb ? (uint32_t)(keys[j] >> 32) : 0u;
       }
-    }
-    const uint64_t rowi = bh * (uint64_t)nb + i;
-    if constexpr (NPL > 0)
-      select_row_regs<NPL>(kr, nb, lane, s_hist, i, topk, band, kmax,
-                           kept_idx + rowi * (uint64_t)kmax, kept_cnt + rowi);
-    else
+      select_row_split<NPL>(
+          hi, [&](int e) { return (uint32_t)keys[64 * e + lane]; }, nb, lane, s_hist, i, topk,
+          band, kmax, kept_idx + rowi * (uint64_t)kmax, kept_cnt + rowi);
+    } else {
+      uint64_t kr[1];
       select_row_lds<NPL>(keys, kr, nb, lane, s_hist, i, topk, band, kmax,
                           kept_idx + rowi * (uint64_t)kmax, kept_cnt + rowi);
+    }
   }
 }
 
@@ -624,28 +696,28 @@ __global__ __launch_bounds__(256) void score_keys_kernel(
 }
 
 // Selection from the keys of score_keys_kernel: one wave per query block,
-// its keys loaded into registers (nb <= 64 * NPL), one histogram per wave.
+// the high halves of its keys kept in registers (nb <= 64 * NPL), the low
+// halves read again (from L2) only for ties, one histogram per wave.
 template <int NPL>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QSA_SEL_ROWS_WAVES))) void select_rows_kernel(const uint64_t* __restrict__ keys,
-                                                          int nb, uint64_t bh0, int topk,
-                                                          Band band, int kmax,
-                                                          int32_t* __restrict__ kept_idx,
-                                                          int32_t* __restrict__ kept_cnt) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QSA_SEL_ROWS_WAVES))) void select_rows_kernel(
+    const uint64_t* __restrict__ keys, int nb, uint64_t bh0, int topk, Band band, int kmax,
+    int32_t* __restrict__ kept_idx, int32_t* __restrict__ kept_cnt) {
   static_assert(NPL > 0, "keys in registers");
   __shared__ uint32_t s_hist_all[4 * kHist];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int i = blockIdx.x * 4 + wave;
   if (i >= nb) return;  // wave-uniform; no workgroup barrier follows
   const uint64_t* row = keys + ((uint64_t)blockIdx.y * nb + i) * key_stride(nb);
-  uint64_t kr[NPL];
+  uint32_t hi[NPL];
 #pragma unroll
   for (int e = 0; e < NPL; ++e) {
     const int j = 64 * e + lane;
-    kr[e] = j < nb ? row[j] : 0ull;
+    hi[e] = j < nb ? (uint32_t)(row[j] >> 32) : 0u;
   }
   const uint64_t rowi = (bh0 + blockIdx.y) * (uint64_t)nb + i;
-  select_row_regs<NPL>(kr, nb, lane, s_hist_all + wave * kHist, i, topk, band, kmax,
-                       kept_idx + rowi * (uint64_t)kmax, kept_cnt + rowi);
+  select_row_split<NPL>(
+      hi, [&](int e) { return (uint32_t)row[64 * e + lane]; }, nb, lane, s_hist_all + wave * kHist, i,
+      topk, band, kmax, kept_idx + rowi * (uint64_t)kmax, kept_cnt + rowi);
 }
 
 }  // namespace

@@ -13,12 +13,16 @@ select tests of test_gpu_parity.py check for both entry points):
 * each register width of the select pass (rows of up to 1,024, 1,536 and
   2,048 blocks), head_dim 64 and 128, ragged last blocks;
 * more than 2,048 blocks falls back to the one-pass kernel;
-* the full Wan-14B 720p shape, all 40 heads.
+* the full Wan-14B 720p shape, all 40 heads;
+* rows whose scores agree in the high 32 bits of their order keys and differ
+  below (the select orders such ties by the low halves), with exact
+  duplicates among them (index order), against the oracle on every row.
 """
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import qsa_gen
 from quantized_sparse_attention_amd import binding as B
 
@@ -103,3 +107,48 @@ def test_fullsize_720p_all_heads():
     slice_b = B.qsa_select_slice_bytes(w.batch, w.heads, w.seq_len, w.head_dim, w.block)
     got = _select(front, w, w.topk, w.band, w.kmax, _work(8 * slice_b))  # five passes
     _same(got, want, "720p")
+
+
+@pytest.mark.parametrize("nb", [300, 1300, 2000])
+def test_high_half_ties(nb):
+    """Pooled sums built so that S_ij = 127 * 8128^2 + pq[i,127] * pk[j,127]
+    with pq[i,127] in [1, 8]: a row's scores lie within about 2^-16 of each
+    other, so tens of keys share their high 32 bits (sign, exponent, top 20
+    mantissa bits) and the order among them is in the low bits.  30-50 % of
+    a head's columns take one of max(30, nb/10) shared sums, so the tied sets
+    also hold exact duplicates (index order; exact ties at the k-th place
+    themselves are the ties-and-ranges tests' case).  Equal scales, full
+    blocks (L = 64 nb); all rows of a head share the column order, so eight
+    heads give eight boundary cases."""
+    rng = np.random.default_rng(nb)
+    H, D, bs = 8, 128, 64
+    L = nb * bs
+    pq = np.full((1, H, nb, D), 8128, np.int32)
+    pk = np.full((1, H, nb, D), 8128, np.int32)
+    pq[..., 127] = rng.integers(1, 9, size=(1, H, nb))
+    last = rng.integers(-8128, 8129, size=(1, H, nb))
+    ns = max(30, nb // 10)
+    shared = rng.integers(-8128, 8129, size=ns)
+    dup = rng.random((1, H, nb)) < rng.uniform(0.3, 0.5, size=(1, H, 1))
+    last[dup] = shared[rng.integers(0, ns, size=int(dup.sum()))]
+    pk[..., 127] = last
+    sq = np.full((1, H, nb), np.float32(1.0) / np.float32(127.0), np.float32)
+    sk = sq.copy()
+    topk = (15 * nb + 99) // 100
+    kmax = topk + 1
+    scores = oracle.block_scores(pq, sq, pk, sk, L, bs)
+    want_idx, want_cnt = oracle.select_blocks(scores, topk, (0,), kmax)
+    # the case is what it claims: at the k-th place, high halves tied with the
+    # low halves apart
+    srt = np.sort(scores, axis=-1)[..., ::-1]
+    a, b = srt[..., topk - 1], srt[..., topk]
+    hi_tie = (a.view(np.uint64) >> np.uint64(32)) == (b.view(np.uint64) >> np.uint64(32))
+    assert np.mean(hi_tie & (a != b)) > 0.5
+    dev = lambda x: torch.from_numpy(np.ascontiguousarray(x)).cuda()  # noqa: E731
+    front = (dev(pq), dev(sq), dev(pk), dev(sk))
+    w = TINY.with_(grid=(1, 1, L), head_dim=D, block=bs, heads=H)
+    for work in (None, _work(B.qsa_select_slice_bytes(1, H, L, D, bs) * H)):
+        got = _select(front, w, topk, (0,), kmax, work)
+        what = "one pass" if work is None else "workspace"
+        assert np.array_equal(got[1], want_cnt), f"{what}: counts"
+        assert np.array_equal(got[0], want_idx), f"{what}: kept lists"
