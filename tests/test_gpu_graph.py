@@ -1,7 +1,8 @@
 """HIP-graph capture of the hot path's two step kinds.
 
 Every entry point takes its buffers from the caller, allocates nothing and
-records no memset, so a sparse step (quantise Q and K, select, order, the
+records no memset, so a sparse step (quantise Q and K, select through the
+caller's workspace, order, the
 sparse attention with the cached r and dr) and a refresh step (the same front
 end, then full + sparse attention writing r and dr in place) can each be
 captured once and replayed on new inputs copied into the captured buffers.
@@ -44,6 +45,9 @@ class StepBuffers:
         self.r = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
         self.dr = torch.zeros(shape, dtype=torch.bfloat16, device=dev)
         self.out = torch.empty(shape, dtype=torch.bfloat16, device=dev)
+        # the select's score keys (qsa_select_blocks_work, every slice in one pass)
+        self.work = torch.empty(B.qsa_select_slice_bytes(Bn, H, L, D, W.block) * Bn * H,
+                                dtype=torch.uint8, device=dev)
         self.L, self.D = L, D
 
     def load(self, x):
@@ -55,7 +59,7 @@ class StepBuffers:
         B.qsa_quantize(self.q, W.block, self.qc, self.qs, self.qp)
         B.qsa_quantize(self.k, W.block, self.kc, self.ks, self.kp)
         B.qsa_select_blocks(self.qp, self.qs, self.kp, self.ks, self.L, W.block, W.topk,
-                            W.band, W.kmax, self.idx, self.cnt)
+                            W.band, W.kmax, self.idx, self.cnt, work=self.work)
         B.qsa_order_query_blocks(self.idx, self.cnt, self.L, W.block, self.D, self.order)
         args = (self.qc, self.qs, self.kc, self.ks, self.v, self.idx, self.cnt)
         if refresh:
