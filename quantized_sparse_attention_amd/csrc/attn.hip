@@ -768,10 +768,14 @@ struct JitWalk {
   static constexpr bool on = QSA_ATTN_JIT && BS == 64 && D == 128;
 };
 
-template <int BS, int D, int QB, bool REFRESH>
+// WIN: each query block keeps the blocks of its own window of a.win_blocks
+// blocks (the local and global passes of windowed attention); the group walks
+// the union of its blocks' windows in ascending order without kept lists.
+template <int BS, int D, int QB, bool REFRESH, bool WIN = false>
 __global__ __launch_bounds__((QB * BS / 32 * 64))
 __attribute__((amdgpu_waves_per_eu(JitWalk<BS, D, REFRESH>::on ? QSA_ATTN_JIT_WAVES : 2, 8))) void attn_kernel(
     AttnArgs a, int L, int nb, uint32_t n_work) {
+  static_assert(!(WIN && REFRESH), "windowed kept sets in the sparse kernel only");
   using C = Cfg<BS, D>;
   constexpr int NWV = QB * C::WPB;  // waves in the workgroup
   constexpr int THREADS = 64 * NWV;
@@ -840,8 +844,9 @@ __attribute__((amdgpu_waves_per_eu(JitWalk<BS, D, REFRESH>::on ? QSA_ATTN_JIT_WA
   x.lane = lane;
   x.c0 = i < nb ? a.sm_scale * a.q_scales[bh * (uint64_t)nb + i] * kLog2e : 0.0f;
 
-  build_kept_bits<QB, THREADS>(s_bits, a, row0, [&](int b) { return block_at(b); }, nq, nb,
-                               tid);
+  if constexpr (!WIN)
+    build_kept_bits<QB, THREADS>(s_bits, a, row0, [&](int b) { return block_at(b); }, nq, nb,
+                                 tid);
   const int n_tiles = (L + KT - 1) / KT;
   const int tail_t = (L % KT) ? n_tiles - 1 : -1;
   const int myb = i < nb ? qsub : -1;
@@ -853,8 +858,35 @@ __attribute__((amdgpu_waves_per_eu(JitWalk<BS, D, REFRESH>::on ? QSA_ATTN_JIT_WA
   acc.init();
   const size_t row_off = head_off + (size_t)qrow * D;
   float inv_k = 0.0f;
+  if constexpr (WIN) {
+    // tiles of the group's windows [t0, t1) and of this block's own [k0, k1)
+    const int per = a.win_blocks;
+    const int g0 = (int)grp * QB;
+    const int w0 = (g0 / per) * per, w1 = min(nb, ((g0 + nq - 1) / per + 1) * per);
+    const int m0 = myb >= 0 ? (i / per) * per : 0;
+    const int m1 = myb >= 0 ? min(nb, m0 + per) : 0;
+    const int t0 = w0 * C::SUB, t1 = min(n_tiles, w1 * C::SUB);
+    const int k0 = m0 * C::SUB, k1 = min(n_tiles, m1 * C::SUB);
+    int t = t0;
+    auto next = [&](bool& keep) {
+      if (t == tail_t) ++t;  // the short last tile is walked apart
+      if (t >= t1) return -1;
+      keep = t >= k0 && t < k1;
+      return t++;
+    };
+#if QSA_ATTN_JIT
+    if constexpr (JitWalk<BS, D, REFRESH>::on)
+      walk_jit<BS, D, NWV>(x, qb, lo, acc, next);
+    else
+#endif
+      walk<BS, D, NWV>(x, qb, lo, acc, next);
+    if (tail_t >= t0 && tail_t < t1)
+      tail_tile<BS, D, NWV>(x, qb, lo, acc, tail_t, tail_t >= k0 && tail_t < k1);
+    const float lk = acc.l + __shfl_xor(acc.l, 32, 64);
+    inv_k = lk > 0.0f ? 1.0f / lk : 0.0f;
+  }
 #pragma unroll 1
-  for (int phase = 0; phase < (REFRESH ? 2 : 1); ++phase) {
+  for (int phase = 0; phase < (WIN ? 0 : REFRESH ? 2 : 1); ++phase) {
     BitWalk<QB, C::SUB> w;
     w.init(s_bits, nb, nq, myb, n_tiles, tail_t, phase == 1);
 #if QSA_ATTN_JIT
@@ -989,13 +1021,13 @@ __attribute__((amdgpu_waves_per_eu(JitWalk<BS, D, REFRESH>::on ? QSA_ATTN_JIT_WA
   }
 }
 
-template <int BS, int D, int QB, bool REFRESH>
+template <int BS, int D, int QB, bool REFRESH, bool WIN = false>
 hipError_t launch_t(const qsa_dims& d, const AttnArgs& a, hipStream_t s) {
   const int nb = (d.seq_len + BS - 1) / BS;
   const uint32_t ng = (uint32_t)((nb + QB - 1) / QB);
   const uint32_t n_work = (uint32_t)((uint64_t)d.batch * d.heads * ng);
-  hipLaunchKernelGGL((attn_kernel<BS, D, QB, REFRESH>), dim3(n_work), dim3(QB * BS / 32 * 64),
-                     0, s, a, d.seq_len, nb, n_work);
+  hipLaunchKernelGGL((attn_kernel<BS, D, QB, REFRESH, WIN>), dim3(n_work),
+                     dim3(QB * BS / 32 * 64), 0, s, a, d.seq_len, nb, n_work);
   return hipGetLastError();
 }
 
@@ -1005,14 +1037,15 @@ hipError_t launch_t(const qsa_dims& d, const AttnArgs& a, hipStream_t s) {
 // their kept sets), and the waves of a group split each tile's loads evenly,
 // which bounds the group size.  Two 64-token blocks for the 64-token kernels
 // and for 128-token blocks with D = 128, one for 128-token blocks with D = 64.
-template <bool REFRESH>
+template <bool REFRESH, bool WIN = false>
 hipError_t dispatch(const qsa_dims& d, const AttnArgs& a, hipStream_t s) {
   constexpr int Q64 = QSA_ATTN_QB;
   constexpr int Q64s = QSA_ATTN_QB < 2 ? QSA_ATTN_QB : 2;
-  if (d.block == 64 && d.head_dim == 128) return launch_t<64, 128, Q64, REFRESH>(d, a, s);
-  if (d.block == 64 && d.head_dim == 64) return launch_t<64, 64, Q64s, REFRESH>(d, a, s);
-  if (d.block == 128 && d.head_dim == 128) return launch_t<128, 128, Q64s, REFRESH>(d, a, s);
-  return launch_t<128, 64, 1, REFRESH>(d, a, s);
+  if (d.block == 64 && d.head_dim == 128) return launch_t<64, 128, Q64, REFRESH, WIN>(d, a, s);
+  if (d.block == 64 && d.head_dim == 64) return launch_t<64, 64, Q64s, REFRESH, WIN>(d, a, s);
+  if (d.block == 128 && d.head_dim == 128)
+    return launch_t<128, 128, Q64s, REFRESH, WIN>(d, a, s);
+  return launch_t<128, 64, 1, REFRESH, WIN>(d, a, s);
 }
 
 }  // namespace
@@ -1023,6 +1056,11 @@ hipError_t launch_sparse_attn(const qsa_dims& d, const AttnArgs& a, hipStream_t 
 
 hipError_t launch_full_attn_residual(const qsa_dims& d, const AttnArgs& a, hipStream_t s) {
   return dispatch<true>(d, a, s);
+}
+
+hipError_t launch_sparse_attn_window(const qsa_dims& d, const AttnArgs& a, hipStream_t s) {
+  if (a.win_blocks < 1 || a.order != nullptr) return hipErrorInvalidValue;
+  return dispatch<false, true>(d, a, s);
 }
 
 }  // namespace qsa

@@ -104,10 +104,16 @@ struct AttnArgs {
   // inverse).  out_w must divide L.
   int32_t out_map;
   int32_t out_w;
+  // launch_sparse_attn_window only: query block i keeps the win_blocks blocks
+  // of its own window, [i - i % win_blocks, ...) (kept_idx, kept_cnt unused)
+  int32_t win_blocks;
 };
 
 hipError_t launch_sparse_attn(const qsa_dims& d, const AttnArgs& a, hipStream_t s);
 hipError_t launch_full_attn_residual(const qsa_dims& d, const AttnArgs& a, hipStream_t s);
+// launch_sparse_attn for windowed kept sets (a.win_blocks), walked without
+// kept lists; the query blocks in natural order (a.order unused)
+hipError_t launch_sparse_attn_window(const qsa_dims& d, const AttnArgs& a, hipStream_t s);
 
 hipError_t launch_order(const qsa_dims& d, const int32_t* kept_idx, const int32_t* kept_cnt,
                         int32_t kmax, int32_t* order, hipStream_t s);
@@ -138,9 +144,8 @@ hipError_t l1_static_scratch(double** work);
 
 // SQuad two-pass attention: scratch layout (byte offsets, 256-aligned).
 struct SquadPlan {
-  int kmax;
   uint64_t bytes;
-  uint64_t q_codes, k_codes, q_scales, k_scales, q_pooled, k_pooled, kept_idx, kept_cnt;
+  uint64_t q_codes, k_codes, q_scales, k_scales, q_pooled, k_pooled;
   uint64_t o_local;
 };
 SquadPlan squad_plan(const qsa_dims& d, int window);

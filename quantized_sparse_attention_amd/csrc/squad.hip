@@ -4,15 +4,17 @@
 // §1): a sequence of n tokens is cut into windows of w consecutive tokens;
 // a local softmax pass mixes each window, then a global softmax pass mixes
 // the tokens at the same position of every window, with the local output as
-// its values.  Both passes here are the block-sparse int8/bf16 attention of
-// attn.hip with block-diagonal kept lists: the local pass over windows of w
-// tokens in the natural order, the global pass over groups of n/w tokens in
-// position-major order (token p of window k at p*(n/w) + k), so every group
-// is a run of whole blocks and both passes run as dense tiles.
+// its values.  Both passes here are the int8/bf16 attention of attn.hip in
+// its windowed mode (each query block keeps the blocks of its own window,
+// walked without kept lists): the local pass over windows of w tokens in the
+// natural order, the global pass over groups of n/w tokens in position-major
+// order (token p of window k at p*(n/w) + k), so every group is a run of
+// whole blocks and both passes run as dense tiles.
 //
-// Kernels of their own: the kept lists of block-diagonal attention, and the
-// reorder between window-major and position-major order (a row gather of
-// 16-byte chunks, HBM-bound; exported for callers that need it).  The
+// Kernels of their own: the kept lists of block-diagonal attention (exported
+// for callers that run the passes through qsa_sparse_attn), and the reorder
+// between window-major and position-major order (a row gather of 16-byte
+// chunks, HBM-bound; exported for callers that need it).  The
 // operator itself reorders nothing: the global pass quantises Q and K from
 // rows gathered in position-major order, the local pass writes its output
 // rows in position-major order and the global pass writes its rows back in
@@ -84,8 +86,6 @@ SquadPlan squad_plan(const qsa_dims& d, int window) {
   const uint64_t bh = (uint64_t)d.batch * d.heads;
   const uint64_t n = (uint64_t)d.seq_len, D = (uint64_t)d.head_dim;
   const uint64_t nb = n / (uint64_t)d.block;
-  const int m = d.seq_len / window;
-  p.kmax = (window > m ? window : m) / d.block;
   auto take = [&](uint64_t bytes) {
     const uint64_t off = p.bytes;
     p.bytes += (bytes + 255) / 256 * 256;
@@ -98,8 +98,6 @@ SquadPlan squad_plan(const qsa_dims& d, int window) {
   p.k_scales = take(bh * nb * 4);
   p.q_pooled = take(bh * nb * D * 4);
   p.k_pooled = take(bh * nb * D * 4);
-  p.kept_idx = take(bh * nb * (uint64_t)p.kmax * 4);
-  p.kept_cnt = take(bh * nb * 4);
   p.o_local = take(bh * n * D * 2);
   return p;
 }
@@ -114,8 +112,6 @@ hipError_t launch_squad(const qsa_dims& d, const uint16_t* q, const uint16_t* k,
   float* ks = reinterpret_cast<float*>(work + p.k_scales);
   int32_t* qp = reinterpret_cast<int32_t*>(work + p.q_pooled);
   int32_t* kp = reinterpret_cast<int32_t*>(work + p.k_pooled);
-  int32_t* idx = reinterpret_cast<int32_t*>(work + p.kept_idx);
-  int32_t* cnt = reinterpret_cast<int32_t*>(work + p.kept_cnt);
   uint16_t* o_local = reinterpret_cast<uint16_t*>(work + p.o_local);
   const int m = d.seq_len / window;
 
@@ -124,10 +120,7 @@ hipError_t launch_squad(const qsa_dims& d, const uint16_t* q, const uint16_t* k,
   a.q_scales = qs;
   a.k_codes = kc;
   a.k_scales = ks;
-  a.kept_idx = idx;
-  a.kept_cnt = cnt;
-  a.order = nullptr;
-  a.kmax = p.kmax;
+  a.order = nullptr;  // windowed kept sets: no lists
   a.sm_scale = sm_scale;
 
   hipError_t e;
@@ -137,22 +130,22 @@ hipError_t launch_squad(const qsa_dims& d, const uint16_t* q, const uint16_t* k,
   // rows are written in position-major order, ready as the global values
   QSA_TRY(launch_quantize(d, q, qc, qs, qp, s));
   QSA_TRY(launch_quantize(d, k, kc, ks, kp, s));
-  QSA_TRY(launch_window_kept(d, window, p.kmax, idx, cnt, s));
   a.v = v;
   a.out = o_local;
   a.out_map = 1;
   a.out_w = window;
-  QSA_TRY(launch_sparse_attn(d, a, s));
+  a.win_blocks = window / d.block;
+  QSA_TRY(launch_sparse_attn_window(d, a, s));
   // global pass: groups of n/w tokens in position-major order (Q and K
   // quantised from rows gathered in that order), values the local output;
   // its output rows are written back in the natural order
   QSA_TRY(launch_quantize_position_major(d, q, window, qc, qs, qp, s));
   QSA_TRY(launch_quantize_position_major(d, k, window, kc, ks, kp, s));
-  QSA_TRY(launch_window_kept(d, m, p.kmax, idx, cnt, s));
   a.v = o_local;
   a.out = out;
   a.out_map = 2;
-  QSA_TRY(launch_sparse_attn(d, a, s));
+  a.win_blocks = m / d.block;
+  QSA_TRY(launch_sparse_attn_window(d, a, s));
 #undef QSA_TRY
   return hipSuccess;
 }
