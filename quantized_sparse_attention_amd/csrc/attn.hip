@@ -463,10 +463,13 @@ __device__ __forceinline__ void build_kept_bits(uint32_t* bits, const AttnArgs& 
     if (blk < 0) continue;
     const uint64_t row = row0 + blk;
     const int32_t* kl = a.kept_idx + row * (uint64_t)a.kmax;
-    const int cnt = min(max(a.kept_cnt[row], 0), a.kmax);
-    for (int p = tid; p < cnt; p += THREADS) {
+    // the count and the entries are read together (one memory round trip);
+    // entries past the count are ignored
+    const int cnt_raw = a.kept_cnt[row];
+    for (int p = tid; p < a.kmax; p += THREADS) {
       const int j = kl[p];
-      if (j >= 0 && j < nb) atomicOr(&bits[b * nw + (j >> 5)], 1u << (j & 31));
+      const int cnt = min(max(cnt_raw, 0), a.kmax);
+      if (p < cnt && j >= 0 && j < nb) atomicOr(&bits[b * nw + (j >> 5)], 1u << (j & 31));
     }
   }
   __syncthreads();
@@ -828,9 +831,9 @@ __attribute__((amdgpu_waves_per_eu(JitWalk<BS, D, REFRESH>::on ? QSA_ATTN_JIT_WA
                                                    g * (D / 2) + 16 * c)
                    : v4i{0, 0, 0, 0};
   }
-  // the Q operands are in registers before any tile load is issued: no wait
-  // for them is left for the compiler to place inside the tile loop
-  __builtin_amdgcn_s_waitcnt(0x0f70);
+  // the Q loads stay in flight while the kept sets are read (their waits
+  // cover them: loads complete in order); in the windowed mode the first
+  // tile's wait does
   LaneOffs<BS, D> lo;
   lo.init(lane);
   Ctx<BS, D> x;
