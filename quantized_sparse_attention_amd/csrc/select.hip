@@ -5,30 +5,42 @@
 // top-k salient local guidance): every query block keeps the key blocks whose
 // mean-pooled dequantised codes score highest, plus a fixed band of offsets.
 //
-// One workgroup per (batch*head, tile of TR query blocks): TR = 16 with 8
-// waves when the tile's keys fit the LDS (up to 1,216 key blocks; one
-// workgroup per CU), else TR = 8 with 4 waves (two per CU) or fewer rows.
+// Two ways to run it, with the same scores, keys and selection code, so the
+// same kept lists bit for bit:
+//  * qsa_select_blocks: one workgroup per (batch*head, tile of TR query
+//    blocks), TR = 16 with 8 waves when the tile's keys fit the LDS (up to
+//    1,216 key blocks; one workgroup per CU), else TR = 8 with 4 waves or
+//    fewer rows; the keys stay in LDS between scoring and selection.
+//  * qsa_select_blocks_work: the keys of whole (batch, head) slices go to a
+//    caller workspace (score_keys_kernel, many workgroups per CU), then one
+//    wave per query block selects from them (select_rows_kernel).
+// The steps:
 //  1. Exact integer scores S_ij = sum_d Pq[i,d] Pk[j,d] on the int8 MFMA:
 //     each pooled sum P (|P| <= 127*128) is split into int8 digits
 //     P = 128*hi + lo with lo in [0,127], hi in [-127,127], and
 //       S = 16384*sum(hi*hi') + 128*(sum(hi*lo') + sum(lo*hi')) + sum(lo*lo')
 //     where every partial sum fits int32 and the recombination is exact in
 //     fp64 (all values are integers below 2^53).
-//  2. score = fl64(fl64(S * sq*sk) / (n_i*n_j)) in IEEE fp64, mapped to an
-//     order-preserving uint64 key (-0 canonicalised to +0), kept in LDS.
-//  3. Per row (one wave), a radix select finds the k-th largest key.  Its
-//     sign class comes first from ballot counts (keys of score >= 0 are
-//     >= 2^63): if fewer than k keys are in the upper class, all of them are
-//     taken and the rest is chosen in the lower one.  Inside the class,
-//     t = key - (smallest key of the class) keeps the order, and the digits
-//     (8 bits, the last one shorter) start at the top bit of the class's
-//     range, so no pass is spent on the sign and exponent bits most keys
-//     share.  The passes stop once the bin holding the k-th key is taken
-//     whole; the threshold is then known on its decided bits only.
+//  2. score = fl64(fl64(S * sq*sk) / (n_i*n_j)) in IEEE fp64 (a power-of-two
+//     count as an exact ldexp), mapped to an order-preserving uint64 key (-0
+//     canonicalised to +0).
+//  3. Per row (one wave), a radix select finds the k-th largest key, on the
+//     keys' high 32 bits first (a monotone function of the key); the slots
+//     tied there are ordered by their low halves.  The sign class comes first
+//     from ballot counts (keys of score >= 0 have the top bit set): if fewer
+//     than k keys are in the upper class, all of them are taken and the rest
+//     is chosen in the lower one.  Inside the class, t = hi - (smallest high
+//     half of the class) keeps the order, and the digits (8 bits, the last
+//     one shorter) start at the top bit of the class's range, so no pass is
+//     spent on the sign and exponent bits most keys share.  The passes stop
+//     once the bin holding the k-th key is taken whole; the threshold is
+//     then known on its decided bits only.
 //  4. Ascending compaction with wave ballots: j is kept if its key is in the
 //     class above the candidates', or it is a candidate whose decided bits
-//     of t exceed the threshold's, or equal them with fewer than `need`
+//     exceed the threshold's, or equal them with fewer than `need`
 //     lower-indexed equal candidates before it, or j - i is a band offset.
+// Rows of more than 2,048 key blocks take the one-pass kernel and the same
+// steps on full 64-bit keys read from LDS each pass.
 #include "qsa_internal.h"
 
 #pragma clang fp contract(off)
