@@ -10,8 +10,9 @@
 //
 // Bit-exactness: the scale is an IEEE fp32 division amax / 127 and each code
 // the round-half-even of an IEEE fp32 division x / scale, reached through a
-// multiplication by 1 / scale and an exact check of the remainder (the
-// division itself only for the rare quotients next to a half-integer).  The
+// multiplication by 1 / scale and a check of that product's distance to its
+// rounding (the division itself only for the rare quotients next to a
+// half-integer).  The
 // library is compiled with correctly rounded fp32 division, no fast-math and
 // no FP contraction in this file, and fp32 denormals preserved.
 //
@@ -47,17 +48,15 @@ __device__ __forceinline__ float wave_max(float v) {
 // value of that integer.
 //
 // Without a division per element: with inv = fl32(1 / s), p = fl32(x * inv)
-// is within 127 * 2^-23 < 2^-16 of the exact quotient q = x / s, and so is
-// fl32(q) (half an ulp below 128 is 2^-18).  Unless q lies within 2^-16 of a
-// half-integer, p, q and fl32(q) round to the same integer c = rint(p).  The
-// remainder d = fl32(x - c s) (one fused rounding) tells: | |d| - s/2 | >
-// 2^-14 s implies | |q - c| - 1/2 | > 2^-16 (the roundings of d and of the
-// test move it by less than 2^-23 s), so c is right; otherwise the element
-// takes the IEEE division.  Needs 1 / s finite and s 2^-14 normal: the caller
-// takes the division for every element when s < 2^-100.
-__device__ __forceinline__ bool near_half(float x, float c, float s) {
-  const float d = __builtin_fmaf(-c, s, x);
-  return !(fabsf(fabsf(d) - 0.5f * s) > s * 0x1p-14f);
+// is within 127 * 2^-23 < 2^-16 of the exact quotient q = x / s, and fl32(q)
+// within half an ulp below 128, 2^-18, of q.  c = rint(p) and d = p - c are
+// exact (d by Sterbenz's lemma).  If |d| <= 1/2 - 2^-15 then |q - c| <
+// 1/2 - 2^-16 and |fl32(q) - c| < 1/2 - 2^-16 + 2^-18 < 1/2, so c is
+// rint(fl32(q)); otherwise the element takes the IEEE division.  Needs 1 / s
+// finite and normal: the caller takes the division for every element when
+// s < 2^-100.
+__device__ __forceinline__ bool near_half(float p, float c) {
+  return !(fabsf(p - c) <= 0.5f - 0x1p-15f);
 }
 
 __device__ __forceinline__ void codes8(const float (&x)[8], float s, float inv, bool fast,
@@ -66,14 +65,15 @@ __device__ __forceinline__ void codes8(const float (&x)[8], float s, float inv, 
   if (fast) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      q[e] = __builtin_rintf(x[e] * inv);
-      any_div |= near_half(x[e], q[e], s);
+      const float p = x[e] * inv;
+      q[e] = __builtin_rintf(p);
+      any_div |= near_half(p, q[e]);
     }
   }
   if (any_div) {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      if (!fast || near_half(x[e], q[e], s)) q[e] = __builtin_rintf(x[e] / s);
+      if (!fast || near_half(x[e] * inv, q[e])) q[e] = __builtin_rintf(x[e] / s);
   }
 #pragma unroll
   for (int e = 0; e < 8; ++e) q[e] = __builtin_amdgcn_fmed3f(q[e], -127.0f, 127.0f);

@@ -2,17 +2,16 @@
 
 The gfx950 quantiser (csrc/quantize.hip, ``codes8``) does not divide every
 element by the block scale.  With s = fl32(amax / 127) and inv = fl32(1 / s)
-it takes c = rint(fl32(x * inv)), forms the remainder d = fl32(x - c * s) with
-one fused rounding, and falls back to the IEEE quotient rint(fl32(x / s)) only
-when | |d| - s/2 | <= 2^-14 s (a quotient within reach of a half-integer) or
-when s < 2^-100 (where 1 / s or 2^-14 s would leave the normal range).  The
+it takes p = fl32(x * inv) and c = rint(p), and falls back to the IEEE
+quotient rint(fl32(x / s)) only when |p - c| > 1/2 - 2^-15 (a quotient within
+reach of a half-integer) or when s < 2^-100 (where 1 / s would leave the
+normal range).  The
 oracle's step 1 (R2: code = clamp(rint(fl32(x / s)), -127, 127), QuantSparse,
 gist.science/es/paper/2509.23681, technical summary §1 and §4: 8-bit
 activations) always divides.
 
 This test runs that sequence of fp32 operations on the CPU, each written out
-with NumPy's IEEE fp32 arithmetic (the fused remainder is computed exactly in
-fp64 and rounded once to fp32), for every finite bf16 amax as block maximum
+with NumPy's IEEE fp32 arithmetic, for every finite bf16 amax as block maximum
 and every finite bf16 x whose quotient reaches at least 1/8 in magnitude
 (smaller quotients round to 0 on every path), and requires the codes to equal
 the oracle's bit for bit.  It also reports how rarely the division is taken.
@@ -38,13 +37,9 @@ def _codes_fast_path(x, s):
     fast = s >= F32(2.0 ** -100)
     with np.errstate(divide="ignore", over="ignore"):
         inv = np.where(fast, F32(1.0) / s, F32(0.0)).astype(F32)
-    q = np.rint((x * inv).astype(F32)).astype(F32)
-    # d = fma(-q, s, x): q * s is exact in fp64 (|q| <= 128, 24-bit s) and so
-    # is x - q * s (its operands lie within a few binades of each other or x
-    # is exact), so one rounding to fp32 gives the fused result
-    d = (x.astype(np.float64) - q.astype(np.float64) * s.astype(np.float64)).astype(F32)
-    band = ~(np.abs((np.abs(d) - (F32(0.5) * s).astype(F32)).astype(F32))
-             > (s * F32(2.0 ** -14)).astype(F32))
+    p = (x * inv).astype(F32)
+    q = np.rint(p).astype(F32)
+    band = ~(np.abs((p - q).astype(F32)) <= F32(0.5 - 2.0 ** -15))
     div = ~fast | band
     with np.errstate(divide="ignore", invalid="ignore"):
         qd = np.rint((x / s).astype(F32)).astype(F32)
