@@ -76,6 +76,28 @@ def test_squad_attention_parity(Bn, H, n, D, window, block):
     assert r <= REL_L2 and m <= _bound(x["v"])
 
 
+# More work items (b*h, group of query blocks) than the device holds
+# workgroups at once, with more heads than the other parity cases: every head
+# sampled at its ends and middle, and heads 0 and 1 (neighbouring items across
+# a head boundary), against the oracle over those whole heads.
+@pytest.mark.parametrize("Bn,H,n,D,window,block", [(1, 60, 4096, 64, 64, 64),
+                                                    (1, 30, 8192, 128, 128, 64),
+                                                    (2, 7, 16384, 128, 128, 128)])
+def test_squad_many_heads(Bn, H, n, D, window, block):
+    print(f"\n[squad many heads] B={Bn} H={H} n={n} D={D} w={window} block={block}", flush=True)
+    x = _inputs(Bn, H, n, D, seed=7 + D // 64, block=block)
+    out = B.qsa_squad_attention(dev_bf16(x["q"]), dev_bf16(x["k"]), dev_bf16(x["v"]), window,
+                                block)
+    torch.cuda.synchronize()
+    heads = [0, 1, H // 2, H - 1]
+    got = host_f64(out)[:, heads]
+    want = oracle.squad_attention(*(x[t][:, heads] for t in "qkv"), window, block)
+    r = rel_l2(got, want)
+    m = float(np.abs(got - want).max())
+    print(f"[squad many heads] heads {heads}: rel_l2={r:.2e} max_abs={m:.2e}", flush=True)
+    assert r <= REL_L2 and m <= _bound(x["v"][:, heads])
+
+
 def test_squad_fullsize_sampled():
     """A 65,536-token sequence (w = sqrt(n) = 256) of 24 heads x 128, the
     head shape of the Wan video DiTs: sampled query blocks of two heads
