@@ -20,13 +20,14 @@
 //     in a fixed order (deterministic), then diagonalises G by the cyclic
 //     Jacobi method (Golub and Van Loan, Matrix Computations, §8.5:
 //     symmetric Schur rotations; parallel round-robin ordering, D/2 disjoint
-//     rotations per round, D-1 rounds per sweep) in fp32 with G and the
-//     eigenvector matrix in LDS.  A round computes its D/2 rotations, then
-//     updates A one 2x2 block (rows of one pair x columns of another) at a
-//     time -- the row and the column rotation of a block in one step, since
-//     the block's new values depend on its own old ones only -- and V by
-//     columns: two barriers per round.  Each thread issues all LDS reads of
-//     its items before any write, so LDS latency overlaps across items.
+//     rotations per round, D-1 rounds per sweep) in fp32 with the upper
+//     triangle of G and the eigenvector matrix in LDS.  A round computes its
+//     D/2 rotations, then updates A one 2x2 block (rows of one pair x columns
+//     of another) at a time -- the row and the column rotation of a block in
+//     one step, since the block's new values depend on its own old ones only;
+//     A stays symmetric, so of two mirrored blocks only one is rotated -- and
+//     V by columns: two barriers per round.  Each thread issues all LDS reads
+//     of its items before any write, so LDS latency overlaps across items.
 //     Eigenvalues are ranked descending (ties: lower index).
 //  3. project_kernel: 32 token rows per wave on the bf16 MFMA: C^T = V_r^T X^T,
 //     then X V_r V_r^T = V_r C^T, with three-term bf16 splits of the basis and
@@ -168,18 +169,26 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(
   constexpr int NP = D / 2;        // disjoint rotations per round
   constexpr int IT = NP * D / T;   // (pair, row-or-column) items per thread
   constexpr int KS = T / D;        // pair stride between a thread's items
-  constexpr int BI = NP * NP / T;  // 2x2 blocks of A per thread
-  static_assert(IT * T == NP * D && KS * D == T && BI * T == NP * NP, "item split");
+  // 2x2 blocks of A per round, one of each mirrored pair: block (P, (P + d)
+  // mod NP) for d = 0 .. NP/2 - 1 and every P (index P * NP/2 + d), then for
+  // d = NP/2 the P < NP/2.  The NP/2 lanes that share a P read one row pair
+  // against distinct columns: a[i][j] and a[j][i] fall in one LDS bank (the
+  // row stride is 1 modulo the bank count), so those reads hit distinct banks
+  // whichever of the two places an entry has.
+  constexpr int NBLK = NP * (NP / 2) + NP / 2;
+  constexpr int BI = (NBLK + T - 1) / T;  // blocks per thread (the last round partial)
+  static_assert(IT * T == NP * D && KS * D == T, "item split");
   __shared__ float a[D * LD];
   __shared__ float v[D * LD];
-  __shared__ Rot rot[NP];
+  __shared__ Rot rot[2][NP];  // this round's rotations and the next round's
   __shared__ float red[T / 64];
   __shared__ int done;
 
   const uint64_t bh = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-  // G = sum of the partials in chunk order; upper triangle mirrored
+  // G = sum of the partials in chunk order (A holds the upper triangle; the
+  // lower one is written here but not used)
   const float* pb = partial + bh * (uint64_t)S * (D * D);
   float fro = 0.0f;
   for (int e = tid; e < D * D; e += T) {
@@ -206,53 +215,72 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(
   // this thread's items: pair k = k0 + KS n, row or column index = idx
   const int k0 = tid / D, idx = tid % D;
 
+  // Rotation tid (< NP) of round t from the current A, into dst; returns
+  // |a_pq| before the rotation.
+  auto make_rot = [&](int t, Rot* dst) {
+    int p, q;
+    if (tid == 0) {
+      p = t;
+      q = D - 1;
+    } else {
+      const int u = (t + tid) % (D - 1), w = (t - tid + (D - 1)) % (D - 1);
+      p = min(u, w);
+      q = max(u, w);
+    }
+    const float apq = a[p * LD + q];
+    float c = 1.0f, sn = 0.0f;
+    if (fabsf(apq) > tol) {
+      // symmetric Schur rotation: J = [[c, s], [-s, c]] zeroes a_pq
+      const float tau = (a[q * LD + q] - a[p * LD + p]) / (2.0f * apq);
+      const float tt = (tau >= 0.0f ? 1.0f : -1.0f) /
+                       (fabsf(tau) + sqrtf(__builtin_fmaf(tau, tau, 1.0f)));
+      c = 1.0f / sqrtf(__builtin_fmaf(tt, tt, 1.0f));
+      sn = tt * c;
+    }
+    dst[tid] = Rot{c, sn, p, q};
+    return fabsf(apq);
+  };
+
+  // A round's rotations depend on A only, so the next round's are computed
+  // (by the first wave) while this round's V update runs, between the A
+  // update and the round's last barrier.
+  int cur = 0;
+  float big_next = 0.0f;  // |a_pq| of round 0 of the next sweep (threads < NP)
+  if (tid < NP) big_next = make_rot(0, rot[0]);
+  __syncthreads();
   for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
-    float big = 0.0f;  // largest |a_pq| met in this sweep (threads < NP)
+    float big = big_next;  // largest |a_pq| met in this sweep (threads < NP)
     for (int t = 0; t < D - 1; ++t) {
-      if (tid < NP) {
-        int p, q;
-        if (tid == 0) {
-          p = t;
-          q = D - 1;
-        } else {
-          const int u = (t + tid) % (D - 1), w = (t - tid + (D - 1)) % (D - 1);
-          p = min(u, w);
-          q = max(u, w);
-        }
-        const float apq = a[p * LD + q];
-        big = fmaxf(big, fabsf(apq));
-        float c = 1.0f, sn = 0.0f;
-        if (fabsf(apq) > tol) {
-          // symmetric Schur rotation: J = [[c, s], [-s, c]] zeroes a_pq
-          const float tau = (a[q * LD + q] - a[p * LD + p]) / (2.0f * apq);
-          const float tt = (tau >= 0.0f ? 1.0f : -1.0f) /
-                           (fabsf(tau) + sqrtf(__builtin_fmaf(tau, tau, 1.0f)));
-          c = 1.0f / sqrtf(__builtin_fmaf(tt, tt, 1.0f));
-          sn = tt * c;
-        }
-        rot[tid] = Rot{c, sn, p, q};
-      }
-      __syncthreads();
+      const Rot* rt = rot[cur];
       // A <- J^T A J one 2x2 block at a time: block (P, Q) holds rows p, q of
       // pair P and columns r, s of pair Q, and its new values depend on its
       // four old ones only (the round's pairs are disjoint), so the row and
       // the column rotation of a block are one step with no barrier between.
-      // The rotated pair's off-diagonal entries are set to 0.
+      // Block (Q, P) is its transpose: only one of the two is rotated, its
+      // entries read and written at their upper-triangle places.  The rotated
+      // pair's off-diagonal entry is set to 0.
       {
         float b4[BI][4];
         Rot rp[BI], rq[BI];
+        int e4[BI][4];  // LDS places of the block's entries
 #pragma unroll
         for (int n = 0; n < BI; ++n) {
-          const int blk = tid + T * n;
-          rp[n] = rot[blk / NP];
-          rq[n] = rot[blk % NP];
-          b4[n][0] = a[rp[n].p * LD + rq[n].p];
-          b4[n][1] = a[rp[n].p * LD + rq[n].q];
-          b4[n][2] = a[rp[n].q * LD + rq[n].p];
-          b4[n][3] = a[rp[n].q * LD + rq[n].q];
+          const int blk = min(tid + T * n, NBLK - 1);
+          const int P = blk < NP * (NP / 2) ? blk / (NP / 2) : blk - NP * (NP / 2);
+          const int Q = (P + (blk < NP * (NP / 2) ? blk % (NP / 2) : NP / 2)) % NP;
+          rp[n] = rt[P];
+          rq[n] = rt[Q];
+          const int r0 = rp[n].p, r1 = rp[n].q, c0 = rq[n].p, c1 = rq[n].q;
+          e4[n][0] = min(r0, c0) * LD + max(r0, c0);
+          e4[n][1] = min(r0, c1) * LD + max(r0, c1);
+          e4[n][2] = min(r1, c0) * LD + max(r1, c0);
+          e4[n][3] = min(r1, c1) * LD + max(r1, c1);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) b4[n][e] = a[e4[n][e]];
         }
 #pragma unroll
         for (int n = 0; n < BI; ++n) {
+          if (tid + T * n >= NBLK) continue;
           if (rp[n].s == 0.0f && rq[n].s == 0.0f) continue;
           const float cp = rp[n].c, sp = rp[n].s, cq = rq[n].c, sq = rq[n].s;
           // rows: J_P^T
@@ -261,15 +289,26 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(
           // columns: J_Q
           float ypr = cq * xpr - sq * xps, yps = sq * xpr + cq * xps;
           float yqr = cq * xqr - sq * xqs, yqs = sq * xqr + cq * xqs;
-          if (rp[n].p == rq[n].p) {  // diagonal block: a_pq = a_qp = 0
-            yps = 0.0f;
-            yqr = 0.0f;
+          if (rp[n].p == rq[n].p) {  // diagonal block: a_pq = 0 (one place)
+            a[e4[n][0]] = ypr;
+            a[e4[n][1]] = 0.0f;
+            a[e4[n][3]] = yqs;
+            continue;
           }
-          a[rp[n].p * LD + rq[n].p] = ypr;
-          a[rp[n].p * LD + rq[n].q] = yps;
-          a[rp[n].q * LD + rq[n].p] = yqr;
-          a[rp[n].q * LD + rq[n].q] = yqs;
+          a[e4[n][0]] = ypr;
+          a[e4[n][1]] = yps;
+          a[e4[n][2]] = yqr;
+          a[e4[n][3]] = yqs;
         }
+      }
+      __syncthreads();  // A is updated
+      // the next round's rotations: round t + 1, or round 0 of the next sweep
+      if (tid < NP) {
+        const float m = make_rot(t + 1 < D - 1 ? t + 1 : 0, rot[cur ^ 1]);
+        if (t + 1 < D - 1)
+          big = fmaxf(big, m);
+        else
+          big_next = m;
       }
       // V <- V J
       {
@@ -277,7 +316,7 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(
         float vp[IT], vq[IT];
 #pragma unroll
         for (int n = 0; n < IT; ++n) {
-          r[n] = rot[k0 + KS * n];
+          r[n] = rt[k0 + KS * n];
           vp[n] = v[idx * LD + r[n].p];
           vq[n] = v[idx * LD + r[n].q];
         }
@@ -289,6 +328,7 @@ __global__ __launch_bounds__(kJacobiThreads) void jacobi_kernel(
         }
       }
       __syncthreads();
+      cur ^= 1;
     }
     if (wave == 0) {
       for (int o = 32; o >= 1; o >>= 1) big = fmaxf(big, __shfl_xor(big, o, 64));
