@@ -418,8 +418,8 @@ int qsa_reorder_windows(const qsa_dims* dims, int32_t window, int32_t inverse, c
 /*
  * qsa_squad_attention -- SQuad two-pass attention (technical summary,
  * methodology §1) on this path's attention core:
- *   1. local pass: qsa_quantize(Q), qsa_quantize(K) in the natural order,
- *      then block-sparse attention (as qsa_sparse_attn) over the windows of
+ *   1. local pass: the codes and scales of qsa_quantize(Q) and
+ *      qsa_quantize(K) in the natural order, then block-sparse attention (as qsa_sparse_attn) over the windows of
  *      `window` tokens, values V; output O_local, bf16;
  *   2. global pass: Q, K and O_local reordered to position-major order
  *      (qsa_reorder_windows), Q and K quantised in that order, attention over

@@ -57,11 +57,13 @@ hipError_t launch_quantize(const qsa_dims& d, const uint16_t* x, int8_t* codes, 
 hipError_t launch_quantize_rotated(const qsa_dims& d, const uint16_t* x, int8_t* codes,
                                    float* scales, int32_t* pooled, hipStream_t s);
 
-// qsa_quantize of the rows in position-major order of windows of `window`
-// tokens (row p*(L/window) + k is row k*window + p of x), gathered from x.
-hipError_t launch_quantize_position_major(const qsa_dims& d, const uint16_t* x, int window,
-                                          int8_t* codes, float* scales, int32_t* pooled,
-                                          hipStream_t s);
+// The codes and scales of qsa_quantize (no pooled sums) for two tensors of
+// the same shape in one launch; with window > 0, of their rows in
+// position-major order of windows of `window` tokens (row p*(L/window) + k
+// is row k*window + p of x), gathered from x.
+hipError_t launch_quantize_pair(const qsa_dims& d, const uint16_t* x, const uint16_t* x2,
+                                int window, int8_t* codes, int8_t* codes2, float* scales,
+                                float* scales2, hipStream_t s);
 
 hipError_t launch_select(const qsa_dims& d, const int32_t* pooled_q, const float* scale_q,
                          const int32_t* pooled_k, const float* scale_k, int32_t topk,
@@ -145,7 +147,7 @@ hipError_t l1_static_scratch(double** work);
 // SQuad two-pass attention: scratch layout (byte offsets, 256-aligned).
 struct SquadPlan {
   uint64_t bytes;
-  uint64_t q_codes, k_codes, q_scales, k_scales, q_pooled, k_pooled;
+  uint64_t q_codes, k_codes, q_scales, k_scales;
   uint64_t o_local;
 };
 SquadPlan squad_plan(const qsa_dims& d, int window);

@@ -150,20 +150,31 @@ __device__ __forceinline__ void fwht_row(float (&v)[8], int lane) {
 
 // MAP: the rows are quantised in position-major order of windows of w tokens
 // (row p*(L/w) + k of the quantised sequence is row k*w + p of x), read
-// straight from x.
-template <int BS, int D, bool ROT, bool MAP>
+// straight from x.  POOL: the pooled code sums are computed and written
+// (the windowed passes, which select nothing, skip them).  Workgroups
+// blockIdx.y = 0 and 1 quantise the two tensors of a pair (x2, codes2 and
+// scales2 for the second).
+template <int BS, int D, bool ROT, bool MAP, bool POOL = true>
 __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ x,
                                                        int8_t* __restrict__ codes,
                                                        float* __restrict__ scales,
                                                        int32_t* __restrict__ pooled, int L,
-                                                       int nb, int w) {
+                                                       int nb, int w,
+                                                       const uint16_t* __restrict__ x2 = nullptr,
+                                                       int8_t* __restrict__ codes2 = nullptr,
+                                                       float* __restrict__ scales2 = nullptr) {
+  if (blockIdx.y) {
+    x = x2;
+    codes = codes2;
+    scales = scales2;
+  }
   constexpr int CPR = D / 8;        // 16-byte chunks per token row
   constexpr int RPP = 256 / CPR;    // rows covered per pass
   constexpr int PASSES = BS / RPP;  // passes over the block
   static_assert(BS % RPP == 0, "block must be a multiple of rows per pass");
 
   __shared__ float s_amax[4];
-  __shared__ int32_t s_pool[4][D];
+  __shared__ int32_t s_pool[POOL ? 4 : 1][POOL ? D : 1];
 
   const uint32_t wg = blockIdx.x;
   const uint32_t i = wg % (uint32_t)nb;
@@ -225,12 +236,19 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
       }
       uint32_t lo, hi, pairs[4];
       pack_codes(q, lo, hi, pairs);
+      if constexpr (POOL) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) psum[k] = add_i16x2(psum[k], pairs[k]);
+        for (int k = 0; k < 4; ++k) psum[k] = add_i16x2(psum[k], pairs[k]);
+      }
       *reinterpret_cast<uint2*>(cb + (size_t)row * D) = make_uint2(lo, hi);
     }
   }
 
+  const uint64_t blk = bh * (uint64_t)nb + i;
+  if constexpr (!POOL) {
+    if (tid == 0) scales[blk] = s;
+    return;
+  }
   // reduce the per-lane channel sums over lanes holding the same channels
 #pragma unroll
   for (int o = CPR; o < 64; o <<= 1) {
@@ -246,7 +264,6 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
     }
   }
   __syncthreads();
-  const uint64_t blk = bh * (uint64_t)nb + i;
   if (tid < D) {
     pooled[blk * D + tid] = s_pool[0][tid] + s_pool[1][tid] + s_pool[2][tid] + s_pool[3][tid];
   }
@@ -261,6 +278,30 @@ hipError_t launch_t(const qsa_dims& d, const uint16_t* x, int8_t* codes, float* 
   hipLaunchKernelGGL((quantize_kernel<BS, D, ROT, MAP>), dim3((uint32_t)n_wg), dim3(256), 0, s,
                      x, codes, scales, pooled, d.seq_len, nb, w);
   return hipGetLastError();
+}
+
+// Two tensors of the same shape, codes and scales only, in one launch.
+template <int BS, int D, bool MAP>
+hipError_t launch_pair_t(const qsa_dims& d, const uint16_t* x, const uint16_t* x2, int8_t* codes,
+                         int8_t* codes2, float* scales, float* scales2, int w, hipStream_t s) {
+  const int nb = (d.seq_len + BS - 1) / BS;
+  const uint64_t n_wg = (uint64_t)d.batch * d.heads * nb;
+  hipLaunchKernelGGL((quantize_kernel<BS, D, false, MAP, false>), dim3((uint32_t)n_wg, 2),
+                     dim3(256), 0, s, x, codes, scales, nullptr, d.seq_len, nb, w, x2, codes2,
+                     scales2);
+  return hipGetLastError();
+}
+
+template <bool MAP>
+hipError_t dispatch_pair(const qsa_dims& d, const uint16_t* x, const uint16_t* x2, int8_t* codes,
+                         int8_t* codes2, float* scales, float* scales2, int w, hipStream_t s) {
+  if (d.block == 64 && d.head_dim == 128)
+    return launch_pair_t<64, 128, MAP>(d, x, x2, codes, codes2, scales, scales2, w, s);
+  if (d.block == 64 && d.head_dim == 64)
+    return launch_pair_t<64, 64, MAP>(d, x, x2, codes, codes2, scales, scales2, w, s);
+  if (d.block == 128 && d.head_dim == 128)
+    return launch_pair_t<128, 128, MAP>(d, x, x2, codes, codes2, scales, scales2, w, s);
+  return launch_pair_t<128, 64, MAP>(d, x, x2, codes, codes2, scales, scales2, w, s);
 }
 
 template <bool ROT, bool MAP>
@@ -287,10 +328,12 @@ hipError_t launch_quantize_rotated(const qsa_dims& d, const uint16_t* x, int8_t*
   return dispatch<true, false>(d, x, codes, scales, pooled, 1, s);
 }
 
-hipError_t launch_quantize_position_major(const qsa_dims& d, const uint16_t* x, int window,
-                                          int8_t* codes, float* scales, int32_t* pooled,
-                                          hipStream_t s) {
-  return dispatch<false, true>(d, x, codes, scales, pooled, window, s);
+hipError_t launch_quantize_pair(const qsa_dims& d, const uint16_t* x, const uint16_t* x2,
+                                int window, int8_t* codes, int8_t* codes2, float* scales,
+                                float* scales2, hipStream_t s) {
+  if (window > 0)
+    return dispatch_pair<true>(d, x, x2, codes, codes2, scales, scales2, window, s);
+  return dispatch_pair<false>(d, x, x2, codes, codes2, scales, scales2, 1, s);
 }
 
 }  // namespace qsa

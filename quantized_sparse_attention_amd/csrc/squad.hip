@@ -96,8 +96,6 @@ SquadPlan squad_plan(const qsa_dims& d, int window) {
   p.k_codes = take(bh * n * D);
   p.q_scales = take(bh * nb * 4);
   p.k_scales = take(bh * nb * 4);
-  p.q_pooled = take(bh * nb * D * 4);
-  p.k_pooled = take(bh * nb * D * 4);
   p.o_local = take(bh * n * D * 2);
   return p;
 }
@@ -110,8 +108,6 @@ hipError_t launch_squad(const qsa_dims& d, const uint16_t* q, const uint16_t* k,
   int8_t* kc = reinterpret_cast<int8_t*>(work + p.k_codes);
   float* qs = reinterpret_cast<float*>(work + p.q_scales);
   float* ks = reinterpret_cast<float*>(work + p.k_scales);
-  int32_t* qp = reinterpret_cast<int32_t*>(work + p.q_pooled);
-  int32_t* kp = reinterpret_cast<int32_t*>(work + p.k_pooled);
   uint16_t* o_local = reinterpret_cast<uint16_t*>(work + p.o_local);
   const int m = d.seq_len / window;
 
@@ -128,8 +124,7 @@ hipError_t launch_squad(const qsa_dims& d, const uint16_t* q, const uint16_t* k,
   if ((e = (x)) != hipSuccess) return e
   // local pass: windows of w tokens, natural order, values V; its output
   // rows are written in position-major order, ready as the global values
-  QSA_TRY(launch_quantize(d, q, qc, qs, qp, s));
-  QSA_TRY(launch_quantize(d, k, kc, ks, kp, s));
+  QSA_TRY(launch_quantize_pair(d, q, k, 0, qc, kc, qs, ks, s));
   a.v = v;
   a.out = o_local;
   a.out_map = 1;
@@ -139,8 +134,7 @@ hipError_t launch_squad(const qsa_dims& d, const uint16_t* q, const uint16_t* k,
   // global pass: groups of n/w tokens in position-major order (Q and K
   // quantised from rows gathered in that order), values the local output;
   // its output rows are written back in the natural order
-  QSA_TRY(launch_quantize_position_major(d, q, window, qc, qs, qp, s));
-  QSA_TRY(launch_quantize_position_major(d, k, window, kc, ks, kp, s));
+  QSA_TRY(launch_quantize_pair(d, q, k, window, qc, kc, qs, ks, s));
   a.v = o_local;
   a.out = out;
   a.out_map = 2;
