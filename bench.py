@@ -6,10 +6,12 @@ One timed step = one denoising cycle of one attention layer under the
 refresh schedule F S S S S (a full-attention refresh step, then four sparse
 steps), with fresh drifted inputs at every denoising step.  Every layer step
 runs quantize(Q), quantize(K) and the block selection; a refresh step then
-runs the full-attention residual kernel, a sparse step orders its query
-blocks by kept-set overlap and runs the block-sparse attention kernel in that
-order with the cached residuals added in its epilogue.  Inputs are
-resident in HBM before the timed region.
+orders the query blocks by kept-set overlap and runs the full-attention
+residual kernel in that order, and a sparse step runs the block-sparse
+attention kernel in the order of the last refresh (the order changes no
+output bit; --order-every-step computes it at every step instead) with the
+cached residuals added in its epilogue.  Inputs are resident in HBM before
+the timed region.
 
 Printed (one JSON line): the headline is the sparse-step time per layer (the
 15 %-density step the metric names), with the kept-tile effective TOPS of the
@@ -66,6 +68,9 @@ def parse():
     p.add_argument("--no-select-work", action="store_true",
                    help="select with qsa_select_blocks (keys in LDS, one pass) instead of "
                         "qsa_select_blocks_work (score keys of every slice in a workspace)")
+    p.add_argument("--order-every-step", action="store_true",
+                   help="order the query blocks at every step (default: at refresh steps, the "
+                        "sparse steps reusing that order)")
     p.add_argument("--no-peaks", action="store_true",
                    help="skip the MFMA-rate probe (libqsa_probe.so) reported as measured_peaks")
     p.add_argument("--calib-copy-mb", type=int, default=0,
@@ -463,7 +468,8 @@ def main():
             e[5].record(stream)
             state["has_prev"] = True
         else:
-            Bn.qsa_order_query_blocks(idx, cnt, L, bs, D, order)
+            if args.order_every_step:
+                Bn.qsa_order_query_blocks(idx, cnt, L, bs, D, order)
             e[4].record(stream)
             Bn.qsa_sparse_attn_ordered(qc, qs, kc, ks, x["v"], idx, cnt, order, bs, sm, r=r,
                                        dr=dr, out=out)
@@ -504,7 +510,8 @@ def main():
             t["quant_pair"].append(e[0].elapsed_time(e[1]))
             t["select"].append(e[1].elapsed_time(e[2]))
             if kind == "S":
-                t["order"].append(e[2].elapsed_time(e[4]))
+                if args.order_every_step:
+                    t["order"].append(e[2].elapsed_time(e[4]))
                 t["sparse"].append(e[4].elapsed_time(e[3]))  # the attention launch alone
             else:
                 t["order"].append(e[2].elapsed_time(e[8]))
@@ -582,6 +589,9 @@ def main():
                    "select": ("qsa_select_blocks" if args.no_select_work else
                               "qsa_select_blocks_work, score keys of all slices in one pass"),
                    "residual_rank": args.rank,
+                   "order": ("qsa_order_query_blocks at every step" if args.order_every_step else
+                             "qsa_order_query_blocks at refresh steps; the sparse steps reuse "
+                             "the last refresh's order (no output bit depends on it)"),
                    "step": "one denoising cycle (%s) of one attention layer" % schedule},
         "effective_tops": round(achieved / 1e12, 1),
         "pct_mfma_peak": round(100 * tmin / t_attn, 1) if t_attn > 0 else None,

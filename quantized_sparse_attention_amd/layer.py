@@ -22,9 +22,14 @@ class QSAConfig:
     band: tuple = (0,)
     sm_scale: float | None = None
     order: int = 2  # 2: sparse + r + dr; 1: sparse + r (first-order reuse)
-    # process the query blocks of sparse steps in an order that groups blocks
-    # with overlapping kept sets (same outputs, more shared key-tile loads)
-    reorder: bool = True
+    # process the query blocks in an order that groups blocks with
+    # overlapping kept sets (same outputs bit for bit, more shared key-tile
+    # loads): "refresh" computes it at refresh steps (and whenever the layer
+    # has none for the input shape) and reuses it on the sparse steps until
+    # the next refresh, as the kept sets drift slowly between refreshes;
+    # "step" recomputes it at every step; "off" keeps ascending order.
+    # True and False stand for "refresh" and "off".
+    reorder: str | bool = "refresh"
     # quantise Hadamard-rotated Q and K rows (DVD-Quant,
     # gist.science/es/paper/2505.18663, technical summary §2B); attention then
     # runs with sm_scale / head_dim
@@ -73,6 +78,7 @@ class QuantSparseAttention:
         self.prev_out = None
         self.change = 0.0       # accumulated normalised L1 change
         self.refresh_next = True
+        self.order = None       # processing order of the query blocks (reorder)
         self.last_sums = None   # (sum|O_t - O_t-1|, sum|O_t-1|) of the last step
         self.l1_work = None
         self.l1_sums = None
@@ -84,6 +90,7 @@ class QuantSparseAttention:
         self.prev_out = None
         self.change = 0.0
         self.refresh_next = True
+        self.order = None
 
     def state_dict(self):
         """A snapshot of the residual cache and trigger state.  Tensors are
@@ -160,16 +167,32 @@ class QuantSparseAttention:
             self.change = 0.0
         self.prev_out.copy_(out)
 
+    def _reorder_mode(self) -> str:
+        m = self.cfg.reorder
+        m = "refresh" if m is True else "off" if m is False else m
+        if m not in ("refresh", "step", "off"):
+            raise ValueError(f"QSAConfig.reorder must be 'refresh', 'step' or 'off', not {m!r}")
+        return m
+
+    def _order(self, idx, cnt, L: int, D: int, refresh: bool):
+        """The processing order for this step (None: ascending order)."""
+        mode = self._reorder_mode()
+        if mode == "off":
+            return None
+        stale = self.order is None or self.order.shape != cnt.shape
+        if mode == "step" or refresh or stale:
+            self.order = B.qsa_order_query_blocks(idx, cnt, L, self.cfg.block, D)
+        return self.order
+
     def _step(self, q, k, v, refresh: bool) -> torch.Tensor:
         c = self.cfg
         qc, qs, kc, ks, idx, cnt = self._front(q, k)
         sm = self._sm_scale(q.shape[3])
+        order = self._order(idx, cnt, q.shape[2], q.shape[3], refresh)
         if refresh:
             if self.r is None:
                 self.r = torch.zeros_like(v)
                 self.dr = torch.zeros_like(v)
-            order = (B.qsa_order_query_blocks(idx, cnt, q.shape[2], c.block, q.shape[3])
-                     if c.reorder else None)
             out = B.qsa_full_attn_residual(qc, qs, kc, ks, v, idx, cnt, c.block, self.r, self.dr,
                                            self.has_prev, sm, order=order)
             if c.rank is not None and self.has_prev:
@@ -183,8 +206,7 @@ class QuantSparseAttention:
         if self.r is None:
             raise RuntimeError("sparse step before any full-attention refresh step")
         dr = self.dr if c.order == 2 else None
-        if c.reorder:
-            order = B.qsa_order_query_blocks(idx, cnt, q.shape[2], c.block, q.shape[3])
+        if order is not None:
             return B.qsa_sparse_attn_ordered(qc, qs, kc, ks, v, idx, cnt, order, c.block,
                                              sm, r=self.r, dr=dr)
         return B.qsa_sparse_attn(qc, qs, kc, ks, v, idx, cnt, c.block, sm, r=self.r,

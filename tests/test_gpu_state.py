@@ -6,6 +6,8 @@
   2509.23681, technical summary §2B, is state carried across denoising
   steps, so a restart must reproduce it exactly).  A snapshot must not change
   when the layer it came from steps on.
+* Reorder modes: the processing order of the query blocks, taken at refresh
+  steps only, at every step, or not at all, changes no output bit.
 * Guard bytes: every output buffer of every entry point is allocated inside a
   larger buffer whose bytes before and after it hold a canary pattern, with a
   ragged sequence length and one head (so a write past row L would land in
@@ -70,6 +72,41 @@ def test_resume_mid_schedule_is_bit_identical(adaptive):
     # loading kept copies: the snapshot is still as taken
     for k, v in snap_bits.items():
         assert np.array_equal(_bits(snap[k]), v), f"snapshot {k} changed by the resumed run"
+
+
+def test_reorder_modes_give_the_same_bits():
+    """The processing order of the query blocks changes no output bit: a
+    layer that orders at refresh steps and reuses that order on the sparse
+    steps (the default), one that orders at every step, and one in ascending
+    order give identical outputs and caches over F S S F S with drifting
+    inputs.  The first keeps its refresh's order through the sparse steps and
+    takes the next refresh's lists' order at the next refresh."""
+    w = TINY.with_(grid=(2, 12, 40), head_dim=128, noise_std=0.3, outlier_channels=3,
+                   outlier_gain=10.0)  # 960 tokens, 15 blocks
+    xs = [{t: dev_bf16(st[t]) for t in "qkv"} for st in qsa_gen.make_qkv_steps(w, 5)]
+    kinds = [True, False, False, True, False]
+    cfg = dict(block=w.block, topk=3, band=(0,))
+    layers = {m: QuantSparseAttention(QSAConfig(reorder=m, **cfg)) for m in ("refresh", "step", "off")}
+    assert QuantSparseAttention(QSAConfig(reorder=True, **cfg))._reorder_mode() == "refresh"
+    assert QuantSparseAttention(QSAConfig(reorder=False, **cfg))._reorder_mode() == "off"
+    with pytest.raises(ValueError):
+        QuantSparseAttention(QSAConfig(reorder="sometimes", **cfg))._reorder_mode()
+    kept = None
+    for s, refresh in enumerate(kinds):
+        outs = {m: _bits(lay.step(**xs[s], refresh=refresh)) for m, lay in layers.items()}
+        for m in ("step", "off"):
+            assert np.array_equal(outs[m], outs["refresh"]), f"step {s}: {m} differs"
+            assert np.array_equal(_bits(layers[m].r), _bits(layers["refresh"].r)), (s, m)
+            assert np.array_equal(_bits(layers[m].dr), _bits(layers["refresh"].dr)), (s, m)
+        lay = layers["refresh"]
+        if refresh:
+            want = B.qsa_order_query_blocks(lay.last.kept_idx, lay.last.kept_cnt, w.seq_len,
+                                            w.block, w.head_dim)
+            assert torch.equal(lay.order, want), f"step {s}: the refresh's order"
+            kept = lay.order.clone()
+        else:
+            assert torch.equal(lay.order, kept), f"step {s}: the order was not reused"
+        assert layers["off"].order is None
 
 
 # ---------------------------------------------------------------------------
