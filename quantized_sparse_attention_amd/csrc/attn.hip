@@ -47,6 +47,7 @@
 // then continues the same state over every other block (the full
 // attention): the two share every exponential and MFMA of the kept tiles.
 #include "qsa_internal.h"
+#include "quant_codes.h"
 
 #ifndef QSA_ATTN_QB
 #define QSA_ATTN_QB 2
@@ -444,6 +445,69 @@ __device__ __forceinline__ void store_bf16x4(uint16_t* p, float a, float b, floa
   *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(a, b), pack_bf16x2(c, d));
 }
 
+// Windowed mode with bf16 Q: the codes of this wave's 32 query rows (the B
+// operand layout of S^T = K Q^T) formed here as qsa_quantize forms them: the
+// block's amax over its rows (the BS/32 waves of a block exchange theirs
+// through LDS, one barrier for the workgroup), s = fl32(amax / 127), each
+// code rounded by codes8.  Row qrow of the sequence is token qrow, or with
+// a.q_pm_w > 0 the position-major row of windows of a.q_pm_w tokens (token
+// (qrow % m) * q_pm_w + qrow / m, m = L / q_pm_w).  Rows past L are zero.
+// Returns s.
+template <int BS, int D>
+__device__ __forceinline__ float quantize_q_rows(const AttnArgs& a, v4i (&qb)[Cfg<BS, D>::KS],
+                                                 uint64_t head_off, int qrow, bool qvalid, int L,
+                                                 int lane, int wave, float* s_qmax) {
+  using C = Cfg<BS, D>;
+  const int g = lane >> 5;
+  int tok = qrow;
+  if (a.q_pm_w > 0) {
+    const int m = L / a.q_pm_w;
+    tok = (qrow % m) * a.q_pm_w + qrow / m;
+  }
+  const uint16_t* src = a.q_x + head_off + (size_t)tok * D + g * (D / 2);
+  float y[C::KS][2][8];
+  float amax = 0.0f;
+#pragma unroll
+  for (int c = 0; c < C::KS; ++c)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint4 r = qvalid ? *reinterpret_cast<const uint4*>(src + 16 * c + 8 * h)
+                             : make_uint4(0u, 0u, 0u, 0u);
+      const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        y[c][h][2 * e] = bf16_lo(w[e]);
+        y[c][h][2 * e + 1] = bf16_hi(w[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(y[c][h][e]));
+    }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 64));
+  if (lane == 0) s_qmax[wave] = amax;
+  __syncthreads();
+  const int w0 = (wave / C::WPB) * C::WPB;
+  amax = 0.0f;
+#pragma unroll
+  for (int w = 0; w < C::WPB; ++w) amax = fmaxf(amax, s_qmax[w0 + w]);
+  const float s = amax / 127.0f;  // IEEE division; 0 for an all-zero block
+  const bool fast = s >= 0x1p-100f;
+  const float inv = fast ? 1.0f / s : 0.0f;
+#pragma unroll
+  for (int c = 0; c < C::KS; ++c) {
+    uint32_t lo[2], hi[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float q[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+      if (s > 0.0f) codes8(y[c][h], s, inv, fast, q);
+      uint32_t pairs[4];
+      pack_codes(q, lo[h], hi[h], pairs);
+    }
+    qb[c] = v4i{(int)lo[0], (int)hi[0], (int)lo[1], (int)hi[1]};
+  }
+  return s;
+}
+
 // Kept sets of the query blocks of a workgroup as bitmaps over the key blocks,
 // in LDS: bit j of row b is set when key block j is in kept(i) of the group's
 // b-th query block i.  Row b holds words [b*nw, (b+1)*nw) of one array sized
@@ -786,6 +850,7 @@ __attribute__((amdgpu_waves_per_eu(JitWalk<BS, D, REFRESH>::on ? QSA_ATTN_JIT_WA
   __shared__ __attribute__((aligned(1024))) int8_t s_k[NBUF * C::K_BYTES];
   __shared__ __attribute__((aligned(1024))) uint16_t s_v[NBUF * C::V_BYTES / 2];
   __shared__ uint32_t s_bits[QB * kMaxWords];
+  __shared__ float s_qmax[WIN ? NWV : 1];  // windowed mode with bf16 Q: per-wave amax
   // The tile list of the two-buffer walk and its length/tail words live in
   // the bitmap array past the words the bitmaps use (it is sized for the
   // largest block count), so the workgroup's LDS footprint, and with it the
@@ -825,11 +890,19 @@ __attribute__((amdgpu_waves_per_eu(JitWalk<BS, D, REFRESH>::on ? QSA_ATTN_JIT_WA
   const int qrow = i * BS + 32 * (wave % C::WPB) + ql;
   const bool qvalid = qrow < L;
   v4i qb[C::KS];
+  bool q_here = false;  // windowed mode: Q codes formed here from bf16 Q
+  float sq_here = 0.0f;
+  if constexpr (WIN) q_here = a.q_x != nullptr;
+  if (q_here) {
+    sq_here = quantize_q_rows<BS, D>(a, qb, head_off, qrow, qvalid && i < nb, L, lane, wave,
+                                     s_qmax);
+  } else {
 #pragma unroll
-  for (int c = 0; c < C::KS; ++c) {
-    qb[c] = qvalid ? *reinterpret_cast<const v4i*>(a.q_codes + head_off + (size_t)qrow * D +
-                                                   g * (D / 2) + 16 * c)
-                   : v4i{0, 0, 0, 0};
+    for (int c = 0; c < C::KS; ++c) {
+      qb[c] = qvalid ? *reinterpret_cast<const v4i*>(a.q_codes + head_off + (size_t)qrow * D +
+                                                     g * (D / 2) + 16 * c)
+                     : v4i{0, 0, 0, 0};
+    }
   }
   // the Q loads stay in flight while the kept sets are read (their waits
   // cover them: loads complete in order); in the windowed mode the first
@@ -845,7 +918,8 @@ __attribute__((amdgpu_waves_per_eu(JitWalk<BS, D, REFRESH>::on ? QSA_ATTN_JIT_WA
   x.L = L;
   x.wave = wave;
   x.lane = lane;
-  x.c0 = i < nb ? a.sm_scale * a.q_scales[bh * (uint64_t)nb + i] * kLog2e : 0.0f;
+  x.c0 = i < nb ? a.sm_scale * (q_here ? sq_here : a.q_scales[bh * (uint64_t)nb + i]) * kLog2e
+               : 0.0f;
 
   if constexpr (!WIN)
     build_kept_bits<QB, THREADS>(s_bits, a, row0, [&](int b) { return block_at(b); }, nq, nb,

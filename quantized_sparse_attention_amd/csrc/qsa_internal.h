@@ -57,13 +57,13 @@ hipError_t launch_quantize(const qsa_dims& d, const uint16_t* x, int8_t* codes, 
 hipError_t launch_quantize_rotated(const qsa_dims& d, const uint16_t* x, int8_t* codes,
                                    float* scales, int32_t* pooled, hipStream_t s);
 
-// The codes and scales of qsa_quantize (no pooled sums) for two tensors of
-// the same shape in one launch; with window > 0, of their rows in
-// position-major order of windows of `window` tokens (row p*(L/window) + k
-// is row k*window + p of x), gathered from x.
-hipError_t launch_quantize_pair(const qsa_dims& d, const uint16_t* x, const uint16_t* x2,
-                                int window, int8_t* codes, int8_t* codes2, float* scales,
-                                float* scales2, hipStream_t s);
+// The codes and scales of qsa_quantize (no pooled sums) of x and, when x2 is
+// not NULL, of a second tensor of the same shape in the same launch; with
+// window > 0, of their rows in position-major order of windows of `window`
+// tokens (row p*(L/window) + k is row k*window + p of x), gathered from x.
+hipError_t launch_quantize_codes(const qsa_dims& d, const uint16_t* x, const uint16_t* x2,
+                                 int window, int8_t* codes, int8_t* codes2, float* scales,
+                                 float* scales2, hipStream_t s);
 
 hipError_t launch_select(const qsa_dims& d, const int32_t* pooled_q, const float* scale_q,
                          const int32_t* pooled_k, const float* scale_k, int32_t topk,
@@ -109,6 +109,12 @@ struct AttnArgs {
   // launch_sparse_attn_window only: query block i keeps the win_blocks blocks
   // of its own window, [i - i % win_blocks, ...) (kept_idx, kept_cnt unused)
   int32_t win_blocks;
+  // launch_sparse_attn_window only, optional: bf16 Q [B,H,L,D], quantised in
+  // the kernel as qsa_quantize would (q_codes, q_scales unused); with
+  // q_pm_w > 0 its rows are taken in position-major order of windows of
+  // q_pm_w tokens (row p*(L/q_pm_w) + k is token k*q_pm_w + p)
+  const uint16_t* q_x;
+  int32_t q_pm_w;
 };
 
 hipError_t launch_sparse_attn(const qsa_dims& d, const AttnArgs& a, hipStream_t s);
@@ -147,7 +153,7 @@ hipError_t l1_static_scratch(double** work);
 // SQuad two-pass attention: scratch layout (byte offsets, 256-aligned).
 struct SquadPlan {
   uint64_t bytes;
-  uint64_t q_codes, k_codes, q_scales, k_scales;
+  uint64_t k_codes, k_scales;
   uint64_t o_local;
 };
 SquadPlan squad_plan(const qsa_dims& d, int window);

@@ -29,6 +29,7 @@
 #include <type_traits>
 
 #include "qsa_internal.h"
+#include "quant_codes.h"
 
 #pragma clang fp contract(off)
 
@@ -41,57 +42,6 @@ __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
   return v;
-}
-
-// code = clamp(rint(fl32(x / s)), -127, 127) for a block scale s > 0 with
-// |x| <= 127 s (the clamp only guards the contract), returned as the fp32
-// value of that integer.
-//
-// Without a division per element: with inv = fl32(1 / s), p = fl32(x * inv)
-// is within 127 * 2^-23 < 2^-16 of the exact quotient q = x / s, and fl32(q)
-// within half an ulp below 128, 2^-18, of q.  c = rint(p) and d = p - c are
-// exact (d by Sterbenz's lemma).  If |d| <= 1/2 - 2^-15 then |q - c| <
-// 1/2 - 2^-16 and |fl32(q) - c| < 1/2 - 2^-16 + 2^-18 < 1/2, so c is
-// rint(fl32(q)); otherwise the element takes the IEEE division.  Needs 1 / s
-// finite and normal: the caller takes the division for every element when
-// s < 2^-100.
-__device__ __forceinline__ bool near_half(float p, float c) {
-  return !(fabsf(p - c) <= 0.5f - 0x1p-15f);
-}
-
-__device__ __forceinline__ void codes8(const float (&x)[8], float s, float inv, bool fast,
-                                       float (&q)[8]) {
-  bool any_div = !fast;  // one flag per lane; the rare branch re-tests each element
-  if (fast) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float p = x[e] * inv;
-      q[e] = __builtin_rintf(p);
-      any_div |= near_half(p, q[e]);
-    }
-  }
-  if (any_div) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (!fast || near_half(x[e] * inv, q[e])) q[e] = __builtin_rintf(x[e] / s);
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) q[e] = __builtin_amdgcn_fmed3f(q[e], -127.0f, 127.0f);
-}
-
-// Eight integer-valued floats in [-127, 127] to their int8 bytes (lo: e 0-3,
-// hi: e 4-7) and to four pairs of int16 (pairs[k] holds elements 2k, 2k+1).
-// Adding 1.5 * 2^23 is exact and leaves the integer's two's complement in the
-// low mantissa bits; byte permutes then gather them.
-__device__ __forceinline__ void pack_codes(const float (&q)[8], uint32_t& lo, uint32_t& hi,
-                                           uint32_t (&pairs)[4]) {
-  uint32_t b[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) b[e] = __float_as_uint(q[e] + 0x1.8p23f);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) pairs[k] = __builtin_amdgcn_perm(b[2 * k + 1], b[2 * k], 0x05040100u);
-  lo = __builtin_amdgcn_perm(pairs[1], pairs[0], 0x06040200u);
-  hi = __builtin_amdgcn_perm(pairs[3], pairs[2], 0x06040200u);
 }
 
 __device__ __forceinline__ uint32_t add_i16x2(uint32_t a, uint32_t b) {
@@ -280,13 +230,15 @@ hipError_t launch_t(const qsa_dims& d, const uint16_t* x, int8_t* codes, float* 
   return hipGetLastError();
 }
 
-// Two tensors of the same shape, codes and scales only, in one launch.
+// Codes and scales only, of one tensor or (x2 not NULL) two of the same
+// shape in one launch.
 template <int BS, int D, bool MAP>
 hipError_t launch_pair_t(const qsa_dims& d, const uint16_t* x, const uint16_t* x2, int8_t* codes,
                          int8_t* codes2, float* scales, float* scales2, int w, hipStream_t s) {
   const int nb = (d.seq_len + BS - 1) / BS;
   const uint64_t n_wg = (uint64_t)d.batch * d.heads * nb;
-  hipLaunchKernelGGL((quantize_kernel<BS, D, false, MAP, false>), dim3((uint32_t)n_wg, 2),
+  hipLaunchKernelGGL((quantize_kernel<BS, D, false, MAP, false>),
+                     dim3((uint32_t)n_wg, x2 ? 2u : 1u),
                      dim3(256), 0, s, x, codes, scales, nullptr, d.seq_len, nb, w, x2, codes2,
                      scales2);
   return hipGetLastError();
@@ -328,9 +280,9 @@ hipError_t launch_quantize_rotated(const qsa_dims& d, const uint16_t* x, int8_t*
   return dispatch<true, false>(d, x, codes, scales, pooled, 1, s);
 }
 
-hipError_t launch_quantize_pair(const qsa_dims& d, const uint16_t* x, const uint16_t* x2,
-                                int window, int8_t* codes, int8_t* codes2, float* scales,
-                                float* scales2, hipStream_t s) {
+hipError_t launch_quantize_codes(const qsa_dims& d, const uint16_t* x, const uint16_t* x2,
+                                 int window, int8_t* codes, int8_t* codes2, float* scales,
+                                 float* scales2, hipStream_t s) {
   if (window > 0)
     return dispatch_pair<true>(d, x, x2, codes, codes2, scales, scales2, window, s);
   return dispatch_pair<false>(d, x, x2, codes, codes2, scales, scales2, 1, s);

@@ -15,8 +15,9 @@
 // for callers that run the passes through qsa_sparse_attn), and the reorder
 // between window-major and position-major order (a row gather of 16-byte
 // chunks, HBM-bound; exported for callers that need it).  The
-// operator itself reorders nothing: the global pass quantises Q and K from
-// rows gathered in position-major order, the local pass writes its output
+// operator itself reorders nothing: each pass quantises its own query rows
+// from bf16 Q (gathered in position-major order for the global pass) and a
+// launch per pass quantises K likewise, the local pass writes its output
 // rows in position-major order and the global pass writes its rows back in
 // the natural order (row maps of the attention epilogue).
 #include "qsa_internal.h"
@@ -92,9 +93,7 @@ SquadPlan squad_plan(const qsa_dims& d, int window) {
     return off;
   };
   p.bytes = 0;
-  p.q_codes = take(bh * n * D);
   p.k_codes = take(bh * n * D);
-  p.q_scales = take(bh * nb * 4);
   p.k_scales = take(bh * nb * 4);
   p.o_local = take(bh * n * D * 2);
   return p;
@@ -104,16 +103,13 @@ hipError_t launch_squad(const qsa_dims& d, const uint16_t* q, const uint16_t* k,
                         const uint16_t* v, int window, float sm_scale, uint16_t* out, char* work,
                         hipStream_t s) {
   const SquadPlan p = squad_plan(d, window);
-  int8_t* qc = reinterpret_cast<int8_t*>(work + p.q_codes);
   int8_t* kc = reinterpret_cast<int8_t*>(work + p.k_codes);
-  float* qs = reinterpret_cast<float*>(work + p.q_scales);
   float* ks = reinterpret_cast<float*>(work + p.k_scales);
   uint16_t* o_local = reinterpret_cast<uint16_t*>(work + p.o_local);
   const int m = d.seq_len / window;
 
   AttnArgs a{};
-  a.q_codes = qc;
-  a.q_scales = qs;
+  a.q_x = q;  // each pass quantises its own query rows
   a.k_codes = kc;
   a.k_scales = ks;
   a.order = nullptr;  // windowed kept sets: no lists
@@ -124,7 +120,8 @@ hipError_t launch_squad(const qsa_dims& d, const uint16_t* q, const uint16_t* k,
   if ((e = (x)) != hipSuccess) return e
   // local pass: windows of w tokens, natural order, values V; its output
   // rows are written in position-major order, ready as the global values
-  QSA_TRY(launch_quantize_pair(d, q, k, 0, qc, kc, qs, ks, s));
+  QSA_TRY(launch_quantize_codes(d, k, nullptr, 0, kc, nullptr, ks, nullptr, s));
+  a.q_pm_w = 0;
   a.v = v;
   a.out = o_local;
   a.out_map = 1;
@@ -134,7 +131,8 @@ hipError_t launch_squad(const qsa_dims& d, const uint16_t* q, const uint16_t* k,
   // global pass: groups of n/w tokens in position-major order (Q and K
   // quantised from rows gathered in that order), values the local output;
   // its output rows are written back in the natural order
-  QSA_TRY(launch_quantize_pair(d, q, k, window, qc, kc, qs, ks, s));
+  QSA_TRY(launch_quantize_codes(d, k, nullptr, window, kc, nullptr, ks, nullptr, s));
+  a.q_pm_w = window;
   a.v = o_local;
   a.out = out;
   a.out_map = 2;
