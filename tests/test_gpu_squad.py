@@ -2,8 +2,9 @@
 gist.science/es/paper/2608.16585, technical summary, methodology §1) through
 the C ABI against the oracle's squad_attention.
 
-Bit-exact: the window kept lists and the reorder between window-major and
-position-major order.  Within tolerance: the output.  Each pass has the
+Bit-exact: the window kept lists, the reorder between window-major and
+position-major order, and the operator against its composition from the
+public entry points.  Within tolerance: the output.  Each pass has the
 attention tolerance; the local output is stored in bf16 on both sides, so
 the global pass sees values that differ by the local pass's error plus one
 bf16 ulp where a rounding flips, and its output (a convex combination of
@@ -74,6 +75,35 @@ def test_squad_attention_parity(Bn, H, n, D, window, block):
     m = float(np.abs(got - want).max())
     print(f"\n[squad] n={n} w={window} block={block}: rel_l2={r:.2e} max_abs={m:.2e}", flush=True)
     assert r <= REL_L2 and m <= _bound(x["v"])
+
+
+@pytest.mark.parametrize("Bn,H,n,D,window,block", [(1, 2, 4096, 64, 64, 64),
+                                                    (1, 2, 8192, 128, 128, 64),
+                                                    (2, 1, 8192, 64, 64, 64),
+                                                    (1, 1, 16384, 128, 128, 128)])
+def test_squad_equals_its_composition_from_entry_points(Bn, H, n, D, window, block):
+    """The operator (one K quantisation per pass, each pass quantising its own
+    query rows, row maps in the attention epilogue, no reorder passes) gives,
+    bit for bit, what the same two passes give when composed from the public
+    entry points: qsa_quantize of Q and K, qsa_window_kept lists and
+    qsa_sparse_attn for the local pass; qsa_reorder_windows of Q, K and the
+    local output to position-major order, qsa_quantize again, the group lists
+    and qsa_sparse_attn for the global pass; the inverse reorder."""
+    x = _inputs(Bn, H, n, D, seed=11 + window // 64, block=block)
+    q, k, v = (dev_bf16(x[t]) for t in "qkv")
+    got = B.qsa_squad_attention(q, k, v, window, block)
+    qc, qs, _ = B.qsa_quantize(q, block)
+    kc, ks, _ = B.qsa_quantize(k, block)
+    idx, cnt = B.qsa_window_kept(Bn, H, n, block, window)
+    o_local = B.qsa_sparse_attn(qc, qs, kc, ks, v, idx, cnt, block)
+    pm = [B.qsa_reorder_windows(t, window) for t in (q, k, o_local)]
+    qc, qs, _ = B.qsa_quantize(pm[0], block)
+    kc, ks, _ = B.qsa_quantize(pm[1], block)
+    idx, cnt = B.qsa_window_kept(Bn, H, n, block, n // window)
+    o_global = B.qsa_sparse_attn(qc, qs, kc, ks, pm[2], idx, cnt, block)
+    want = B.qsa_reorder_windows(o_global, window, inverse=True)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int16), want.view(torch.int16))
 
 
 # More work items (b*h, group of query blocks) than the device holds
