@@ -50,17 +50,17 @@ __device__ __forceinline__ uint32_t add_i16x2(uint32_t a, uint32_t b) {
 
 // The value of lane (lane ^ M) for M < 16, moved with DPP inside the lane's
 // row of 16 (no LDS crossbar): lane distances 1 and 2 by quad permutes, 8 by
-// a rotate of the row by 8 (its own inverse); 4 by the row rotate by 4 or by
-// 12, whichever brings lane ^ 4 (take4: this lane's choice, found once by
-// moving the lane ids themselves).
+// a rotate of the row by 8 (its own inverse), 4 by two moves: a mirror of
+// each half-row (lane i takes lane 7 - i) after a reversal of each quad
+// (lane i takes i ^ 3), so lane i reads 7 - (i ^ 3) = i ^ 4.
 template <int M>
-__device__ __forceinline__ float lane_xor(float v, bool take4) {
+__device__ __forceinline__ float lane_xor(float v) {
   static_assert(M == 1 || M == 2 || M == 4 || M == 8, "partners inside a row of 16 lanes");
   const int x = __float_as_int(v);
   if constexpr (M == 4) {
-    const int a = __builtin_amdgcn_update_dpp(0, x, 0x124, 0xF, 0xF, true);  // row_ror:4
-    const int b = __builtin_amdgcn_update_dpp(0, x, 0x12C, 0xF, 0xF, true);  // row_ror:12
-    return __int_as_float(take4 ? a : b);
+    const int t = __builtin_amdgcn_update_dpp(0, x, 0x141, 0xF, 0xF, true);  // row_half_mirror
+    return __int_as_float(
+        __builtin_amdgcn_update_dpp(0, t, 0x1B, 0xF, 0xF, true));  // quad_perm [3,2,1,0]
   } else {
     // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_ror:8
     constexpr int ctrl = M == 1 ? 0xB1 : M == 2 ? 0x4E : 0x128;
@@ -82,14 +82,13 @@ __device__ __forceinline__ void fwht_row(float (&v)[8], int lane) {
       v[e + h] = a - b;
     }
   }
-  const bool take4 = __builtin_amdgcn_update_dpp(0, lane, 0x124, 0xF, 0xF, true) == (lane ^ 4);
   auto stage = [&](auto mc) {  // h = 8 m: the partner lane is lane ^ m
     constexpr int m = decltype(mc)::value;
     // lower lane: v_j + v_{j+h}; upper lane: v_j - v_{j+h}.  One fused
     // multiply-add by +-1 rounds exactly as that sum or difference.
     const float sgn = (lane & m) != 0 ? -1.0f : 1.0f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = __builtin_fmaf(sgn, v[e], lane_xor<m>(v[e], take4));
+    for (int e = 0; e < 8; ++e) v[e] = __builtin_fmaf(sgn, v[e], lane_xor<m>(v[e]));
   };
   if constexpr (CPR > 1) stage(std::integral_constant<int, 1>{});
   if constexpr (CPR > 2) stage(std::integral_constant<int, 2>{});
