@@ -391,10 +391,13 @@ __device__ __forceinline__ void split3(float v, uint16_t (&t)[3]) {
   }
 }
 
+// A workgroup splits the basis into LDS once, then projects `tiles`
+// consecutive tiles of 32 * kProjWaves rows (the split costs more than one
+// tile's rows).
 template <int D, int RP>
 __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(uint16_t* __restrict__ x,
                                                                   const float* __restrict__ wbasis,
-                                                                  int L) {
+                                                                  int L, int tiles) {
   constexpr int RPAD = RP < 32 ? 32 : RP;     // ranks of the first stage's tiles
   constexpr int RT = RPAD / 32;               // first-stage rank tiles
   constexpr int KS1 = D / 16;                 // first-stage k-steps (channels)
@@ -421,85 +424,99 @@ __global__ __launch_bounds__(64 * kProjWaves) void project_kernel(uint16_t* __re
   }
   __syncthreads();
 
-  const int row0 = (blockIdx.x * kProjWaves + wave) * 32;
-  if (row0 >= L) return;  // past the only barrier
-  // rows past the end re-read the last row and are not stored; that row
-  // belongs to this wave, whose reads all precede its stores
-  const int row = min(row0 + l32, L - 1);
   uint16_t* xb = x + bh * (uint64_t)L * D;
-
+  // this wave's rows of tile tt; rows past the end re-read the last row and
+  // are not stored (that row belongs to this wave, whose reads all precede
+  // its stores)
+  auto row_of = [&](int tt) { return ((blockIdx.x * tiles + tt) * kProjWaves + wave) * 32; };
+  auto load_rows = [&](v4i(&dst)[KS1], int row0) {
+    const int row = min(row0 + l32, L - 1);
+#pragma unroll
+    for (int ks = 0; ks < KS1; ++ks)
+      dst[ks] = *reinterpret_cast<const v4i*>(xb + (size_t)row * D + 16 * ks + 8 * g);
+  };
   v4i xo[KS1];
-#pragma unroll
-  for (int ks = 0; ks < KS1; ++ks)
-    xo[ks] = *reinterpret_cast<const v4i*>(xb + (size_t)row * D + 16 * ks + 8 * g);
-  v16f ct[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) ct[rt][r] = 0.0f;
-#pragma unroll
-  for (int ks = 0; ks < KS1; ++ks) {
-    const v8bf b = __builtin_bit_cast(v8bf, xo[ks]);
+  if (row_of(0) < L) load_rows(xo, row_of(0));
+  for (int tt = 0; tt < tiles; ++tt) {
+    const int row0 = row_of(tt);
+    if (row0 >= L) break;  // past the only barrier
+    // the next tile's rows load while this one is computed
+    v4i xn[KS1];
+    const bool more = tt + 1 < tiles && row_of(tt + 1) < L;
+    if (more) load_rows(xn, row_of(tt + 1));
+    v16f ct[RT];
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int s3 = 0; s3 < 3; ++s3) {
-        const v8bf a = *reinterpret_cast<const v8bf*>(
-            &s_vt[s3][(32 * rt + l32) * VT_LD + 16 * ks + 8 * g]);
-        ct[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, ct[rt], 0, 0, 0);
-      }
-  }
-
-  // coefficient splits as second-stage B operands: k-step ks2 takes
-  // registers 8 (ks2 % 2) .. +7 of rank tile ks2 / 2
-  uint32_t cb[3][KS2][4];
+      for (int r = 0; r < 16; ++r) ct[rt][r] = 0.0f;
 #pragma unroll
-  for (int ks2 = 0; ks2 < KS2; ++ks2)
+    for (int ks = 0; ks < KS1; ++ks) {
+      const v8bf b = __builtin_bit_cast(v8bf, xo[ks]);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 8 * (ks2 & 1) + 2 * j;
-      float c0 = ct[ks2 >> 1][r], c1 = ct[ks2 >> 1][r + 1];
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-      for (int s3 = 0; s3 < 3; ++s3) {
-        const uint32_t h = pack_bf16x2(c0, c1);
-        cb[s3][ks2][j] = h;
-        c0 -= bf16_lo(h);
-        c1 -= bf16_hi(h);
-      }
+        for (int s3 = 0; s3 < 3; ++s3) {
+          const v8bf a = *reinterpret_cast<const v8bf*>(
+              &s_vt[s3][(32 * rt + l32) * VT_LD + 16 * ks + 8 * g]);
+          ct[rt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, ct[rt], 0, 0, 0);
+        }
     }
 
-  const bool store = row0 + l32 < L;
+    // coefficient splits as second-stage B operands: k-step ks2 takes
+    // registers 8 (ks2 % 2) .. +7 of rank tile ks2 / 2
+    uint32_t cb[3][KS2][4];
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    v16f o;
+    for (int ks2 = 0; ks2 < KS2; ++ks2)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) o[r] = 0.0f;
+      for (int j = 0; j < 4; ++j) {
+        const int r = 8 * (ks2 & 1) + 2 * j;
+        float c0 = ct[ks2 >> 1][r], c1 = ct[ks2 >> 1][r + 1];
 #pragma unroll
-    for (int ks2 = 0; ks2 < KS2; ++ks2) {
-      v8bf a[3], b[3];
-#pragma unroll
-      for (int s3 = 0; s3 < 3; ++s3) {
-        const uint16_t* base = &s_v[s3][(32 * dt + l32) * V_LD + 16 * ks2 + 4 * g];
-        const uint2 lo4 = *reinterpret_cast<const uint2*>(base);
-        const uint2 hi4 = *reinterpret_cast<const uint2*>(base + 8);
-        a[s3] = __builtin_bit_cast(v8bf, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
-        b[s3] = __builtin_bit_cast(v8bf, make_uint4(cb[s3][ks2][0], cb[s3][ks2][1],
-                                                    cb[s3][ks2][2], cb[s3][ks2][3]));
+        for (int s3 = 0; s3 < 3; ++s3) {
+          const uint32_t h = pack_bf16x2(c0, c1);
+          cb[s3][ks2][j] = h;
+          c0 -= bf16_lo(h);
+          c1 -= bf16_hi(h);
+        }
       }
-      // smallest products first
-      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[1], o, 0, 0, 0);
-      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[0], o, 0, 0, 0);
-      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[2], o, 0, 0, 0);
-      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[0], o, 0, 0, 0);
-      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[1], o, 0, 0, 0);
-      o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[0], o, 0, 0, 0);
-    }
-    if (store) {
-      uint16_t* xr = xb + (size_t)(row0 + l32) * D + 32 * dt + 4 * g;
+
+    const bool store = row0 + l32 < L;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<uint2*>(xr + 8 * q) =
-            make_uint2(pack_bf16x2(o[4 * q], o[4 * q + 1]), pack_bf16x2(o[4 * q + 2], o[4 * q + 3]));
+    for (int dt = 0; dt < DT; ++dt) {
+      v16f o;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[r] = 0.0f;
+#pragma unroll
+      for (int ks2 = 0; ks2 < KS2; ++ks2) {
+        v8bf a[3], b[3];
+#pragma unroll
+        for (int s3 = 0; s3 < 3; ++s3) {
+          const uint16_t* base = &s_v[s3][(32 * dt + l32) * V_LD + 16 * ks2 + 4 * g];
+          const uint2 lo4 = *reinterpret_cast<const uint2*>(base);
+          const uint2 hi4 = *reinterpret_cast<const uint2*>(base + 8);
+          a[s3] = __builtin_bit_cast(v8bf, make_uint4(lo4.x, lo4.y, hi4.x, hi4.y));
+          b[s3] = __builtin_bit_cast(v8bf, make_uint4(cb[s3][ks2][0], cb[s3][ks2][1],
+                                                      cb[s3][ks2][2], cb[s3][ks2][3]));
+        }
+        // smallest products first
+        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[1], o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[2], b[0], o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[2], o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[1], b[0], o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[1], o, 0, 0, 0);
+        o = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[0], b[0], o, 0, 0, 0);
+      }
+      if (store) {
+        uint16_t* xr = xb + (size_t)(row0 + l32) * D + 32 * dt + 4 * g;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<uint2*>(xr + 8 * q) = make_uint2(
+              pack_bf16x2(o[4 * q], o[4 * q + 1]), pack_bf16x2(o[4 * q + 2], o[4 * q + 3]));
+      }
+    }
+    if (more) {
+#pragma unroll
+      for (int ks = 0; ks < KS1; ++ks) xo[ks] = xn[ks];
     }
   }
 }
@@ -516,24 +533,28 @@ hipError_t launch_d(const qsa_dims& d, uint16_t* dr, int rank, float* basis, flo
   hipLaunchKernelGGL((jacobi_kernel<D>), dim3(bh), dim3(kJacobiThreads), 0, st, partial, pl.chunks,
                      rank, pl.rank_pad, eigvals, basis, wbasis);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  const dim3 grid((uint32_t)((d.seq_len + 32 * kProjWaves - 1) / (32 * kProjWaves)), bh);
+  // about 2048 workgroups in all, each over `tiles` row tiles
+  const int64_t n_tiles = (d.seq_len + 32 * kProjWaves - 1) / (32 * kProjWaves);
+  const int64_t want = (n_tiles * (int64_t)bh + 2047) / 2048;
+  const int tiles = (int)(want < 1 ? 1 : want > n_tiles ? n_tiles : want);
+  const dim3 grid((uint32_t)((n_tiles + tiles - 1) / tiles), bh);
   const dim3 block(64 * kProjWaves);
   switch (pl.rank_pad) {
     case 8:
       hipLaunchKernelGGL((project_kernel<D, 8>), grid, block, 0, st, dr, wbasis,
-                         d.seq_len);
+                         d.seq_len, tiles);
       break;
     case 16:
       hipLaunchKernelGGL((project_kernel<D, 16>), grid, block, 0, st, dr, wbasis,
-                         d.seq_len);
+                         d.seq_len, tiles);
       break;
     case 32:
       hipLaunchKernelGGL((project_kernel<D, 32>), grid, block, 0, st, dr, wbasis,
-                         d.seq_len);
+                         d.seq_len, tiles);
       break;
     default:
       hipLaunchKernelGGL((project_kernel<D, 64>), grid, block, 0, st, dr, wbasis,
-                         d.seq_len);
+                         d.seq_len, tiles);
       break;
   }
   return hipGetLastError();
