@@ -467,6 +467,58 @@ def test_short_sequences(L, bs, D):
             assert np.array_equal(a_, b_)
 
 
+def _boost_block(bits, h, blk, block, gain):
+    """bf16 bits with the rows of key block blk of head h scaled by gain."""
+    x = oracle.bf16_to_f64(bits)
+    x[:, h, blk * block:(blk + 1) * block] *= gain
+    return qsa_gen.f32_to_bf16_bits(x.astype(np.float32))
+
+
+@pytest.mark.parametrize("D", [128, 64])
+def test_running_max_moves_mid_walk(D):
+    """Rows whose first kept tile has far smaller logits than a later one: the
+    walk's running max (taken on the first tile) must move up, rescaling the
+    state, when a later tile holds a P above 2^64.  Head 0 has a large middle
+    block, head 1 a large ragged last block (the masked tail tile).  Sparse
+    step with all blocks and with the selected blocks, refresh step (the
+    large block falls in the kept or in the complement phase), against the
+    oracle."""
+    w = TINY.with_(grid=(1, 10, 30), block=64, head_dim=D, heads=2)  # 300 tokens, 5 blocks
+    x = dict(qsa_gen.make_qkv(w))
+    x["k"] = _boost_block(x["k"], 0, 2, w.block, 60.0)
+    x["k"] = _boost_block(x["k"], 1, w.n_blocks - 1, w.block, 60.0)
+    o = oracle_front(x, w, topk=1, band=(0,))
+    # the case is what it claims: in log2 units the large block's logits exceed
+    # block 0's by more than 64 for most query rows of both heads
+    sm = oracle.default_sm_scale(D) * np.log2(np.e)
+    qf = o["qc"].astype(np.float64) * np.repeat(o["sq"], w.block, axis=2)[:, :, :w.seq_len, None]
+    kf = o["kc"].astype(np.float64) * np.repeat(o["sk"], w.block, axis=2)[:, :, :w.seq_len, None]
+    z = np.einsum("bhid,bhjd->bhij", qf, kf) * sm
+    for h, blk in ((0, 2), (1, w.n_blocks - 1)):
+        big = z[0, h, :, blk * w.block:(blk + 1) * w.block].max(axis=1)
+        first = z[0, h, :, :w.block].max(axis=1)
+        assert np.mean(big - first > 64) > 0.9, h
+    g = _gpu_front(x, w, o["topk"], o["band"], o["kmax"])
+    for gk, ok in (("qc", "qc"), ("kc", "kc"), ("idx", "idx"), ("cnt", "cnt")):
+        assert np.array_equal(g[gk].cpu().numpy(), o[ok]), gk
+    v = dev_bf16(x["v"])
+    full_lists = oracle.full_kept_lists(w.batch, w.heads, w.n_blocks)
+    o_full = _oracle_attn(o, x, w, full_lists)
+    fi, fc = (torch.from_numpy(a).cuda() for a in full_lists)
+    out = B.qsa_sparse_attn(g["qc"], g["qs"], g["kc"], g["ks"], v, fi, fc, w.block)
+    assert_close(host_f64(out), o_full, what=f"D={D} all blocks")
+    out = B.qsa_sparse_attn(g["qc"], g["qs"], g["kc"], g["ks"], v, g["idx"], g["cnt"], w.block)
+    o_sp = _oracle_attn(o, x, w)
+    assert_close(host_f64(out), o_sp, what=f"D={D} selected blocks")
+    r, dr = torch.zeros_like(v), torch.zeros_like(v)
+    full = B.qsa_full_attn_residual(g["qc"], g["qs"], g["kc"], g["ks"], v, g["idx"], g["cnt"],
+                                    w.block, r, dr, 0)
+    assert_close(host_f64(full), o_full, what=f"D={D} refresh full")
+    err = host_f64(r) - (o_full - o_sp)
+    assert np.linalg.norm(err) / np.linalg.norm(o_full) <= 5e-3
+    assert np.max(np.abs(err)) <= 2e-2
+
+
 def _messy_lists(w, seed):
     """Kept lists with repeats, entries outside [0, nb) and shuffled order."""
     nb = w.n_blocks
