@@ -16,8 +16,9 @@ the timed region.
 Printed (one JSON line): the headline is the sparse-step time per layer (the
 15 %-density step the metric names), with the kept-tile effective TOPS of the
 sparse attention kernel against the MFMA roofline, the refresh-step and
-cycle-average times, a per-kernel breakdown, and the CPU oracle timed on a
-bounded sample of the same workload on this host.
+cycle-average times, a per-kernel breakdown, the board power and clock
+while sparse steps run (amd-smi), and the CPU oracle timed on a bounded
+sample of the same workload on this host.
 """
 from __future__ import annotations
 
@@ -73,6 +74,9 @@ def parse():
                         "sparse steps reusing that order)")
     p.add_argument("--no-peaks", action="store_true",
                    help="skip the MFMA-rate probe (libqsa_probe.so) reported as measured_peaks")
+    p.add_argument("--no-power", action="store_true",
+                   help="skip the board power and clock sample (amd-smi) taken while sparse "
+                        "steps run back to back after the timed region")
     p.add_argument("--calib-copy-mb", type=int, default=0,
                    help="before the run, copy a bf16 buffer of this many MiB once with a "
                         "plain elementwise kernel (reads and writes each byte once): the "
@@ -117,6 +121,76 @@ def measured_peaks(stream, blocks=2048, iters=40000):
         res[name] = round(ops / min(ts[1:]) / 1e12, 1)
     res["launch"] = f"{blocks} workgroups x 256 threads, {iters} iterations per wave"
     return res
+
+
+def board_power(run_step, seconds=3.0):
+    """Board power and graphics clocks, sampled with `amd-smi metric -p -c`
+    in a thread while run_step() runs back to back for about `seconds`
+    (outside the timed region).  The first quarter of the samples, taken
+    while the clock settles, is dropped.  An error entry where amd-smi is
+    missing or unreadable."""
+    import shutil
+    import subprocess
+    import threading
+
+    import torch
+
+    exe = shutil.which("amd-smi")
+    if exe is None and os.path.exists("/opt/rocm/bin/amd-smi"):
+        exe = "/opt/rocm/bin/amd-smi"
+    if exe is None:
+        return {"error": "amd-smi not found"}
+    samples, stop = [], threading.Event()
+
+    def sample():
+        while not stop.is_set():
+            try:
+                r = subprocess.run([exe, "metric", "-p", "-c", "--json"], capture_output=True,
+                                   text=True, timeout=10)
+                samples.append(r.stdout)
+            except (OSError, subprocess.SubprocessError):
+                samples.append("")
+            stop.wait(0.2)
+
+    th = threading.Thread(target=sample, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    steps = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            run_step()
+            steps += 1
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+
+    def num(v):
+        try:
+            return float(v)
+        except (TypeError, ValueError):
+            return None
+
+    power, clocks = [], []
+    for text in samples[len(samples) // 4:]:
+        try:
+            d = json.loads(text)
+            d = d["gpu_data"][0] if isinstance(d, dict) else d[0]
+            pw = num(d["power"]["socket_power"]["value"])
+            ck = [num(v["clk"]["value"]) for k, v in d["clock"].items() if k.startswith("gfx_")]
+        except (ValueError, KeyError, IndexError, TypeError):
+            continue
+        ck = [c for c in ck if c is not None]
+        if pw is not None and ck:
+            power.append(pw)
+            clocks.append(sum(ck) / len(ck))
+    if not power:
+        return {"error": "no readable amd-smi samples"}
+    return {"power_w": round(sum(power) / len(power), 1),
+            "power_w_range": [min(power), max(power)],
+            "gfx_clock_mhz": round(sum(clocks) / len(clocks)),
+            "samples": len(power), "sparse_steps": steps,
+            "source": "amd-smi metric -p -c (socket power, mean clock of the graphics "
+                      "partitions) while sparse steps run back to back"}
 
 
 TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic_sparse_attn_wan14b_720p.json")
@@ -646,6 +720,8 @@ def main():
     }
     if cold is not None:
         res["cold"] = cold
+    if not args.no_power and sp_steps:
+        res["board"] = board_power(lambda: layer_step(sp_steps[-1], "S", None))
     if not args.no_peaks:
         pk = measured_peaks(stream)
         if "mixed_tops" in pk and t_attn > 0:
